@@ -1,0 +1,193 @@
+// C ABI of libbsfp4: argument validation, device check, dispatch.
+//
+// Every entry point validates all arguments before launching anything and
+// reports the first violation through a status code plus a per-thread
+// message.  Checks follow the pages' entry points (vLLM `sm103` branch
+// comparison page: `scaled_fp4_quant_sm103a_impl` requires a row length
+// divisible by 16 and bf16/fp16 input; `cutlass_scaled_fp4_mm_sm103a_impl`
+// requires equal K, K % 32 == 0 and N % 32 == 0, contiguous scale tensors;
+// "feat: sm100 cute_dsl w4a16 gemm" review: bf16 activations, aligned
+// pointers, exact scale sizes) restated for this library's unpadded layouts.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/bsfp4.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsfp4_status fail(bsfp4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bsfp4_status ok() {
+  g_err[0] = '\0';
+  return BSFP4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE_PTR(p)                                                             \
+  do {                                                                             \
+    if ((p) == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "%s is NULL", #p);      \
+    if (!aligned((p), 16)) return fail(BSFP4_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define REQUIRE_SCALAR_PTR(p)                                                      \
+  do {                                                                             \
+    if ((p) == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "%s is NULL", #p);      \
+    if (!aligned((p), 4)) return fail(BSFP4_ERR_ALIGNMENT, "%s is not 4-byte aligned", #p); \
+  } while (0)
+
+// The current device must be a gfx950; the answer is cached per device id.
+bsfp4_status check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(BSFP4_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(BSFP4_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+      known[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (known[dev] == 1) return BSFP4_OK;
+  }
+  return fail(BSFP4_ERR_DEVICE, "device %d is not a gfx950 GPU", dev);
+}
+
+bsfp4_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BSFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int bsfp4_version(void) { return 100; }
+
+const char* bsfp4_status_string(int s) {
+  switch (s) {
+    case BSFP4_OK: return "ok";
+    case BSFP4_ERR_INVALID_ARG: return "invalid argument";
+    case BSFP4_ERR_SHAPE: return "unsupported shape";
+    case BSFP4_ERR_ALIGNMENT: return "misaligned pointer";
+    case BSFP4_ERR_WORKSPACE: return "workspace too small";
+    case BSFP4_ERR_DEVICE: return "unsupported device";
+    case BSFP4_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsfp4_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ global scale
+
+size_t fp4_global_scale_workspace_size(int64_t numel) {
+  if (numel <= 0) return 0;
+  return sizeof(float) * (size_t)bsfp4::global_scale_parts(numel);
+}
+
+bsfp4_status fp4_global_scale(const uint16_t* x, int64_t numel, float* gs_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (numel <= 0) return fail(BSFP4_ERR_SHAPE, "numel must be > 0 (got %lld)", (long long)numel);
+  REQUIRE_PTR(x);
+  REQUIRE_SCALAR_PTR(gs_out);
+  REQUIRE_SCALAR_PTR(ws);
+  const size_t need = fp4_global_scale_workspace_size(numel);
+  if (ws_bytes < need)
+    return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_global_scale(x, numel, gs_out, static_cast<float*>(ws), as_stream(stream)),
+                  "fp4_global_scale launch");
+}
+
+// ------------------------------------------------------------------ quantiser
+
+bsfp4_status fp4_quantize(int fmt, const uint16_t* x, int64_t rows_in, int64_t K, const float* gs,
+                          const int32_t* row_map, int64_t rows_out, uint8_t* q, uint8_t* sf,
+                          void* stream) {
+  if (fmt != BSFP4_NVFP4 && fmt != BSFP4_MXFP4) return fail(BSFP4_ERR_INVALID_ARG, "unknown format %d", fmt);
+  if (rows_in < 0 || rows_out < 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0 and K > 0 (rows_in=%lld rows_out=%lld K=%lld)",
+                (long long)rows_in, (long long)rows_out, (long long)K);
+  const int blk = fmt == BSFP4_NVFP4 ? 16 : 32;
+  if (K % blk) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of %d", (long long)K, blk);
+  if (row_map == nullptr && rows_out != rows_in)
+    return fail(BSFP4_ERR_SHAPE, "without row_map rows_out (%lld) must equal rows_in (%lld)",
+                (long long)rows_out, (long long)rows_in);
+  if (fmt == BSFP4_NVFP4) {
+    REQUIRE_SCALAR_PTR(gs);
+  } else if (gs != nullptr) {
+    return fail(BSFP4_ERR_INVALID_ARG, "MXFP4 takes no global scale (gs must be NULL)");
+  }
+  if (rows_out == 0) return ok();
+  if (rows_in > 0) REQUIRE_PTR(x);
+  if (row_map != nullptr && !aligned(row_map, 4)) return fail(BSFP4_ERR_ALIGNMENT, "row_map is not 4-byte aligned");
+  REQUIRE_PTR(q);
+  if (sf == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "sf is NULL");
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_quantize(fmt, x, rows_in, K, gs, row_map, rows_out, q, sf, as_stream(stream)),
+                  "fp4_quantize launch");
+}
+
+// ------------------------------------------------------------------ GEMM
+
+size_t fp4_gemm_workspace_size(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0) return 0;
+  if (fmt == BSFP4_NVFP4) return bsfp4::nvfp4_gemm_workspace(M, N, K);
+  return 0;
+}
+
+bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                      const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M, int64_t N,
+                      int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  if (fmt != BSFP4_NVFP4 && fmt != BSFP4_MXFP4) return fail(BSFP4_ERR_INVALID_ARG, "unknown format %d", fmt);
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need M >= 0, N > 0, K > 0 (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+  if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
+  if (M > 0) {
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(SFA);
+    REQUIRE_PTR(D);
+  }
+  REQUIRE_PTR(B);
+  REQUIRE_PTR(SFB);
+  if (alpha != nullptr && !aligned(alpha, 4)) return fail(BSFP4_ERR_ALIGNMENT, "alpha is not 4-byte aligned");
+  const size_t need = fp4_gemm_workspace_size(fmt, M, N, K);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+  }
+  if (M == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  if (fmt == BSFP4_NVFP4)
+    return launched(bsfp4::launch_nvfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, ws, ws_bytes, as_stream(stream)),
+                    "fp4_gemm launch");
+  return fail(BSFP4_ERR_INVALID_ARG, "MXFP4 dense GEMM is not available yet");
+}
+
+}  // extern "C"

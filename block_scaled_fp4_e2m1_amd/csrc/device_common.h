@@ -1,0 +1,36 @@
+// Device-side helpers shared by the gfx950 kernels of libbsfp4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfp4 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even of a finite binary32 to bf16 bits (NaN not handled:
+// the kernels never produce one from finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two binary32 values -> packed bf16 pair (first in the low half), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return float_to_bf16_rne(lo) | (float_to_bf16_rne(hi) << 16);
+}
+
+}  // namespace bsfp4

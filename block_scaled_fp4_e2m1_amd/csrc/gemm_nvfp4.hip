@@ -1,0 +1,261 @@
+// NVFP4 W4A4 GEMM for gfx950:  D = bf16(alpha * dec(A) @ dec(B)^T).
+//
+// The operation of `Fp4GemmSm103` / `cutlass_scaled_fp4_mm` (vLLM `sm103`
+// branch comparison page, `nvfp4_scaled_mm_kernels.cu`) and CuTe-DSL `mm_fp4`
+// ("perf(gemm): optimize SM103 CuTe DSL mm_fp4 kernel"): E2M1 operands with one
+// E4M3 scale per 16 K-elements, FP32 accumulation, alpha applied to the FP32
+// accumulator followed by one conversion to bf16 ("Alpha epilogue bug").
+//
+// Why fp16 MFMA: gfx950's scaled FP4 MFMA applies one power-of-two (E8M0) scale
+// per 32 K-elements, while NVFP4 carries a 3-mantissa-bit E4M3 scale per 16.
+// The product of an E2M1 value and an E4M3 scale has at most 6 significant bits
+// and lies in [2^-10, 2688], so it is exact in fp16; the fp16 MFMA multiplies
+// exactly and accumulates in FP32.  Dequantisation is two VALU instructions per
+// pair of values: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) and a packed fp16
+// multiply by the block scale.
+//
+// Structure (one workgroup = 256 threads = 4 waves in a 2x2 grid):
+//   * BM x BN output tile, K walked in stages of 128 elements (64 code bytes and
+//     8 scale bytes per row);
+//   * each stage's packed codes and scale bytes are loaded from HBM with 128-bit
+//     loads into registers one stage ahead, then stored to LDS (double buffered)
+//     in a chunk-swizzled layout that keeps the MFMA fragment reads free of bank
+//     conflicts;
+//   * every wave reads its fragments from LDS as packed FP4 (4x less LDS traffic
+//     than fp16 tiles), dequantises them in registers and issues
+//     v_mfma_f32_32x32x16_f16 on a (BM/2) x (BN/2) wave tile;
+//   * epilogue: alpha * acc, RNE to bf16, bounds-checked stores.
+//
+// MFMA lane layouts (measured on gfx950): for 32x32x16, lane l supplies row
+// l%32 and eight consecutive K values of group l/32 of each operand; output
+// register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Within
+// a stage the K index assigned to a lane's values is a fixed permutation shared
+// by A and B, which leaves the sum unchanged; each lane's eight values always
+// lie inside one 16-element scale block.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace bsfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kStageK = 128;              // K elements per stage
+constexpr int kStageBytes = kStageK / 2;  // 64 code bytes per row per stage
+constexpr int kStageBlocks = kStageK / 16;  // 8 E4M3 scales per row per stage
+
+// Position of 16-byte chunk c (0..3) of row r inside the row's 64 bytes.  With
+// this swizzle, 8 (or 16) lanes reading the same logical chunk of 8 (or 16)
+// consecutive rows touch 8 (or 16) distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+template <int ROWS>
+struct StageRegs {
+  static constexpr int kChunks = ROWS * 4 / kThreads;  // 16-byte code chunks per thread
+  uint4 code[kChunks];
+  uint32_t sc[2];  // 8 scale bytes of row `tid` (threads < ROWS)
+};
+
+template <int ROWS>
+__device__ __forceinline__ void load_stage(StageRegs<ROWS>& st, const uint8_t* __restrict__ q,
+                                           const uint8_t* __restrict__ sf, int row0, int nrows,
+                                           int64_t K, int k0, int tid) {
+  const int64_t row_bytes = K / 2;
+  const int64_t row_blocks = K / 16;
+#pragma unroll
+  for (int i = 0; i < StageRegs<ROWS>::kChunks; i++) {
+    const int idx = tid + i * kThreads;
+    const int r = idx >> 2, c = idx & 3;
+    const int64_t kb = (int64_t)k0 / 2 + c * 16;  // byte offset in the row
+    if (row0 + r < nrows && kb < row_bytes) {
+      st.code[i] = *reinterpret_cast<const uint4*>(q + (int64_t)(row0 + r) * row_bytes + kb);
+    } else {
+      st.code[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  if (tid < ROWS) {
+    const int r = tid;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (row0 + r < nrows) {
+      // K % 32 == 0, so scale bytes come in valid pairs (2-byte aligned)
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(sf + (int64_t)(row0 + r) * row_blocks);
+      const int64_t b0 = k0 / 16;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (b0 + 2 * j < row_blocks) w[j] = p[b0 / 2 + j];
+    }
+    st.sc[0] = w[0] | (w[1] << 16);
+    st.sc[1] = w[2] | (w[3] << 16);
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void store_stage(const StageRegs<ROWS>& st, uint8_t* lds_q, uint8_t* lds_s,
+                                            int tid) {
+#pragma unroll
+  for (int i = 0; i < StageRegs<ROWS>::kChunks; i++) {
+    const int idx = tid + i * kThreads;
+    const int r = idx >> 2, c = idx & 3;
+    *reinterpret_cast<uint4*>(lds_q + r * kStageBytes + swz(r, c) * 16) = st.code[i];
+  }
+  if (tid < ROWS) *reinterpret_cast<uint2*>(lds_s + tid * kStageBlocks) = make_uint2(st.sc[0], st.sc[1]);
+}
+
+// Two E4M3 scale bytes (low 16 bits of `pair`) -> packed fp16 pair, exact.
+// Placing the 7 magnitude bits of an E4M3 code at fp16 bit 7 gives the E4M3
+// value times 2^-8 for normal and subnormal codes alike; one multiply by 256
+// (exact) restores it.
+__device__ __forceinline__ v2h e4m3x2_to_f16x2(uint32_t pair) {
+  const uint32_t bits = ((pair & 0x7Fu) << 7) | ((pair & 0x7F00u) << 15);
+  v2h h = __builtin_bit_cast(v2h, bits);
+  const v2h k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return h * k256;
+}
+
+// Eight E2M1 values (one 32-bit word, first value in the low nibble) times the
+// fp16 scale `s` -> eight fp16 values, exact.
+__device__ __forceinline__ v8h dequant8(uint32_t word, _Float16 s) {
+  const v2h ss = {s, s};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * ss;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * ss;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * ss;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * ss;
+  const v4h lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const v4h hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(kThreads, 1)
+    nvfp4_gemm_tiled(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA,
+                     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
+                     const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N,
+                     int64_t K, int tiles_n) {
+  constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
+  constexpr int kABytes = BM * kStageBytes, kBBytes = BN * kStageBytes;
+  constexpr int kStage = kABytes + kBBytes + (BM + BN) * kStageBlocks;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
+
+  const int nstages = (int)((K + kStageK - 1) / kStageK);
+  StageRegs<BM> ra;
+  StageRegs<BN> rb;
+  load_stage<BM>(ra, A, SFA, m0, M, K, 0, tid);
+  load_stage<BN>(rb, B, SFB, n0, N, K, 0, tid);
+  {
+    uint8_t* s = smem;
+    store_stage<BM>(ra, s, s + kABytes + kBBytes, tid);
+    store_stage<BN>(rb, s + kABytes, s + kABytes + kBBytes + BM * kStageBlocks, tid);
+  }
+  __syncthreads();
+
+  const int g = lane >> 5;     // K group of this lane inside an MFMA
+  const int lr = lane & 31;    // row inside a 32-row MFMA tile
+
+  for (int s = 0; s < nstages; s++) {
+    const bool more = (s + 1) < nstages;
+    if (more) {
+      load_stage<BM>(ra, A, SFA, m0, M, K, (s + 1) * kStageK, tid);
+      load_stage<BN>(rb, B, SFB, n0, N, K, (s + 1) * kStageK, tid);
+    }
+    const uint8_t* st = smem + (s & 1) * kStage;
+    const uint8_t* sq_a = st;
+    const uint8_t* sq_b = st + kABytes;
+    const uint8_t* ss_a = st + kABytes + kBBytes;
+    const uint8_t* ss_b = ss_a + BM * kStageBlocks;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      // lane covers chunk 2j+g of its row: K elements 64j + 32g + [0, 32)
+      uint4 ca[TM], cb[TN];
+      v2h sa[TM], sb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int r = wm * WM + i * 32 + lr;
+        ca[i] = *reinterpret_cast<const uint4*>(sq_a + r * kStageBytes + swz(r, 2 * j + g) * 16);
+        sa[i] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(ss_a + r * kStageBlocks + 4 * j + 2 * g));
+      }
+#pragma unroll
+      for (int i = 0; i < TN; i++) {
+        const int r = wn * WN + i * 32 + lr;
+        cb[i] = *reinterpret_cast<const uint4*>(sq_b + r * kStageBytes + swz(r, 2 * j + g) * 16);
+        sb[i] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(ss_b + r * kStageBlocks + 4 * j + 2 * g));
+      }
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        v8h fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+          const uint32_t word = w == 0 ? ca[i].x : w == 1 ? ca[i].y : w == 2 ? ca[i].z : ca[i].w;
+          fa[i] = dequant8(word, (w < 2) ? sa[i].x : sa[i].y);
+        }
+#pragma unroll
+        for (int i = 0; i < TN; i++) {
+          const uint32_t word = w == 0 ? cb[i].x : w == 1 ? cb[i].y : w == 2 ? cb[i].z : cb[i].w;
+          fb[i] = dequant8(word, (w < 2) ? sb[i].x : sb[i].y);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int jn = 0; jn < TN; jn++)
+            acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jn], acc[i][jn], 0, 0, 0);
+      }
+    }
+    if (more) {
+      uint8_t* nx = smem + ((s + 1) & 1) * kStage;
+      store_stage<BM>(ra, nx, nx + kABytes + kBBytes, tid);
+      store_stage<BN>(rb, nx + kABytes, nx + kABytes + kBBytes + BM * kStageBlocks, tid);
+    }
+    __syncthreads();
+  }
+
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < TM; i++) {
+#pragma unroll
+    for (int jn = 0; jn < TN; jn++) {
+      const int n = n0 + wn * WN + jn * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < M && n < N) D[(int64_t)m * N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][jn][r]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                             const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (M == 0) return hipSuccess;
+  constexpr int BM = 256, BN = 256;
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  nvfp4_gemm_tiled<BM, BN><<<tiles_m * tiles_n, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M,
+                                                                       (int)N, K, tiles_n);
+  return hipGetLastError();
+}
+
+size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+}  // namespace bsfp4

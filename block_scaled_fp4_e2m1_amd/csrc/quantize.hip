@@ -1,0 +1,217 @@
+// bf16 -> NVFP4 / MXFP4 block quantiser and the tensor-amax global scale.
+//
+// Implements the activation quantiser of the vLLM `sm103` branch comparison
+// page (`nvfp4_quant_kernels.cu`, `cvt_fp16_to_fp4_sm103`; its `UE8M0_SF`
+// switch gives the power-of-two MX form) and the per-expert MXFP4 activation
+// quant of "[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on SM12x"
+// (`mxfp4_experts_quant`, here a row gather through `row_map`).  The page
+// calls the per-block routine (`cvt_warp_fp16_to_fp4`) without printing it;
+// the arithmetic below is the NVFP4 recipe: block scale = amax / 6 times the
+// global scale, rounded to E4M3; values divided by the decoded scale and
+// rounded to nearest-even onto E2M1.
+//
+// Each step is one correctly rounded binary32 operation (the library is built
+// with -ffp-contract=off and correctly rounded division), so the output bytes
+// are a deterministic function of the input: the kernel is bit-exact by
+// construction, not approximately right.
+//
+// Mapping: one thread quantises one block (16 or 32 elements = 32 or 64
+// bytes of bf16, read with 128-bit loads); consecutive lanes take consecutive
+// blocks of a row, so a wave reads 2 KB (NVFP4) or 4 KB (MXFP4) of contiguous
+// input and writes 512 B / 1 KB of contiguous codes plus 64 scale bytes.
+#include "device_common.h"
+#include "launchers.h"
+
+#pragma clang fp contract(off)
+
+namespace bsfp4 {
+namespace {
+
+// Nearest-even E4M3 code of s >= 0, saturating to 0x7E (448) instead of NaN.
+__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;
+  if (s < 0.015625f) {
+    // Subnormal range (below 2^-6): the grid is k * 2^-9, k = 0..8, and
+    // k = 8 is the bit pattern of 2^-6 itself.  s * 512 is exact.
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t e = (u >> 23) - 120u;  // E4M3 biased exponent (bias 7), 1..15
+  const uint32_t keep = (u >> 20) & 7u;  // top three mantissa bits
+  const uint32_t rest = u & 0xFFFFFu;    // the 20 bits rounded away
+  uint32_t code = (e << 3) | keep;
+  code += (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));  // may carry into e
+  return code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;          // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+}
+
+// Smallest power of two >= s (s >= 0) as an E8M0 code in [0, 254].
+__device__ __forceinline__ uint32_t e8m0_ceil(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t ef = u >> 23, m = u & 0x7FFFFFu;
+  if (ef == 0) return m > 0x400000u ? 1u : 0u;  // binary32 subnormal: 2^-127 = m of 2^22
+  const uint32_t c = ef + (m != 0u);
+  return c > 254u ? 254u : c;
+}
+
+// 2^(127 - c) for an E8M0 code c in [0, 254] (2^-127 is a binary32 subnormal).
+__device__ __forceinline__ float e8m0_inverse(uint32_t c) {
+  return c == 254u ? __uint_as_float(0x00400000u) : __uint_as_float((254u - c) << 23);
+}
+
+// Nearest-even E2M1 code of y, saturating at 6, keeping the sign bit.  The
+// magnitude code counts the midpoints |y| has passed; at a midpoint the
+// neighbour with mantissa bit 0 wins, hence the alternating > / >=.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+template <int BLK>
+__global__ void __launch_bounds__(256)
+    quantize_blocks(const uint16_t* __restrict__ x, int64_t rows_in, int64_t K,
+                    const float* __restrict__ gs_ptr, const int32_t* __restrict__ row_map,
+                    int64_t rows_out, uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  constexpr bool kNV = (BLK == 16);
+  constexpr int kWords = BLK / 2;  // bf16 pairs per block
+  const int64_t bpr = K / BLK;
+  const int64_t total = rows_out * bpr;
+  const float gs = kNV ? gs_ptr[0] : 1.0f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t r = i / bpr;
+    const int64_t b = i - r * bpr;
+    const int64_t src = row_map ? (int64_t)row_map[r] : r;
+    uint32_t w[kWords];
+    if (src >= 0 && src < rows_in) {
+      const uint4* p = reinterpret_cast<const uint4*>(x + src * K + b * BLK);
+#pragma unroll
+      for (int j = 0; j < kWords / 4; j++) {
+        const uint4 t = p[j];
+        w[4 * j + 0] = t.x;
+        w[4 * j + 1] = t.y;
+        w[4 * j + 2] = t.z;
+        w[4 * j + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWords; j++) w[j] = 0u;
+    }
+    float v[BLK];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWords; j++) {
+      v[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    uint32_t scode;
+    float inv;
+    if constexpr (kNV) {
+      const float s = (amax / 6.0f) * gs;
+      scode = e4m3_rne_satfinite(s);
+      const float sdec = e4m3_decode(scode);
+      inv = (sdec == 0.0f) ? 0.0f : gs / sdec;
+    } else {
+      scode = e8m0_ceil(amax / 6.0f);
+      inv = e8m0_inverse(scode);
+    }
+    uint32_t packed[BLK / 8];
+#pragma unroll
+    for (int j = 0; j < BLK / 8; j++) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t = 0; t < 8; t++) word |= e2m1_rne(v[8 * j + t] * inv) << (4 * t);
+      packed[j] = word;
+    }
+    uint8_t* qdst = q + r * (K / 2) + b * (BLK / 2);
+    if constexpr (kNV) {
+      *reinterpret_cast<uint2*>(qdst) = make_uint2(packed[0], packed[1]);
+    } else {
+      *reinterpret_cast<uint4*>(qdst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
+    sf[r * bpr + b] = (uint8_t)scode;
+  }
+}
+
+// Per-workgroup max |x| (grid-stride, 8 bf16 per 128-bit load).
+__global__ void __launch_bounds__(256)
+    amax_partial(const uint16_t* __restrict__ x, int64_t numel, float* __restrict__ partial) {
+  float m = 0.0f;
+  const int64_t nvec = numel / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  for (int64_t i = tid; i < nvec; i += stride) {
+    const uint4 t = xv[i];
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] >> 16)));
+    }
+  }
+  for (int64_t i = nvec * 8 + tid; i < numel; i += stride) m = fmaxf(m, fabsf(bf16_bits_to_float(x[i])));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ void __launch_bounds__(256)
+    global_scale_finalize(const float* __restrict__ partial, int n, float* __restrict__ gs) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    gs[0] = 2688.0f / amax;  // FLOAT8_E4M3_MAX * FLOAT4_E2M1_MAX / amax
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, const uint16_t* x, int64_t rows_in, int64_t K, const float* gs,
+                           const int32_t* row_map, int64_t rows_out, uint8_t* q, uint8_t* sf,
+                           hipStream_t stream) {
+  if (rows_out == 0) return hipSuccess;
+  const int blk = (fmt == 0) ? 16 : 32;
+  const int64_t items = rows_out * (K / blk);
+  const int64_t want = (items + 255) / 256;
+  const int grid = (int)(want < kQuantMaxGrid ? want : kQuantMaxGrid);
+  if (fmt == 0) {
+    quantize_blocks<16><<<grid, 256, 0, stream>>>(x, rows_in, K, gs, row_map, rows_out, q, sf);
+  } else {
+    quantize_blocks<32><<<grid, 256, 0, stream>>>(x, rows_in, K, nullptr, row_map, rows_out, q, sf);
+  }
+  return hipGetLastError();
+}
+
+int global_scale_parts(int64_t numel) {
+  const int64_t want = (numel / 8 + 255) / 256;
+  return (int)(want < 1 ? 1 : (want < kAmaxMaxParts ? want : kAmaxMaxParts));
+}
+
+hipError_t launch_global_scale(const uint16_t* x, int64_t numel, float* gs, float* partial,
+                               hipStream_t stream) {
+  const int parts = global_scale_parts(numel);
+  amax_partial<<<parts, 256, 0, stream>>>(x, numel, partial);
+  global_scale_finalize<<<1, 256, 0, stream>>>(partial, parts, gs);
+  return hipGetLastError();
+}
+
+}  // namespace bsfp4

@@ -1,0 +1,229 @@
+/*
+ * bsfp4.h -- block-scaled FP4 (E2M1) kernels for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsfp4.so.  Every entry point takes plain device pointers,
+ * element counts and a HIP stream passed as `void*` (a hipStream_t; NULL
+ * means the null stream).  No entry point allocates, frees or synchronises:
+ * the caller owns every buffer (inputs, outputs and workspace) and every
+ * call is asynchronous on the given stream.  Device-side faults surface at
+ * the caller's next synchronisation, as with any HIP call.
+ *
+ * Data formats (as named on the pages this library implements):
+ *   E2M1   4-bit float, values {0, 0.5, 1, 1.5, 2, 3, 4, 6} and negatives.
+ *          Packed two per byte along K; element 2j sits in the low nibble of
+ *          byte j (vLLM `sm103` branch comparison page,
+ *          `nvfp4_quant_kernels.cu`, `cvt_fp16_to_fp4_sm103`: the first
+ *          elements of a thread land in the low bits of the packed word).
+ *   E4M3   8-bit scale (OCP "fn": bias 7, max 448, NaN at 0x7F/0xFF); one
+ *          per 16 K-elements in the NVFP4 form (`float_ue4m3_t` block scales
+ *          of `Fp4GemmSm103`, same page, `nvfp4_scaled_mm_kernels.cu`).
+ *   E8M0   8-bit power-of-two scale 2^(c-127); one per 32 K-elements in the
+ *          MXFP4 form ("[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on SM12x").
+ *   bf16   activations and outputs, passed as 16-bit patterns.
+ * Scale tensors are row-major [rows, K/16] (NVFP4) or [rows, K/32] (MXFP4),
+ * one byte per block, unpadded and unswizzled.  Codes are row-major
+ * [rows, K/2].  Every matrix is contiguous.
+ *
+ * Errors: each call validates its arguments before any launch and returns a
+ * status; on error nothing is launched and bsfp4_last_error() returns a
+ * message for the calling thread.  Pointers must be 16-byte aligned
+ * (128-bit vector loads and stores), except the scalar `gs`/`alpha`
+ * pointers (4-byte aligned).  All entry points are thread-safe: the library
+ * keeps no state besides the per-thread error message.
+ */
+#ifndef BSFP4_H_
+#define BSFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define BSFP4_API __attribute__((visibility("default")))
+#else
+#define BSFP4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsfp4_status {
+  BSFP4_OK = 0,
+  BSFP4_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, negative size */
+  BSFP4_ERR_SHAPE = 2,       /* a size violates a divisibility or range rule */
+  BSFP4_ERR_ALIGNMENT = 3,   /* a pointer is not 16-byte (scalars: 4-byte) aligned */
+  BSFP4_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  BSFP4_ERR_DEVICE = 5,      /* the current device is not a gfx950 GPU */
+  BSFP4_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+} bsfp4_status;
+
+typedef enum bsfp4_format {
+  BSFP4_NVFP4 = 0, /* E2M1 values, E4M3 scale per 16 elements, FP32 global scale */
+  BSFP4_MXFP4 = 1  /* E2M1 values, E8M0 scale per 32 elements */
+} bsfp4_format;
+
+/* Library version (major*10000 + minor*100 + patch). */
+BSFP4_API int bsfp4_version(void);
+/* Static description of a status code. */
+BSFP4_API const char* bsfp4_status_string(int status);
+/* Message of the last failed call on the calling thread ("" if none). */
+BSFP4_API const char* bsfp4_last_error(void);
+
+/* ----------------------------------------------------------------------------
+ * fp4_global_scale: gs = 2688 / max|x| over a bf16 tensor (448 * 6 =
+ * FLOAT8_E4M3_MAX * FLOAT4_E2M1_MAX; vLLM `sm103` branch comparison page,
+ * `test_nvfp4_quant.py`, `test_scaled_fp4_quant_sm103_matches_sm100`).
+ *   x        device, numel bf16 values (16-byte aligned)
+ *   gs_out   device, one float written with fl32(2688 / amax); amax == 0
+ *            gives +inf (the caller must not quantise an all-zero tensor
+ *            with it)
+ *   ws       device workspace of fp4_global_scale_workspace_size(numel) bytes
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t fp4_global_scale_workspace_size(int64_t numel);
+BSFP4_API bsfp4_status fp4_global_scale(const uint16_t* x, int64_t numel, float* gs_out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * fp4_quantize: bf16 rows -> packed E2M1 codes + block scales.
+ * Defines the activation quantiser `cvt_fp16_to_fp4_sm103` (vLLM `sm103`
+ * branch comparison page, `nvfp4_quant_kernels.cu`) and the per-expert
+ * MXFP4 activation quant (`mxfp4_experts_quant`, "[Kernel] Enable CUTLASS
+ * MXFP4 W4A4 MoE on SM12x").  Per block of 16 (NVFP4) or 32 (MXFP4)
+ * elements v along a row:
+ *   NVFP4: s = fl32(fl32(amax/6) * gs); sf = E4M3 round-to-nearest-even of
+ *          s, saturating at 448; inv = fl32(gs / dec(sf)) (0 if dec(sf)==0)
+ *   MXFP4: sf = E8M0 of the smallest power of two >= fl32(amax/6);
+ *          inv = 2^(127-sf)
+ *   code  = E2M1 round-to-nearest-even of fl32(v * inv), saturating at 6,
+ *           sign bit kept (negative values that round to 0 give code 8).
+ *   fmt       BSFP4_NVFP4 or BSFP4_MXFP4
+ *   x         device bf16 [rows_in, K]
+ *   K         row length; K % 16 == 0 (NVFP4) or K % 32 == 0 (MXFP4), K > 0
+ *   gs        device float[1]; required for NVFP4, must be NULL for MXFP4
+ *   row_map   device int32[rows_out] or NULL.  If given, output row r
+ *             quantises input row row_map[r] (0 <= row_map[r] < rows_in;
+ *             out-of-range entries produce all-zero rows).  NULL means
+ *             rows_out == rows_in and row r -> row r.
+ *   q         device uint8 [rows_out, K/2]
+ *   sf        device uint8 [rows_out, K/16] or [rows_out, K/32]
+ * rows_out == 0 is a valid no-op.
+ * ------------------------------------------------------------------------- */
+BSFP4_API bsfp4_status fp4_quantize(int fmt, const uint16_t* x, int64_t rows_in, int64_t K,
+                          const float* gs, const int32_t* row_map, int64_t rows_out,
+                          uint8_t* q, uint8_t* sf, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * fp4_gemm: D[M,N] = bf16_rne(alpha * sum_k dec(A)[m,k] * dec(B)[n,k]).
+ * The W4A4 block-scaled GEMM of `Fp4GemmSm103` / `cutlass_scaled_fp4_mm`
+ * (vLLM `sm103` branch comparison page, `nvfp4_scaled_mm_kernels.cu` and
+ * `nvfp4_scaled_mm_entry.cu`) and CuTe-DSL `mm_fp4` ("perf(gemm): optimize
+ * SM103 CuTe DSL mm_fp4 kernel"); alpha multiplies the FP32 accumulator and
+ * the result is converted to bf16 once (that page, "Alpha epilogue bug").
+ *   fmt       BSFP4_NVFP4 (E4M3 scales per 16) or BSFP4_MXFP4 (E8M0 per 32)
+ *   A, SFA    device [M, K/2] codes, [M, K/16 or K/32] scales
+ *   B, SFB    device [N, K/2] codes, [N, K/16 or K/32] scales (row n holds
+ *             output column n's weights, contiguous along K)
+ *   alpha     device float[1]; NULL means 1.0
+ *   D         device bf16 [M, N]
+ *   sizes     M >= 0, N % 32 == 0, K % 32 == 0, N > 0, K > 0 (the pages'
+ *             `cutlass_scaled_fp4_mm_sm103a_impl` checks)
+ *   ws        device workspace of fp4_gemm_workspace_size(...) bytes (may be
+ *             NULL when that size is 0); its contents need no initialisation
+ * Results equal the float64 definition up to FP32 summation order.
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t fp4_gemm_workspace_size(int fmt, int64_t M, int64_t N, int64_t K);
+BSFP4_API bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                      const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M, int64_t N,
+                      int64_t K, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * w4a16_gemm: D[M,N] = bf16_rne(alpha * sum_k A[m,k] * dec(B)[n,k]) with bf16
+ * activations and NVFP4 weights ("feat: sm100 cute_dsl w4a16 gemm": bf16
+ * activations x native NVFP4 weights; the tensor-wide FP32 weight scale
+ * multiplies the FP32 accumulator in the epilogue).
+ *   A         device bf16 [M, K]
+ *   B, SFB    device [N, K/2] E2M1 codes, [N, K/16] E4M3 scales
+ *   alpha     device float[1]; NULL means 1.0
+ *   D         device bf16 [M, N]
+ *   sizes     M >= 0, N % 32 == 0, K % 32 == 0
+ *   ws        device workspace of w4a16_gemm_workspace_size(...) bytes
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+BSFP4_API bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
+                        const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * fp4_moe_prep: group routed (token, slot) pairs by expert.  Produces the
+ * per-expert row offsets that the pages' experts ops take
+ * (`input_offset_by_experts`, vLLM `sm103` branch comparison page,
+ * `csrc/ops.h`).
+ *   topk_ids        device int32 [T, topk], each in [0, E)
+ *   expert_offsets  device int32 [E+1]: rows of expert e are
+ *                   [offsets[e], offsets[e+1]); offsets[E] == T*topk
+ *   sorted_ids      device int32 [T*topk]: flat index t*topk+j of each row,
+ *                   stable within an expert (increasing flat index)
+ *   sorted_tokens   device int32 [T*topk] or NULL: token t = sorted_ids/topk
+ *                   of each row (the row_map of the experts quantiser)
+ *   ws              device workspace of fp4_moe_prep_workspace_size bytes
+ * Ids outside [0, E) are not checked on the device and give undefined
+ * groupings (never out-of-bounds writes: they are dropped).
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t fp4_moe_prep_workspace_size(int64_t T, int64_t topk, int64_t E);
+BSFP4_API bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E,
+                          int32_t* expert_offsets, int32_t* sorted_ids,
+                          int32_t* sorted_tokens, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * mxfp4_moe_grouped_gemm: for every expert e, rows [off[e], off[e+1]) of the
+ * expert-sorted MXFP4 activations times expert e's MXFP4 weights
+ * ("[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on SM12x": MXFP4 x MXFP4 grouped
+ * GEMM over per-expert weights).  alpha is 1.  A persistent grid walks the
+ * list of (expert, row tile, column tile) work items.
+ *   Aq, Asf          device [rows, K/2], [rows, K/32]; rows = T*topk
+ *   expert_offsets   device int32 [E+1] (from fp4_moe_prep)
+ *   W, Wsf           device [E, N, K/2], [E, N, K/32]
+ *   N % 64 == 0, K % 128 == 0
+ *   epilogue         one of bsfp4_moe_epilogue; its fields in `ep`:
+ *     BSFP4_MOE_STORE_BF16:  ep.out = bf16 [rows, N]
+ *     BSFP4_MOE_SILU_MUL_QUANT: act = bf16(silu(h[:, :N/2]) * h[:, N/2:])
+ *         with h the bf16-rounded GEMM row, then MXFP4-quantised into
+ *         ep.out_q [rows, N/4] and ep.out_sf [rows, N/64]
+ *         (the fused `silu_and_mul_scaled_fp4_experts_quant` pattern of
+ *         the vLLM page's `csrc/ops.h`, in its MXFP4 form)
+ *     BSFP4_MOE_WEIGHTED_COMBINE: ep.out = bf16 [T, N] with
+ *         out[t] = bf16(sum_j w[t,j] * Y[row(t,j)]), summed in FP32;
+ *         uses ep.sorted_ids, ep.topk_weights [T*topk], ep.num_tokens,
+ *         ep.topk, and T*N*4 bytes of workspace
+ *   ws               device workspace of
+ *                    mxfp4_moe_grouped_gemm_workspace_size(...) bytes
+ * ------------------------------------------------------------------------- */
+typedef enum bsfp4_moe_epilogue {
+  BSFP4_MOE_STORE_BF16 = 0,
+  BSFP4_MOE_SILU_MUL_QUANT = 1,
+  BSFP4_MOE_WEIGHTED_COMBINE = 2
+} bsfp4_moe_epilogue;
+
+typedef struct bsfp4_moe_epilogue_args {
+  void* out;                   /* bf16 output (STORE_BF16, WEIGHTED_COMBINE) */
+  uint8_t* out_q;              /* MXFP4 codes of act (SILU_MUL_QUANT) */
+  uint8_t* out_sf;             /* E8M0 scales of act (SILU_MUL_QUANT) */
+  const int32_t* sorted_ids;   /* WEIGHTED_COMBINE */
+  const float* topk_weights;   /* WEIGHTED_COMBINE, [num_tokens * topk] */
+  int64_t num_tokens;          /* WEIGHTED_COMBINE */
+  int64_t topk;                /* WEIGHTED_COMBINE */
+} bsfp4_moe_epilogue_args;
+
+BSFP4_API size_t mxfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K,
+                                             int epilogue, int64_t num_tokens);
+BSFP4_API bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf,
+                                    const int32_t* expert_offsets, int64_t E, int64_t rows,
+                                    const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                    int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFP4_H_ */

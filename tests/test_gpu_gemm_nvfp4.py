@@ -1,0 +1,120 @@
+"""GPU parity: NVFP4 W4A4 fp4_gemm against the float64 oracle.
+
+Tolerance (the acceptance rule of oracle/tolerance.py, checked element by
+element): |D - Dref| <= 8e-3 |Dref| + 1e-3 rms(Dref), Dref = bf16(float64 result).
+Shapes span several 256x256 tiles, ragged M/N/K tails, M = 1 and the
+workload sizes; at the largest size the oracle computes sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_e2m1_amd as bs
+from block_scaled_fp4_e2m1_amd import synth
+from oracle import formats as F
+from oracle import gemm as OG
+from oracle import tolerance as TOL
+from gpu_helpers import dev_f32, dev_u8, host_bf16_bits, nvfp4_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(aq, sfa, bq, sfb, alpha):
+    d = bs.gemm(dev_u8(aq), dev_u8(sfa), dev_u8(bq), dev_u8(sfb),
+                None if alpha is None else dev_f32([alpha]), fmt="nvfp4")
+    torch.cuda.synchronize()
+    return host_bf16_bits(d)
+
+
+def _check(got, aq, sfa, bq, sfb, alpha, rows=None):
+    a = 1.0 if alpha is None else alpha
+    if rows is None:
+        want = OG.nvfp4_gemm(aq, sfa, bq, sfb, a)
+        ok, worst, nbad = TOL.check_bf16(got, want)
+    else:
+        want = OG.nvfp4_gemm(aq[rows], sfa[rows], bq, sfb, a)
+        ok, worst, nbad = TOL.check_bf16(got[rows], want)
+    assert ok, f"{nbad} elements out of tolerance (worst ratio {worst:.2f})"
+    return worst
+
+
+SHAPES = [
+    (1, 32, 32), (5, 64, 96), (32, 32, 128), (64, 256, 256), (255, 288, 416),
+    (256, 256, 7168), (300, 544, 1056), (513, 768, 2048),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_nvfp4_gemm_random(M, N, K):
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=10 + M)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+def test_nvfp4_gemm_every_scale_code():
+    """Random codes with every finite E4M3 scale code (incl. subnormal scales)."""
+    M, N, K = 96, 160, 512
+    aq = synth.random_bytes(1, (M, K // 2))
+    bq = synth.random_bytes(2, (N, K // 2))
+    sfa = synth.random_e4m3_scales(3, (M, K // 16), 0x00, 0x7F)
+    sfb = synth.random_e4m3_scales(4, (N, K // 16), 0x00, 0x50)
+    got = _run(aq, sfa, bq, sfb, np.float32(0.01))
+    _check(got, aq, sfa, bq, sfb, np.float32(0.01))
+
+
+def test_nvfp4_gemm_zero_blocks_and_no_alpha():
+    M, N, K = 64, 96, 256
+    aq, sfa, bq, sfb, _ = nvfp4_problem(M, N, K, seed=5)
+    aq[:, 32:64] = 0          # zero a whole 64-element K range in A
+    sfb[:, 3] = 0             # zero scale block in B
+    got = _run(aq, sfa, bq, sfb, None)
+    _check(got, aq, sfa, bq, sfb, None)
+
+
+def test_nvfp4_gemm_small_m_workload():
+    """The memory-bound workload shape: M=16, N=4096, K=7168 (full check)."""
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(16, 4096, 7168, seed=100)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_nvfp4_gemm_sweep_small(M):
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, 4096, 7168, seed=122 + M)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+def test_nvfp4_gemm_large_workload_sampled():
+    """4096 x 4096 x 7168: every output of 48 sampled rows (incl. first/last)."""
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(4096, 4096, 7168, seed=120)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    rows = np.unique(np.concatenate([[0, 255, 256, 4095],
+                                     np.random.default_rng(0).choice(4096, 44, replace=False)]))
+    _check(got, aq, sfa, bq, sfb, alpha, rows=rows)
+
+
+def test_nvfp4_gemm_deterministic():
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(300, 512, 1024, seed=7)
+    g1 = _run(aq, sfa, bq, sfb, alpha)
+    g2 = _run(aq, sfa, bq, sfb, alpha)
+    assert np.array_equal(g1, g2)
+
+
+def test_nvfp4_gemm_m_zero():
+    d = bs.gemm(dev_u8(np.zeros((0, 16), np.uint8)), dev_u8(np.zeros((0, 2), np.uint8)),
+                dev_u8(np.zeros((32, 16), np.uint8)), dev_u8(np.zeros((32, 2), np.uint8)))
+    assert d.shape == (0, 32)
+
+
+def test_nvfp4_gemm_output_guard_band():
+    """Writes stay inside D: canaries around a ragged output are untouched."""
+    M, N, K = 37, 96, 160
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=9)
+    buf = torch.full((M * N + 2 * 4096,), 0x7E57, dtype=torch.int16, device="cuda:0")
+    out = buf[4096:4096 + M * N].view(M, N).view(torch.bfloat16)
+    bs.gemm(dev_u8(aq), dev_u8(sfa), dev_u8(bq), dev_u8(sfb), dev_f32([alpha]), out=out)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy()
+    assert np.all(h[:4096] == 0x7E57) and np.all(h[4096 + M * N:] == 0x7E57)
+    _check(host_bf16_bits(out), aq, sfa, bq, sfb, alpha)
