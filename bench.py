@@ -1,0 +1,307 @@
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-rows]
+
+Headline (one JSON line on stdout): the NVFP4 W4A4 GEMM at M=4096, N=4096,
+K=7168 -- A and B bf16 ~ N(0,1) from seeds 120/121, quantised on the GPU by
+this library's quantiser with the tensor-amax global scales, alpha =
+1/(gsA*gsB), bf16 output.  One step = one fp4_gemm launch; W warm-up steps,
+then K timed steps bracketed by device synchronisation; value = algorithmic
+TFLOP/s (2*M*N*K per step).
+
+The same line carries:
+  roofline      the GEMM kernel's achieved rate from HIP events on the
+                launch stream against the fp16 dense MFMA peak it computes
+                with (2.5 PFLOP/s), plus the measured HBM traffic when the
+                committed counter summary matches the current kernel source;
+  cpu_baseline  the float64 CPU oracle timed on this host on the same inputs;
+  rows          the other hot-path rows (quantiser, small-M GEMM, W4A16,
+                MXFP4 GEMM, MoE layer) with per-launch times, cold and warm.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOPS at 4096x4096x7168 (% FP4 MFMA peak); GB/s at M=16"
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "fp4": 10100.0, "fp8": 5000.0}  # dense TFLOP/s
+HBM_PEAK_GBS = 8000.0
+PUBLISHED_TFLOPS = 6549.9  # B300 SM103 CuTe-DSL mm_fp4 at 4096x4096x7168 (context)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-rows", action="store_true", help="only the headline GEMM")
+    p.add_argument("--rows-only", default="", help="comma list of rows to run")
+    return p.parse_args()
+
+
+def src_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "block_scaled_fp4_e2m1_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_key: str, source: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    e = tab.get(kernel_key)
+    if not e or e.get("source_sha") != src_sha(source):
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Timer:
+    """Per-launch durations with HIP events recorded on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+
+    def run(self, fn, iters=20, warmup=3, cold=False):
+        t = self.torch
+        for _ in range(warmup):
+            fn()
+        t.cuda.synchronize()
+        times = []
+        for _ in range(iters):
+            if cold:
+                self.flush.zero_()  # evicts L2 and the 256 MB MALL
+            e0 = t.cuda.Event(enable_timing=True)
+            e1 = t.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        a = np.array(times)
+        return {"median_us": float(np.median(a)), "p10_us": float(np.percentile(a, 10)),
+                "p90_us": float(np.percentile(a, 90))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_scaled_fp4_e2m1_amd as bs
+    from block_scaled_fp4_e2m1_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------------------------------------------------------- inputs
+    M, N, K = 4096, 4096, 7168
+    a = bf16(synth.bf16_normal(120, (M, K)))
+    b = bf16(synth.bf16_normal(121, (N, K)))
+    gsa, gsb = bs.global_scale(a), bs.global_scale(b)
+    aq, sfa = bs.quantize(a, "nvfp4", gs=gsa)
+    bq, sfb = bs.quantize(b, "nvfp4", gs=gsb)
+    g = torch.cat([gsa, gsb]).cpu().numpy()
+    alpha = torch.tensor([np.float32(1.0) / np.float32(g[0] * g[1])], dtype=torch.float32, device=dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
+
+    # ---------------------------------------------------------------- timed region
+    print(f"[bench] headline: {args.warmup} warm-up + {args.steps} timed steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    alg_bytes = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 4 + 2 * M * N
+
+    traffic = stored_traffic("nvfp4_gemm_4096x4096x7168", "gemm_nvfp4.hip")
+    roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK["f16"], "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK["f16"], 4), "traffic": traffic,
+                "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4),
+                "algorithmic_bytes": alg_bytes}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PUBLISHED_TFLOPS, 4),
+        "vs_baseline_ref": "B300 SM103 CuTe-DSL mm_fp4, 6549.9 TFLOPS (other hardware; context)",
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "nvfp4_gemm_4096x4096x7168", "M": M, "N": N, "K": K,
+                   "operands": "NVFP4 (E2M1 + E4M3/16 + fp32 alpha)", "output": "bf16",
+                   "mfma": "v_mfma_f32_32x32x16_f16 on exactly dequantised operands",
+                   "timed_wall_s": round(wall, 4)},
+        "roofline": roofline,
+    }
+
+    # ---------------------------------------------------------------- other rows
+    if not args.no_rows:
+        only = [r for r in args.rows_only.split(",") if r]
+        out["rows"] = run_rows(torch, bs, synth, Timer(torch), only)
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(aq, sfa, bq, sfb, alpha, D)
+
+    print(json.dumps(out), flush=True)
+
+
+def _nv_bytes(M, N, K):
+    return M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 4 + 2 * M * N
+
+
+def _rate(t, flops=None, nbytes=None):
+    r = dict(t)
+    us = t["median_us"]
+    if flops:
+        r["tflops"] = round(flops / us / 1e6, 2)
+        r["frac_f16_peak"] = round(flops / us / 1e6 / PEAK["f16"], 4)
+        r["frac_fp4_peak"] = round(flops / us / 1e6 / PEAK["fp4"], 4)
+    if nbytes:
+        r["gbs"] = round(nbytes / us / 1e3, 1)
+        r["frac_hbm"] = round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)
+    return r
+
+
+def run_rows(torch, bs, synth, timer, only):
+    dev = "cuda:0"
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def want(name):
+        if only and name not in only:
+            return False
+        print(f"[bench] row {name}", file=sys.stderr, flush=True)
+        return True
+
+    rows = {}
+
+    def nv_inputs(M, N, K, sa, sb, b_std=1.0, outliers=False):
+        a = bf16(synth.bf16_normal_with_outliers(sa, sa + 1000, (M, K)) if outliers
+                 else synth.bf16_normal(sa, (M, K)))
+        b = bf16(synth.bf16_normal(sb, (N, K), b_std))
+        gsa, gsb = bs.global_scale(a), bs.global_scale(b)
+        aq, sfa = bs.quantize(a, "nvfp4", gs=gsa)
+        bq, sfb = bs.quantize(b, "nvfp4", gs=gsb)
+        g = torch.cat([gsa, gsb]).cpu().numpy()
+        alpha = torch.tensor([np.float32(1.0) / np.float32(g[0] * g[1])], device=dev)
+        return a, gsa, aq, sfa, bq, sfb, alpha
+
+    # a3/a4 at the memory-bound workload: M=16, N=4096, K=7168 (HBM roofline)
+    if want("nvfp4_gemm_16x4096x7168"):
+        M, N, K = 16, 4096, 7168
+        _, _, aq, sfa, bq, sfb, alpha = nv_inputs(M, N, K, 100, 101)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fn = lambda: bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
+        rows["nvfp4_gemm_16x4096x7168"] = {
+            "cold": _rate(timer.run(fn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+            "warm": _rate(timer.run(fn), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+            "bound": "hbm", "algorithmic_bytes": _nv_bytes(M, N, K)}
+
+    # a3 sweep at N=4096, K=7168
+    if want("nvfp4_gemm_sweep"):
+        sweep = {}
+        for i, M in enumerate([1, 64, 512, 2048]):
+            N, K = 4096, 7168
+            _, _, aq, sfa, bq, sfb, alpha = nv_inputs(M, N, K, 122 + i, 121)
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = lambda: bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
+            sweep[f"M={M}"] = _rate(timer.run(fn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K))
+        rows["nvfp4_gemm_sweep_cold"] = sweep
+
+    # a1 + a3: quantise bf16 activations, then the NVFP4 GEMM (M=256, N=14336, K=4096)
+    if want("quant_then_gemm_256x14336x4096"):
+        M, N, K = 256, 14336, 4096
+        x, gsx, _, _, wq, wsf, alpha = nv_inputs(M, N, K, 110, 112, b_std=0.02, outliers=True)
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xsf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        qfn = lambda: bs.quantize(x, "nvfp4", gs=gsx, q=xq, sf=xsf)
+        gfn = lambda: bs.gemm(xq, xsf, wq, wsf, alpha, out=D)
+
+        def both():
+            qfn()
+            gfn()
+        qbytes = 2 * M * K + M * K // 2 + M * K // 16 + 4
+        rows["quant_then_gemm_256x14336x4096"] = {
+            "quant_cold": _rate(timer.run(qfn, cold=True), None, qbytes),
+            "gemm_cold": _rate(timer.run(gfn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+            "pipeline_cold": _rate(timer.run(both, cold=True), 2.0 * M * N * K),
+            "pipeline_warm": _rate(timer.run(both), 2.0 * M * N * K)}
+    return rows
+
+
+def cpu_baseline(aq, sfa, bq, sfb, alpha, D):
+    """The float64 oracle on the same quantised inputs, timed on this host.
+
+    Sample: 512 of the 4096 rows of A (every column, all of K): dequantise
+    A-sample and B exactly to float64, one float64 matmul, bf16 rounding.
+    The GPU output on those rows is also checked against it."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as OG
+    from oracle import tolerance as TOL
+
+    rows = np.arange(0, 4096, 8)
+    A = aq.cpu().numpy()[rows]
+    SA = sfa.cpu().numpy()[rows]
+    B = bq.cpu().numpy()
+    SB = sfb.cpu().numpy()
+    al = float(alpha.cpu().numpy()[0])
+    t0 = time.perf_counter()
+    ref = OG.nvfp4_gemm(A, SA, B, SB, al)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * B.shape[0] * B.shape[1] * 2
+    got = D.view(__import__("torch").int16).cpu().numpy().view(np.uint16)[rows]
+    ok, worst, nbad = TOL.check_bf16(got, ref)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(rows)} of 4096 rows of A x all 4096 columns x K=7168 "
+                      "(exact float64 dequant + float64 matmul + bf16 rounding)",
+            "parity_on_sample": {"ok": ok, "worst_ratio": round(worst, 4), "n_bad": nbad}}
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,9 @@ SOURCES = [
     "api.cpp",
     "quantize.hip",
     "gemm_nvfp4.hip",
+    "gemm_skinny.hip",
+    "gemm_mxfp4.hip",
+    "moe.hip",
 ]
 
 ARCH = "gfx950"

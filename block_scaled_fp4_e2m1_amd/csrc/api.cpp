@@ -187,7 +187,152 @@ bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8
   if (fmt == BSFP4_NVFP4)
     return launched(bsfp4::launch_nvfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, ws, ws_bytes, as_stream(stream)),
                     "fp4_gemm launch");
-  return fail(BSFP4_ERR_INVALID_ARG, "MXFP4 dense GEMM is not available yet");
+  return launched(bsfp4::launch_mxfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, as_stream(stream)),
+                  "fp4_gemm launch");
+}
+
+// ------------------------------------------------------------------ W4A16
+
+size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;
+}
+
+bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                        uint16_t* D, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                        void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need M >= 0, N > 0, K > 0 (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+  if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
+  if (M > 0) {
+    REQUIRE_PTR(A);
+    REQUIRE_PTR(D);
+  }
+  REQUIRE_PTR(B);
+  REQUIRE_PTR(SFB);
+  if (alpha != nullptr && !aligned(alpha, 4)) return fail(BSFP4_ERR_ALIGNMENT, "alpha is not 4-byte aligned");
+  if (M == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  // rows in chunks of kSkinnyMaxM (the weight stream is re-read once per chunk)
+  for (int64_t m0 = 0; m0 < M; m0 += bsfp4::kSkinnyMaxM) {
+    const int64_t mc = (M - m0 < bsfp4::kSkinnyMaxM) ? (M - m0) : bsfp4::kSkinnyMaxM;
+    hipError_t e = bsfp4::launch_skinny_w4a16(A + m0 * K, B, SFB, alpha, D + m0 * N, mc, N, K, as_stream(stream));
+    if (e != hipSuccess) return launched(e, "w4a16_gemm launch");
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ MoE
+
+size_t fp4_moe_prep_workspace_size(int64_t T, int64_t topk, int64_t E) {
+  (void)T;
+  (void)topk;
+  (void)E;
+  return 0;
+}
+
+bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E,
+                          int32_t* expert_offsets, int32_t* sorted_ids, int32_t* sorted_tokens, void* ws,
+                          size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (T < 0 || topk <= 0 || E <= 0 || E > bsfp4::kMaxExperts)
+    return fail(BSFP4_ERR_SHAPE, "need T >= 0, topk > 0, 0 < E <= %lld (T=%lld topk=%lld E=%lld)",
+                (long long)bsfp4::kMaxExperts, (long long)T, (long long)topk, (long long)E);
+  if (T * topk > INT32_MAX) return fail(BSFP4_ERR_SHAPE, "T*topk must fit in 31 bits");
+  if (T > 0) {
+    REQUIRE_PTR(topk_ids);
+    if (sorted_ids == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "sorted_ids is NULL");
+    if (!aligned(sorted_ids, 4)) return fail(BSFP4_ERR_ALIGNMENT, "sorted_ids is not 4-byte aligned");
+    if (sorted_tokens != nullptr && !aligned(sorted_tokens, 4))
+      return fail(BSFP4_ERR_ALIGNMENT, "sorted_tokens is not 4-byte aligned");
+  }
+  if (expert_offsets == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "expert_offsets is NULL");
+  if (!aligned(expert_offsets, 4)) return fail(BSFP4_ERR_ALIGNMENT, "expert_offsets is not 4-byte aligned");
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_moe_prep(topk_ids, T, topk, E, expert_offsets, sorted_ids, sorted_tokens,
+                                         as_stream(stream)),
+                  "fp4_moe_prep launch");
+}
+
+size_t mxfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K, int epilogue,
+                                             int64_t num_tokens) {
+  (void)rows;
+  (void)E;
+  (void)K;
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE && num_tokens > 0 && N > 0)
+    return (size_t)num_tokens * (size_t)N * sizeof(float);
+  return 0;
+}
+
+bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, const int32_t* expert_offsets,
+                                    int64_t E, int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N,
+                                    int64_t K, int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (epilogue != BSFP4_MOE_STORE_BF16 && epilogue != BSFP4_MOE_SILU_MUL_QUANT &&
+      epilogue != BSFP4_MOE_WEIGHTED_COMBINE)
+    return fail(BSFP4_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+  if (ep == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep is NULL");
+  if (rows < 0 || E <= 0 || E > bsfp4::kMaxExperts || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0, 0 < E <= %lld, N > 0, K > 0", (long long)bsfp4::kMaxExperts);
+  if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+  if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
+  if (epilogue == BSFP4_MOE_SILU_MUL_QUANT && N % 64)
+    return fail(BSFP4_ERR_SHAPE, "SILU_MUL_QUANT needs N %% 64 == 0 (got N=%lld)", (long long)N);
+  if (rows > INT32_MAX || E * N * (K / 2) > ((int64_t)1 << 40))
+    return fail(BSFP4_ERR_SHAPE, "problem too large");
+  REQUIRE_PTR(W);
+  REQUIRE_PTR(Wsf);
+  REQUIRE_PTR(expert_offsets);
+  const int64_t T = ep->num_tokens;
+  if (rows > 0) {
+    REQUIRE_PTR(Aq);
+    REQUIRE_PTR(Asf);
+    if (epilogue == BSFP4_MOE_STORE_BF16) {
+      if (ep->out == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep.out is NULL");
+      if (!aligned(ep->out, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out is not 16-byte aligned");
+    } else if (epilogue == BSFP4_MOE_SILU_MUL_QUANT) {
+      if (ep->out_q == nullptr || ep->out_sf == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep.out_q/out_sf is NULL");
+      if (!aligned(ep->out_q, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out_q is not 16-byte aligned");
+    }
+  }
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
+    if (T <= 0 || ep->topk <= 0 || T * ep->topk != rows)
+      return fail(BSFP4_ERR_SHAPE, "WEIGHTED_COMBINE needs num_tokens*topk == rows (T=%lld topk=%lld rows=%lld)",
+                  (long long)T, (long long)ep->topk, (long long)rows);
+    if (ep->out == nullptr || ep->sorted_ids == nullptr || ep->topk_weights == nullptr)
+      return fail(BSFP4_ERR_INVALID_ARG, "ep.out / sorted_ids / topk_weights is NULL");
+    if (!aligned(ep->out, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out is not 16-byte aligned");
+    const size_t need = mxfp4_moe_grouped_gemm_workspace_size(rows, E, N, K, epilogue, T);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+  }
+  if (bsfp4_status s = check_device()) return s;
+  const hipStream_t st = as_stream(stream);
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
+    float* acc = static_cast<float*>(ws);
+    hipError_t e = bsfp4::launch_fill_zero(acc, T * N, st);
+    if (e == hipSuccess && rows > 0)
+      e = bsfp4::launch_mxfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, N, K, bsfp4::kEpiCombine, nullptr,
+                                      nullptr, nullptr, ep->sorted_ids, ep->topk_weights, ep->topk, acc, st);
+    if (e == hipSuccess) e = bsfp4::launch_f32_to_bf16(acc, static_cast<uint16_t*>(ep->out), T * N, st);
+    return launched(e, "mxfp4_moe_grouped_gemm launch");
+  }
+  if (rows == 0) return ok();
+  return launched(bsfp4::launch_mxfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, N, K,
+                                              epilogue == BSFP4_MOE_STORE_BF16 ? bsfp4::kEpiStore : bsfp4::kEpiSilu,
+                                              static_cast<uint16_t*>(ep->out), ep->out_q, ep->out_sf, nullptr,
+                                              nullptr, 0, nullptr, st),
+                  "mxfp4_moe_grouped_gemm launch");
 }
 
 }  // extern "C"

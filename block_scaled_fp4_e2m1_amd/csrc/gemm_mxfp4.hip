@@ -1,0 +1,434 @@
+// MXFP4 W4A4 GEMM on gfx950's scaled FP4 MFMA, dense and grouped by expert.
+//
+//   dense:    D[m, n]  = bf16(alpha * sum_k dec(A)[m,k] * dec(B)[n,k])
+//   grouped:  rows [off[e], off[e+1]) of A times expert e's weights W[e]
+//
+// The MXFP4 form of the block-scaled GEMM (E2M1 values, one E8M0 scale per 32
+// K-elements) and the MXFP4 x MXFP4 per-expert grouped GEMM of "[Kernel]
+// Enable CUTLASS MXFP4 W4A4 MoE on SM12x".  Its scales are exactly what
+// v_mfma_scale_f32_32x32x64_f8f6f4 applies: lane l supplies 32 E2M1 values of
+// row l%32 (K group l/32) in 16 bytes plus that block's E8M0 byte, so the
+// packed codes and scale bytes go from HBM to the matrix cores untouched.
+//
+// One workgroup = 256 threads = 4 waves (2 x 2), BM x BN tile, K in stages of
+// SK = 128 or 256 values (SK/2 code bytes + SK/32 scale bytes per row), register-staged prefetch one
+// stage ahead, double-buffered LDS with a 16-byte-chunk swizzle that keeps the
+// fragment reads conflict-free.  The grid is persistent: each workgroup walks
+// a list of (group, column tile, row tile) work items with row tiles innermost;
+// consecutive items are assigned to workgroups of the same XCD so that row tiles
+// that share a weight panel run on one L2.  The item list is built in LDS from
+// the per-expert offsets at kernel start: a group with m rows contributes
+// ceil(m / BM) * ceil(N / BN) items, so the load follows the routing.
+//
+// Epilogues:
+//   STORE    alpha * acc -> bf16 rows;
+//   SILU     the tile's columns are gate/up pairs: column blocks of 32 alternate
+//            gate rows [32b, 32b+32) and up rows [N/2 + 32b, ...) of W, so a lane
+//            holds gate and up of the same element; act = bf16(silu(h_g) * h_u)
+//            from the bf16-rounded h, staged in LDS and re-quantised to MXFP4 per
+//            32-element block (the fused `silu_and_mul_scaled_fp4_experts_quant`
+//            pattern of the vLLM `sm103` branch comparison page, MXFP4 form);
+//   COMBINE  out_f32[token] += topk_weight * acc with hardware float atomics
+//            (summation order across a token's experts is not fixed).
+#include "device_common.h"
+#include "launchers.h"
+#include "quant_device.h"
+
+namespace bsfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Stage geometry for SK K-values per stage: SK/2 code bytes (SK/32 chunks of 16
+// bytes) and SK/32 E8M0 bytes per row.
+template <int SK>
+struct Geo {
+  static constexpr int kRowBytes = SK / 2;
+  static constexpr int kChunks = SK / 32;   // 16-byte chunks per row
+  static constexpr int kRowScales = SK / 32;
+  // chunk position inside the row: 8 (or 16) lanes reading the same logical
+  // chunk of 8 (or 16) consecutive rows hit distinct 16-byte bank groups
+  __device__ static __forceinline__ int swz(int r, int c) {
+    if constexpr (kChunks == 8) return c ^ ((r ^ (r >> 3)) & 7);
+    else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+  }
+};
+
+template <int ROWS, int SK>
+struct Stage {
+  static constexpr int kChunks = ROWS * Geo<SK>::kChunks / kThreads;
+  uint4 code[kChunks];
+  uint32_t sc[Geo<SK>::kRowScales / 4];
+};
+
+// Loads one stage of ROWS rows.  Row i of the tile is global row rowmap(i);
+// rows at or beyond `nvalid` (and rowmap < 0) read as zero.
+template <int ROWS, int SK, class RowMap>
+__device__ __forceinline__ void load_stage(Stage<ROWS, SK>& st, const uint8_t* __restrict__ q,
+                                           const uint8_t* __restrict__ sf, RowMap rowmap, int nvalid,
+                                           int K, int k0, bool sc_aligned, int tid) {
+  using Gm = Geo<SK>;
+  const int row_bytes = K / 2, row_blocks = K / 32;
+#pragma unroll
+  for (int i = 0; i < Stage<ROWS, SK>::kChunks; i++) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
+    const int gr = rowmap(r);
+    const int kb = k0 / 2 + c * 16;
+    st.code[i] = (gr >= 0 && gr < nvalid && kb < row_bytes)
+                     ? *reinterpret_cast<const uint4*>(q + (int64_t)gr * row_bytes + kb)
+                     : make_uint4(0, 0, 0, 0);
+  }
+  if (tid < ROWS) {
+    constexpr int kW = Gm::kRowScales / 4;  // scale words per row per stage
+    const int gr = rowmap(tid);
+#pragma unroll
+    for (int j = 0; j < kW; j++) st.sc[j] = 0;
+    if (gr >= 0 && gr < nvalid) {
+      const int b0 = k0 / 32;
+      const uint8_t* p = sf + (int64_t)gr * row_blocks;
+      if (sc_aligned && b0 + Gm::kRowScales <= row_blocks) {
+        if constexpr (kW == 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(p + b0);
+          st.sc[0] = v.x;
+          st.sc[1] = v.y;
+        } else {
+          st.sc[0] = *reinterpret_cast<const uint32_t*>(p + b0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < Gm::kRowScales; j++) {
+          const uint32_t b = (b0 + j < row_blocks) ? p[b0 + j] : 0u;
+          st.sc[j / 4] |= b << (8 * (j % 4));
+        }
+      }
+    }
+  }
+}
+
+template <int ROWS, int SK>
+__device__ __forceinline__ void store_stage(const Stage<ROWS, SK>& st, uint8_t* lq, uint8_t* ls, int tid) {
+  using Gm = Geo<SK>;
+#pragma unroll
+  for (int i = 0; i < Stage<ROWS, SK>::kChunks; i++) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
+    *reinterpret_cast<uint4*>(lq + r * Gm::kRowBytes + Gm::swz(r, c) * 16) = st.code[i];
+  }
+  if (tid < ROWS) {
+    if constexpr (Gm::kRowScales == 8)
+      *reinterpret_cast<uint2*>(ls + tid * 8) = make_uint2(st.sc[0], st.sc[1]);
+    else
+      *reinterpret_cast<uint32_t*>(ls + tid * 4) = st.sc[0];
+  }
+}
+
+struct Args {
+  const uint8_t* A;
+  const uint8_t* SFA;
+  int rows;
+  const int32_t* offsets;  // nullptr: one group holding every row
+  int E;
+  const uint8_t* W;
+  const uint8_t* WSF;
+  int N;
+  int K;
+  const float* alpha;
+  uint16_t* out;           // STORE: bf16 [rows, N]
+  uint8_t* out_q;          // SILU: [rows, N/4]
+  uint8_t* out_sf;         // SILU: [rows, N/64]
+  const int32_t* sorted_ids;  // COMBINE
+  const float* topk_w;        // COMBINE
+  int topk;                   // COMBINE
+  float* acc_f32;             // COMBINE: [T, N]
+};
+
+constexpr int kMaxGroups = (int)kMaxExperts;
+
+template <int BM, int BN, int SK, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
+  using Gm = Geo<SK>;
+  constexpr int kRowBytes = Gm::kRowBytes, kRowScales = Gm::kRowScales;
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
+  constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
+  static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ int tile_start[kMaxGroups + 1];
+  __shared__ int wave_sum[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, g = lane >> 5;
+  const int ntn = (p.N + BN - 1) / BN;
+  const int K = p.K;
+  const bool sc_aligned = ((K / 32) % kRowScales) == 0;
+
+  // ---- work list: tile_start[e] = items of groups before e
+  int total;
+  if (p.offsets == nullptr) {
+    total = ((p.rows + BM - 1) / BM) * ntn;
+  } else {
+    // each thread owns up to 4 consecutive groups; block-wide exclusive scan
+    int cnt[4];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = tid * 4 + j;
+      int c = 0;
+      if (e < p.E) {
+        const int m = p.offsets[e + 1] - p.offsets[e];
+        c = ((m + BM - 1) / BM) * ntn;
+      }
+      cnt[j] = c;
+      local += c;
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    int base = incl - local;
+    for (int w = 0; w < wave; w++) base += wave_sum[w];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = tid * 4 + j;
+      if (e < p.E) tile_start[e] = base;
+      base += cnt[j];
+    }
+    if (tid == 255) tile_start[p.E] = base;  // thread 255 owns the last groups
+    __syncthreads();
+    total = tile_start[p.E];
+  }
+
+  const int G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const float alpha = p.alpha ? p.alpha[0] : 1.0f;
+
+  for (int t = slot; t < total; t += G) {
+    // ---- locate the work item
+    int e = 0, row0, row_end, nmt;
+    if (p.offsets == nullptr) {
+      nmt = (p.rows + BM - 1) / BM;
+      row0 = 0;
+      row_end = p.rows;
+    } else {
+      int lo = 0, hi = p.E - 1;  // largest e with tile_start[e] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+      row0 = p.offsets[e];
+      row_end = p.offsets[e + 1];
+      nmt = (row_end - row0 + BM - 1) / BM;
+    }
+    const int local = t - (p.offsets ? tile_start[e] : 0);
+    const int tn = local / nmt, tmi = local % nmt;
+    const int m0 = row0 + tmi * BM;
+    const int nvalid_a = row_end < p.rows ? row_end : p.rows;
+    const uint8_t* Wq = p.W + (int64_t)e * p.N * (K / 2);
+    const uint8_t* Ws = p.WSF + (int64_t)e * p.N * (K / 32);
+
+    auto amap = [&](int i) { return m0 + i; };
+    auto bmap = [&](int i) -> int {
+      if constexpr (EPI == kEpiSilu) {
+        // LDS row i: wave column half wc = i / WN, column tile jn = (i % WN) / 32;
+        // even jn = gate, odd jn = up, act block b = tn*(BN/64) + wc*(TN/2) + jn/2
+        const int wc = i / WN, jn = (i % WN) >> 5;
+        const int b = tn * (BN / 64) + wc * (TN / 2) + (jn >> 1);
+        if (32 * b >= p.N / 2) return -1;
+        return ((jn & 1) ? p.N / 2 : 0) + 32 * b + (i & 31);
+      } else {
+        return tn * BN + i;
+      }
+    };
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
+
+    const int nst = (K + SK - 1) / SK;
+    Stage<BM, SK> ra;
+    Stage<BN, SK> rb;
+    load_stage<BM, SK>(ra, p.A, p.SFA, amap, nvalid_a, K, 0, sc_aligned, tid);
+    load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
+    store_stage<BM, SK>(ra, smem, smem + kA + kB, tid);
+    store_stage<BN, SK>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
+    __syncthreads();
+
+    for (int s = 0; s < nst; s++) {
+      const bool more = s + 1 < nst;
+      if (more) {
+        load_stage<BM, SK>(ra, p.A, p.SFA, amap, nvalid_a, K, (s + 1) * SK, sc_aligned, tid);
+        load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
+      }
+      const uint8_t* st = smem + (s & 1) * kStage;
+      const uint8_t* qa = st;
+      const uint8_t* qb = st + kA;
+      const uint8_t* sa = st + kA + kB;
+      const uint8_t* sb = sa + BM * kRowScales;
+#pragma unroll
+      for (int j = 0; j < SK / 64; j++) {
+        const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
+        v8i fb[TN];
+        int xb[TN];
+#pragma unroll
+        for (int i = 0; i < TN; i++) {
+          const int r = wn * WN + i * 32 + lr;
+          const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
+          fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          xb[i] = sb[r * kRowScales + c];
+        }
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+          const int r = wm * WM + i * 32 + lr;
+          const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
+          const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          const int xa = sa[r * kRowScales + c];
+#pragma unroll
+          for (int jn = 0; jn < TN; jn++)
+            acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
+                                                                         0, xb[jn]);
+        }
+      }
+      if (more) {
+        uint8_t* nx = smem + ((s + 1) & 1) * kStage;
+        store_stage<BM, SK>(ra, nx, nx + kA + kB, tid);
+        store_stage<BN, SK>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
+      }
+      __syncthreads();
+    }
+
+    // ---- epilogues.  acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) + 4g + r%4,
+    //      tile column wn*WN + 32jn + lr.
+    if constexpr (EPI == kEpiStore) {
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int jn = 0; jn < TN; jn++) {
+          const int n = tn * BN + wn * WN + jn * 32 + lr;
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (m < nvalid_a && n < p.N)
+              p.out[(int64_t)m * p.N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][jn][r]);
+          }
+        }
+    } else if constexpr (EPI == kEpiCombine) {
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m >= nvalid_a) continue;
+          const int f = p.sorted_ids[m];
+          const float w = p.topk_w[f];
+          float* dst = p.acc_f32 + (int64_t)(f / p.topk) * p.N;
+#pragma unroll
+          for (int jn = 0; jn < TN; jn++) {
+            const int n = tn * BN + wn * WN + jn * 32 + lr;
+            if (n < p.N) atomicAdd(dst + n, w * acc[i][jn][r]);
+          }
+        }
+      }
+    } else {
+      // SILU: act tile of this wave = WM rows x (TN/2)*32 columns, bf16, in LDS
+      constexpr int kActCols = (TN / 2) * 32;
+      uint16_t* act = reinterpret_cast<uint16_t*>(smem) + wave * (WM * kActCols);
+#pragma unroll
+      for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int jp = 0; jp < TN / 2; jp++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const float hg = bf16_bits_to_float(float_to_bf16_rne(acc[i][2 * jp][r]));
+            const float hu = bf16_bits_to_float(float_to_bf16_rne(acc[i][2 * jp + 1][r]));
+            const float a = hg / (1.0f + expf(-hg)) * hu;
+            const int row = i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            act[row * kActCols + jp * 32 + lr] = (uint16_t)float_to_bf16_rne(a);
+          }
+      __syncthreads();
+      // each lane quantises (row, 32-column block) items of its wave's act tile
+      const int act_w = p.N / 2;
+      for (int it = lane; it < WM * (TN / 2); it += 64) {
+        const int row = it / (TN / 2), jp = it % (TN / 2);
+        const int m = m0 + wm * WM + row;
+        const int b = tn * (BN / 64) + wn * (TN / 2) + jp;  // act block index
+        if (m >= nvalid_a || 32 * b >= act_w) continue;
+        float v[32];
+        const uint16_t* src = act + row * kActCols + jp * 32;
+#pragma unroll
+        for (int k = 0; k < 32; k++) v[k] = bf16_bits_to_float(src[k]);
+        uint32_t packed[4];
+        const uint32_t sc = mxfp4_block32(v, packed);
+        *reinterpret_cast<uint4*>(p.out_q + (int64_t)m * (act_w / 2) + b * 16) =
+            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        p.out_sf[(int64_t)m * (act_w / 32) + b] = (uint8_t)sc;
+      }
+    }
+    __syncthreads();  // LDS is reused by the next work item
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int BM, int BN, int SK, int EPI>
+hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
+  int64_t grid = cu_count();
+  if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
+  mxfp4_grouped<BM, BN, SK, EPI><<<(unsigned)grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                             const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  Args a{};
+  a.A = A; a.SFA = SFA; a.rows = (int)M; a.offsets = nullptr; a.E = 1;
+  a.W = B; a.WSF = SFB; a.N = (int)N; a.K = (int)K; a.alpha = alpha; a.out = D;
+  const int64_t items = ((M + 255) / 256) * ((N + 255) / 256);
+  return launch<256, 256, 128, kEpiStore>(a, items, stream);
+}
+
+hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* offsets, int64_t E,
+                                int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                int epilogue, uint16_t* out, uint8_t* out_q, uint8_t* out_sf,
+                                const int32_t* sorted_ids, const float* topk_w, int64_t topk, float* acc_f32,
+                                hipStream_t stream) {
+  Args a{};
+  a.A = Aq; a.SFA = Asf; a.rows = (int)rows; a.offsets = offsets; a.E = (int)E;
+  a.W = W; a.WSF = Wsf; a.N = (int)N; a.K = (int)K; a.alpha = nullptr;
+  a.out = out; a.out_q = out_q; a.out_sf = out_sf;
+  a.sorted_ids = sorted_ids; a.topk_w = topk_w; a.topk = (int)topk; a.acc_f32 = acc_f32;
+  constexpr int BM = 128, BN = 256;
+  const int64_t max_items = ((rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
+  switch (epilogue) {
+    case kEpiStore: return launch<BM, BN, 256, kEpiStore>(a, max_items, stream);
+    case kEpiSilu: return launch<BM, BN, 256, kEpiSilu>(a, max_items, stream);
+    default: return launch<BM, BN, 256, kEpiCombine>(a, max_items, stream);
+  }
+}
+
+}  // namespace bsfp4

@@ -243,6 +243,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
   (void)ws;
   (void)ws_bytes;
   if (M == 0) return hipSuccess;
+  if (M <= kSkinnyMaxM) return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, stream);
   constexpr int BM = 256, BN = 256;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((N + BN - 1) / BN);

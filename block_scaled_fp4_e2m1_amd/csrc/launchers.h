@@ -25,4 +25,32 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              void* ws, size_t ws_bytes, hipStream_t stream);
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 
+// Small-M (M <= 64) split-K kernels with NVFP4 weights.
+constexpr int64_t kSkinnyMaxM = 64;
+hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream);
+hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                               uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// MXFP4 scaled-MFMA GEMMs (dense and grouped by expert).
+constexpr int kEpiStore = 0;    // bf16 rows
+constexpr int kEpiSilu = 1;     // SiLU(gate) * up, re-quantised to MXFP4
+constexpr int kEpiCombine = 2;  // top-k weighted FP32 accumulation into token rows
+constexpr int64_t kMaxExperts = 1024;
+hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                             const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream);
+hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* offsets, int64_t E,
+                                int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                int epilogue, uint16_t* out, uint8_t* out_q, uint8_t* out_sf,
+                                const int32_t* sorted_ids, const float* topk_w, int64_t topk, float* acc_f32,
+                                hipStream_t stream);
+
+// MoE routing prep and the combine's helpers.
+hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* offsets,
+                           int32_t* sorted_ids, int32_t* sorted_tokens, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
+
 }  // namespace bsfp4

@@ -1,0 +1,142 @@
+// MoE routing prep and the combine's fill / finalize kernels.
+//
+// Routing prep groups the routed (token, slot) pairs by expert, producing the
+// per-expert row offsets that the pages' per-expert ops take
+// (`input_offset_by_experts` of `silu_and_mul_scaled_fp4_experts_quant`, vLLM
+// `sm103` branch comparison page, `csrc/ops.h`).  One workgroup per expert
+// reads the whole id list (L2-resident): it counts the ids below its expert
+// (its row offset), then stably compacts the flat indices equal to it with
+// block-wide prefix sums.  No atomics, no workspace, deterministic output.
+// The combine of the down projection accumulates into an FP32 buffer that is
+// cleared first and rounded to bf16 last by the two elementwise kernels here.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace bsfp4 {
+namespace {
+
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / 64;
+
+// Exclusive prefix of v over the workgroup (thread order) and the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kPrepWaves; w++) {
+    const int sw = sh[w];
+    base += (w < wave) ? sw : 0;
+    total += sw;
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+// One workgroup per expert e.  Pass 1 counts ids below e (the row offset of e)
+// and ids equal to e; pass 2 walks the ids in rounds of 4 consecutive ids per
+// thread (coalesced 128-bit loads) and writes the flat index of every id equal
+// to e at offset + (matches before it), which keeps the original order.
+__global__ void __launch_bounds__(kPrepThreads)
+    moe_prep_kernel(const int32_t* __restrict__ ids, int n, int topk, int E, int32_t* __restrict__ offsets,
+                    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_tokens) {
+  __shared__ int sh[kPrepWaves];
+  const int e = blockIdx.x;
+  const int nvec = n / 4;
+  const int4* ids4 = reinterpret_cast<const int4*>(ids);
+  int below = 0, mine = 0;
+  for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
+    const int4 v = ids4[i];
+    below += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+    mine += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  }
+  for (int i = nvec * 4 + threadIdx.x; i < n; i += kPrepThreads) {
+    below += ids[i] < e;
+    mine += ids[i] == e;
+  }
+  int total_below, total_mine;
+  (void)block_excl_scan(below, sh, total_below);
+  (void)block_excl_scan(mine, sh, total_mine);
+  if (threadIdx.x == 0) {
+    offsets[e] = total_below;
+    if (e == E - 1) offsets[E] = total_below + total_mine;
+  }
+  int base = total_below;
+  const int rounds = (n + 4 * kPrepThreads - 1) / (4 * kPrepThreads);
+  for (int r = 0; r < rounds; r++) {
+    const int i0 = (r * kPrepThreads + threadIdx.x) * 4;  // first of this thread's 4 ids
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = (i0 + j < n) ? ids[i0 + j] : -1;
+    const int cnt = (v[0] == e) + (v[1] == e) + (v[2] == e) + (v[3] == e);
+    int round_total;
+    int pos = base + block_excl_scan(cnt, sh, round_total);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (v[j] == e) {
+        sorted_ids[pos] = i0 + j;
+        if (sorted_tokens) sorted_tokens[pos] = (i0 + j) / topk;
+        pos++;
+      }
+    }
+    base += round_total;
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<float4*>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      for (int64_t j = i; j < n; j++) p[j] = 0.0f;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    f32_to_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      const float4 v = *reinterpret_cast<const float4*>(src + i);
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    } else {
+      for (int64_t j = i; j < n; j++) dst[j] = (uint16_t)float_to_bf16_rne(src[j]);
+    }
+  }
+}
+
+unsigned elementwise_grid(int64_t n) {
+  const int64_t want = (n / 4 + 255) / 256;
+  return (unsigned)(want < 1 ? 1 : (want > 8192 ? 8192 : want));
+}
+
+}  // namespace
+
+hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* offsets,
+                           int32_t* sorted_ids, int32_t* sorted_tokens, hipStream_t stream) {
+  moe_prep_kernel<<<(unsigned)E, kPrepThreads, 0, stream>>>(topk_ids, (int)(T * topk), (int)topk, (int)E,
+                                                             offsets, sorted_ids, sorted_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+  fill_zero_f32<<<elementwise_grid(n), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream) {
+  f32_to_bf16<<<elementwise_grid(n), 256, 0, stream>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace bsfp4

@@ -39,8 +39,11 @@ def _check(got, aq, sfa, bq, sfb, alpha, rows=None):
 
 
 SHAPES = [
-    (1, 32, 32), (5, 64, 96), (32, 32, 128), (64, 256, 256), (255, 288, 416),
-    (256, 256, 7168), (300, 544, 1056), (513, 768, 2048),
+    # small-M split-K path (M <= 64): m-tile boundaries, ragged K slices, K % 256 != 0
+    (1, 32, 32), (5, 64, 96), (16, 96, 1056), (17, 64, 2080), (32, 32, 128), (33, 160, 1024),
+    (63, 128, 9216), (64, 256, 256),
+    # tiled path (M > 64)
+    (65, 96, 160), (255, 288, 416), (256, 256, 7168), (300, 544, 1056), (513, 768, 2048),
 ]
 
 
@@ -51,9 +54,10 @@ def test_nvfp4_gemm_random(M, N, K):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
-def test_nvfp4_gemm_every_scale_code():
+@pytest.mark.parametrize("M", [24, 96])
+def test_nvfp4_gemm_every_scale_code(M):
     """Random codes with every finite E4M3 scale code (incl. subnormal scales)."""
-    M, N, K = 96, 160, 512
+    N, K = 160, 512
     aq = synth.random_bytes(1, (M, K // 2))
     bq = synth.random_bytes(2, (N, K // 2))
     sfa = synth.random_e4m3_scales(3, (M, K // 16), 0x00, 0x7F)
@@ -107,9 +111,10 @@ def test_nvfp4_gemm_m_zero():
     assert d.shape == (0, 32)
 
 
-def test_nvfp4_gemm_output_guard_band():
+@pytest.mark.parametrize("M", [37, 77])
+def test_nvfp4_gemm_output_guard_band(M):
     """Writes stay inside D: canaries around a ragged output are untouched."""
-    M, N, K = 37, 96, 160
+    N, K = 96, 160
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=9)
     buf = torch.full((M * N + 2 * 4096,), 0x7E57, dtype=torch.int16, device="cuda:0")
     out = buf[4096:4096 + M * N].view(M, N).view(torch.bfloat16)

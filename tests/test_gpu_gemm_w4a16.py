@@ -1,0 +1,60 @@
+"""GPU parity: W4A16 (bf16 activations x NVFP4 weights) against the float64 oracle.
+
+Tolerance: |D - Dref| <= 8e-3 |Dref| + 1e-3 rms(Dref) element-wise.  The
+workload shapes (M = 64 and M = 1 at N = 4096, K = 7168) are checked in
+full; smaller shapes cover m-tile boundaries, ragged K and M > 64 (rows
+processed in chunks of 64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_e2m1_amd as bs
+from block_scaled_fp4_e2m1_amd import synth
+from oracle import gemm as OG
+from oracle import quant as OQ
+from oracle import tolerance as TOL
+from gpu_helpers import dev_bf16, dev_f32, dev_u8, host_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _problem(M, N, K, seed):
+    a = synth.bf16_normal(seed, (M, K))
+    w = synth.bf16_normal(seed + 1, (N, K), 0.02)
+    gw = OQ.global_scale(w)
+    wq, wsf = OQ.nvfp4_quantize(w, gw)
+    alpha = np.float32(np.float32(1.0) / gw)
+    return a, wq, wsf, alpha
+
+
+def _run_check(a, wq, wsf, alpha):
+    d = bs.w4a16_gemm(dev_bf16(a), dev_u8(wq), dev_u8(wsf), None if alpha is None else dev_f32([alpha]))
+    torch.cuda.synchronize()
+    got = host_bf16_bits(d)
+    want = OG.w4a16_gemm(a, wq, wsf, 1.0 if alpha is None else alpha)
+    ok, worst, nbad = TOL.check_bf16(got, want)
+    assert ok, f"{nbad} out of tolerance (worst {worst:.2f})"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (3, 64, 96), (16, 128, 1056), (17, 96, 2048),
+                                   (40, 64, 4128), (64, 256, 512), (100, 96, 256), (130, 64, 1024)])
+def test_w4a16_shapes(M, N, K):
+    _run_check(*_problem(M, N, K, 30 + M))
+
+
+@pytest.mark.parametrize("M,seed", [(64, 130), (1, 131)])
+def test_w4a16_workload(M, seed):
+    a = synth.bf16_normal(seed, (M, 7168))
+    w = synth.bf16_normal(132, (4096, 7168), 0.02)
+    gw = OQ.global_scale(w)
+    wq, wsf = OQ.nvfp4_quantize(w, gw)
+    _run_check(a, wq, wsf, np.float32(np.float32(1.0) / gw))
+
+
+def test_w4a16_every_scale_code_no_alpha():
+    M, N, K = 8, 64, 512
+    a = synth.bf16_normal(1, (M, K), 4.0)
+    wq = synth.random_bytes(2, (N, K // 2))
+    wsf = synth.random_e4m3_scales(3, (N, K // 16), 0x00, 0x7F)
+    _run_check(a, wq, wsf, None)
