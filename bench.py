@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-rows", action="store_true", help="only the headline GEMM")
     p.add_argument("--rows-only", default="", help="comma list of rows to run")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run a plain 256 MiB device-to-device copy (3 times), the "
+                        "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     return p.parse_args()
 
 
@@ -76,14 +79,27 @@ class Timer:
         self.flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
 
     def run(self, fn, iters=20, warmup=3, cold=False):
+        """cold: each call timed alone after a 512 MiB fill that evicts L2 and the
+        256 MB MALL (median/p10/p90 of per-call event times).  warm: `iters` calls
+        back to back between two events (their mean), as a pipeline would issue
+        them -- per-call event pairs would add the event overhead to each call."""
         t = self.torch
         for _ in range(warmup):
             fn()
         t.cuda.synchronize()
+        if not cold:
+            e0 = t.cuda.Event(enable_timing=True)
+            e1 = t.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / iters
+            return {"median_us": us, "mean_back_to_back": True}
         times = []
         for _ in range(iters):
-            if cold:
-                self.flush.zero_()  # evicts L2 and the 256 MB MALL
+            self.flush.zero_()
             e0 = t.cuda.Event(enable_timing=True)
             e1 = t.cuda.Event(enable_timing=True)
             e0.record()
@@ -112,6 +128,14 @@ def main():
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- inputs
     M, N, K = 4096, 4096, 7168
@@ -269,21 +293,125 @@ def run_rows(torch, bs, synth, timer, only):
             "gemm_cold": _rate(timer.run(gfn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
             "pipeline_cold": _rate(timer.run(both, cold=True), 2.0 * M * N * K),
             "pipeline_warm": _rate(timer.run(both), 2.0 * M * N * K)}
+
+    # a5: W4A16 at M=64 and M=1, N=4096, K=7168 (HBM roofline)
+    if want("w4a16_4096x7168"):
+        res = {}
+        N, K = 4096, 7168
+        w = bf16(synth.bf16_normal(132, (N, K), 0.02))
+        gw = bs.global_scale(w)
+        wq, wsf = bs.quantize(w, "nvfp4", gs=gw)
+        alpha = torch.tensor([np.float32(1.0) / np.float32(gw.cpu().numpy()[0])], device=dev)
+        for M, seed in [(64, 130), (1, 131)]:
+            a = bf16(synth.bf16_normal(seed, (M, K)))
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = lambda: bs.w4a16_gemm(a, wq, wsf, alpha, out=D)
+            nbytes = 2 * M * K + N * K // 2 + N * K // 16 + 4 + 2 * M * N
+            res[f"M={M}"] = {"cold": _rate(timer.run(fn, cold=True), 2.0 * M * N * K, nbytes),
+                             "warm": _rate(timer.run(fn), 2.0 * M * N * K, nbytes),
+                             "algorithmic_bytes": nbytes}
+        rows["w4a16_4096x7168"] = res
+
+    # a6: the MXFP4 form at the large workload shape (FP4 MFMA roofline)
+    if want("mxfp4_gemm_4096x4096x7168"):
+        M, N, K = 4096, 4096, 7168
+        a = bf16(synth.bf16_normal(120, (M, K)))
+        b = bf16(synth.bf16_normal(121, (N, K)))
+        aq, sfa = bs.quantize(a, "mxfp4")
+        bq, sfb = bs.quantize(b, "mxfp4")
+        del a, b
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fn = lambda: bs.gemm(aq, sfa, bq, sfb, None, fmt="mxfp4", out=D)
+        nbytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
+        rows["mxfp4_gemm_4096x4096x7168"] = {
+            "warm": _rate(timer.run(fn), 2.0 * M * N * K, nbytes), "bound": "mfma (fp4)",
+            "peak_tflops": PEAK["fp4"]}
+
+    # a2, a7-a10: the MXFP4 MoE layer (4096 tokens, hidden 2048, 128 experts, top-8, I=768)
+    if want("moe_mxfp4_4096x2048_e128_top8"):
+        T, H, I, E, topk = 4096, 2048, 768, 128, 8
+        x = bf16(synth.bf16_normal(140, (T, H)))
+        ids_np, w_np = synth.routing(141, T, E, topk)
+        ids = torch.from_numpy(ids_np).to(dev)
+        tw = torch.from_numpy(w_np.reshape(-1)).to(dev)
+        w13 = bf16(synth.bf16_normal(142, (E * 2 * I, H), 0.02))
+        W13, W13sf = bs.quantize(w13, "mxfp4")
+        del w13
+        w2 = bf16(synth.bf16_normal(143, (E * H, I), 0.02))
+        W2, W2sf = bs.quantize(w2, "mxfp4")
+        del w2
+        W13, W13sf = W13.view(E, 2 * I, H // 2), W13sf.view(E, 2 * I, H // 32)
+        W2, W2sf = W2.view(E, H, I // 2), W2sf.view(E, H, I // 32)
+        R = T * topk
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        sids = torch.empty(R, dtype=torch.int32, device=dev)
+        stok = torch.empty(R, dtype=torch.int32, device=dev)
+        xq = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+        xsf = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        aq = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+        asf = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        lib = bs.load()
+        import ctypes
+        ws_bytes = lib.mxfp4_moe_grouped_gemm_workspace_size(R, E, H, I, bs.MOE_WEIGHTED_COMBINE, T)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        from block_scaled_fp4_e2m1_amd import binding as B
+
+        def prep():
+            B._check(lib.fp4_moe_prep(B._p(ids), T, topk, E, B._p(offs), B._p(sids), B._p(stok), None, 0,
+                                      B._stream(dev)), "prep")
+
+        def equant():  # each token once; the gate_up GEMM reads rows by token
+            bs.quantize(x, "mxfp4", q=xq, sf=xsf)
+
+        a1 = B.MoeEpilogueArgs(out_q=aq.data_ptr(), out_sf=asf.data_ptr())
+        a2 = B.MoeEpilogueArgs(out=out.data_ptr(), sorted_ids=sids.data_ptr(), topk_weights=tw.data_ptr(),
+                               num_tokens=T, topk=topk)
+
+        def gemm1():
+            B._check(lib.mxfp4_moe_grouped_gemm(B._p(xq), B._p(xsf), T, B._p(stok), B._p(offs), E, R, B._p(W13),
+                                                B._p(W13sf), 2 * I, H, bs.MOE_SILU_MUL_QUANT, ctypes.byref(a1),
+                                                None, 0, B._stream(dev)), "gemm1")
+
+        def gemm2():
+            B._check(lib.mxfp4_moe_grouped_gemm(B._p(aq), B._p(asf), R, None, B._p(offs), E, R, B._p(W2),
+                                                B._p(W2sf), H, I, bs.MOE_WEIGHTED_COMBINE, ctypes.byref(a2),
+                                                B._p(ws), ws_bytes, B._stream(dev)), "gemm2")
+
+        def layer():
+            prep()
+            equant()
+            gemm1()
+            gemm2()
+        wbytes = W13.numel() + W13sf.numel() + W2.numel() + W2sf.numel()
+        # weights + x read + out written + quantised x written/read + act codes written/read
+        nbytes = wbytes + 2 * T * H * 2 + 2 * (xq.numel() + xsf.numel()) + 2 * (aq.numel() + asf.numel())
+        flops = 2.0 * R * (2 * I) * H + 2.0 * R * H * I
+        layer()
+        rows["moe_mxfp4_4096x2048_e128_top8"] = {
+            "layer_cold": _rate(timer.run(layer, iters=10, cold=True), flops, nbytes),
+            "layer_warm": _rate(timer.run(layer, iters=10), flops, nbytes),
+            "stages_cold_us": {"prep": timer.run(prep, cold=True)["median_us"],
+                               "experts_quant": timer.run(equant, cold=True)["median_us"],
+                               "gate_up_silu_quant": timer.run(gemm1, cold=True)["median_us"],
+                               "down_combine": timer.run(gemm2, cold=True)["median_us"]},
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "bound": "hbm (weights are 83% of the bytes)"}
     return rows
 
 
 def cpu_baseline(aq, sfa, bq, sfb, alpha, D):
     """The float64 oracle on the same quantised inputs, timed on this host.
 
-    Sample: 512 of the 4096 rows of A (every column, all of K): dequantise
-    A-sample and B exactly to float64, one float64 matmul, bf16 rounding.
-    The GPU output on those rows is also checked against it."""
+    Sample: the whole workload (all 4096 rows of A, every column, all of K):
+    dequantise A and B exactly to float64, one float64 matmul, bf16 rounding.
+    The GPU output is also checked against it element by element."""
     from threadpoolctl import threadpool_info
 
     from oracle import gemm as OG
     from oracle import tolerance as TOL
 
-    rows = np.arange(0, 4096, 8)
+    rows = np.arange(0, 4096)
     A = aq.cpu().numpy()[rows]
     SA = sfa.cpu().numpy()[rows]
     B = bq.cpu().numpy()
@@ -298,7 +426,7 @@ def cpu_baseline(aq, sfa, bq, sfb, alpha, D):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{len(rows)} of 4096 rows of A x all 4096 columns x K=7168 "
+            "sample": f"full workload: {len(rows)} rows x 4096 columns x K=7168 "
                       "(exact float64 dequant + float64 matmul + bf16 rounding)",
             "parity_on_sample": {"ok": ok, "worst_ratio": round(worst, 4), "n_bad": nbad}}
 

@@ -62,8 +62,8 @@ _SIGNATURES = {
                                     _c_size, _c_ptr]),
     "mxfp4_moe_grouped_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
                                                         _c_i64]),
-    "mxfp4_moe_grouped_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr,
-                                              _c_i64, _c_i64, ctypes.c_int,
+    "mxfp4_moe_grouped_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_i64,
+                                              _c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_int,
                                               ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size,
                                               _c_ptr]),
 }
@@ -235,13 +235,22 @@ def moe_prep(topk_ids: torch.Tensor, num_experts: int):
 
 
 def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_BF16, *,
-                           out=None, out_q=None, out_sf=None, sorted_ids=None,
-                           topk_weights=None, num_tokens=0, topk=0):
-    """Grouped MXFP4 GEMM over expert-sorted rows; see the C header for epilogues."""
+                           rows=None, a_row_index=None, out=None, out_q=None, out_sf=None,
+                           sorted_ids=None, topk_weights=None, num_tokens=0, topk=0):
+    """Grouped MXFP4 GEMM over expert-sorted rows; see the C header for epilogues.
+
+    With a_row_index, problem row m reads row a_row_index[m] of Aq and `rows`
+    defaults to len(a_row_index); otherwise rows = Aq.shape[0]."""
     for t, n in ((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf")):
         _need(t, torch.uint8, n)
     _need(expert_offsets, torch.int32, "expert_offsets")
-    rows, K = Aq.shape[0], Aq.shape[1] * 2
+    a_total, K = Aq.shape[0], Aq.shape[1] * 2
+    if a_row_index is not None:
+        _need(a_row_index, torch.int32, "a_row_index")
+        if rows is None:
+            rows = a_row_index.numel()
+    elif rows is None:
+        rows = a_total
     E, N = W.shape[0], W.shape[1]
     dev = Aq.device
     if epilogue == MOE_STORE_BF16 and out is None:
@@ -265,8 +274,8 @@ def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_B
         num_tokens=num_tokens, topk=topk)
     lib = load()
     ws = _workspace(lib.mxfp4_moe_grouped_gemm_workspace_size(rows, E, N, K, epilogue, num_tokens), dev)
-    _check(lib.mxfp4_moe_grouped_gemm(_p(Aq), _p(Asf), _p(expert_offsets), E, rows, _p(W), _p(Wsf), N,
-                                      K, epilogue, ctypes.byref(args), _p(ws),
+    _check(lib.mxfp4_moe_grouped_gemm(_p(Aq), _p(Asf), a_total, _p(a_row_index), _p(expert_offsets), E,
+                                      rows, _p(W), _p(Wsf), N, K, epilogue, ctypes.byref(args), _p(ws),
                                       0 if ws is None else ws.numel(), _stream(dev)),
            "mxfp4_moe_grouped_gemm")
     if epilogue == MOE_SILU_MUL_QUANT:
@@ -274,17 +283,17 @@ def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_B
     return out
 
 
-def moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf, *, fused_act_quant=True):
-    """The MXFP4 W4A4 MoE layer: prep -> experts quant -> gate_up GEMM with
-    SiLU-gate + MXFP4 re-quant -> down GEMM with the top-k weighted combine."""
+def moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf):
+    """The MXFP4 W4A4 MoE layer: routing prep -> MXFP4 quantisation of each
+    token once -> gate_up grouped GEMM reading the activations by token, with
+    the fused SiLU-gate + MXFP4 re-quant epilogue -> down grouped GEMM with the
+    top-k weighted combine."""
     T, topk = topk_ids.shape
     E = W13.shape[0]
     offsets, sorted_ids, sorted_tokens = moe_prep(topk_ids, E)
-    xq, xsf = quantize(x, "mxfp4", row_map=sorted_tokens)
-    if fused_act_quant:
-        aq, asf = mxfp4_moe_grouped_gemm(xq, xsf, offsets, W13, W13sf, MOE_SILU_MUL_QUANT)
-    else:
-        raise NotImplementedError("unfused act path is exposed stage by stage in the tests")
+    xq, xsf = quantize(x, "mxfp4")
+    aq, asf = mxfp4_moe_grouped_gemm(xq, xsf, offsets, W13, W13sf, MOE_SILU_MUL_QUANT,
+                                     a_row_index=sorted_tokens)
     return mxfp4_moe_grouped_gemm(aq, asf, offsets, W2, W2sf, MOE_WEIGHTED_COMBINE,
                                   sorted_ids=sorted_ids, topk_weights=topk_weights,
                                   num_tokens=T, topk=topk)

@@ -265,34 +265,40 @@ bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int6
 
 size_t mxfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K, int epilogue,
                                              int64_t num_tokens) {
-  (void)rows;
   (void)E;
   (void)K;
-  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE && num_tokens > 0 && N > 0)
-    return (size_t)num_tokens * (size_t)N * sizeof(float);
+  (void)num_tokens;
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE && rows > 0 && N > 0)
+    return (size_t)rows * (size_t)N * sizeof(float);
   return 0;
 }
 
-bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, const int32_t* expert_offsets,
-                                    int64_t E, int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N,
-                                    int64_t K, int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
-                                    size_t ws_bytes, void* stream) {
+bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, int64_t a_rows_total,
+                                    const int32_t* a_row_index, const int32_t* expert_offsets, int64_t E,
+                                    int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                    int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws, size_t ws_bytes,
+                                    void* stream) {
   if (epilogue != BSFP4_MOE_STORE_BF16 && epilogue != BSFP4_MOE_SILU_MUL_QUANT &&
       epilogue != BSFP4_MOE_WEIGHTED_COMBINE)
     return fail(BSFP4_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
   if (ep == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep is NULL");
-  if (rows < 0 || E <= 0 || E > bsfp4::kMaxExperts || N <= 0 || K <= 0)
-    return fail(BSFP4_ERR_SHAPE, "need rows >= 0, 0 < E <= %lld, N > 0, K > 0", (long long)bsfp4::kMaxExperts);
+  if (rows < 0 || a_rows_total < 0 || E <= 0 || E > bsfp4::kMaxExperts || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0, a_rows_total >= 0, 0 < E <= %lld, N > 0, K > 0",
+                (long long)bsfp4::kMaxExperts);
+  if (a_row_index == nullptr && a_rows_total != rows)
+    return fail(BSFP4_ERR_SHAPE, "without a_row_index, a_rows_total (%lld) must equal rows (%lld)",
+                (long long)a_rows_total, (long long)rows);
   if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
   if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
   if (epilogue == BSFP4_MOE_SILU_MUL_QUANT && N % 64)
     return fail(BSFP4_ERR_SHAPE, "SILU_MUL_QUANT needs N %% 64 == 0 (got N=%lld)", (long long)N);
-  if (rows > INT32_MAX || E * N * (K / 2) > ((int64_t)1 << 40))
-    return fail(BSFP4_ERR_SHAPE, "problem too large");
+  if (rows > INT32_MAX || a_rows_total > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
   REQUIRE_PTR(W);
   REQUIRE_PTR(Wsf);
   REQUIRE_PTR(expert_offsets);
-  const int64_t T = ep->num_tokens;
+  if (a_row_index != nullptr && !aligned(a_row_index, 4))
+    return fail(BSFP4_ERR_ALIGNMENT, "a_row_index is not 4-byte aligned");
   if (rows > 0) {
     REQUIRE_PTR(Aq);
     REQUIRE_PTR(Asf);
@@ -304,6 +310,7 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, const
       if (!aligned(ep->out_q, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out_q is not 16-byte aligned");
     }
   }
+  const int64_t T = ep->num_tokens;
   if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
     if (T <= 0 || ep->topk <= 0 || T * ep->topk != rows)
       return fail(BSFP4_ERR_SHAPE, "WEIGHTED_COMBINE needs num_tokens*topk == rows (T=%lld topk=%lld rows=%lld)",
@@ -316,22 +323,22 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, const
       return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
     if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
   }
+  if (rows == 0) return ok();
   if (bsfp4_status s = check_device()) return s;
   const hipStream_t st = as_stream(stream);
   if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
-    float* acc = static_cast<float*>(ws);
-    hipError_t e = bsfp4::launch_fill_zero(acc, T * N, st);
-    if (e == hipSuccess && rows > 0)
-      e = bsfp4::launch_mxfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, N, K, bsfp4::kEpiCombine, nullptr,
-                                      nullptr, nullptr, ep->sorted_ids, ep->topk_weights, ep->topk, acc, st);
-    if (e == hipSuccess) e = bsfp4::launch_f32_to_bf16(acc, static_cast<uint16_t*>(ep->out), T * N, st);
+    float* y = static_cast<float*>(ws);
+    hipError_t e = bsfp4::launch_mxfp4_grouped(Aq, Asf, a_row_index, a_rows_total, expert_offsets, E, rows, W, Wsf,
+                                               N, K, bsfp4::kEpiCombine, nullptr, nullptr, nullptr, ep->sorted_ids,
+                                               ep->topk_weights, y, st);
+    if (e == hipSuccess) e = bsfp4::launch_topk_sum(y, static_cast<uint16_t*>(ep->out), T, ep->topk, N, st);
     return launched(e, "mxfp4_moe_grouped_gemm launch");
   }
-  if (rows == 0) return ok();
-  return launched(bsfp4::launch_mxfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, N, K,
+  return launched(bsfp4::launch_mxfp4_grouped(Aq, Asf, a_row_index, a_rows_total, expert_offsets, E, rows, W, Wsf,
+                                              N, K,
                                               epilogue == BSFP4_MOE_STORE_BF16 ? bsfp4::kEpiStore : bsfp4::kEpiSilu,
                                               static_cast<uint16_t*>(ep->out), ep->out_q, ep->out_sf, nullptr,
-                                              nullptr, 0, nullptr, st),
+                                              nullptr, nullptr, st),
                   "mxfp4_moe_grouped_gemm launch");
 }
 

@@ -28,8 +28,10 @@
 //            from the bf16-rounded h, staged in LDS and re-quantised to MXFP4 per
 //            32-element block (the fused `silu_and_mul_scaled_fp4_experts_quant`
 //            pattern of the vLLM `sm103` branch comparison page, MXFP4 form);
-//   COMBINE  out_f32[token] += topk_weight * acc with hardware float atomics
-//            (summation order across a token's experts is not fixed).
+//   COMBINE  y[f] = topk_weight[f] * row in FP32 for the row's flat (token, slot)
+//            index f; a second kernel sums each token's top-k rows in slot order
+//            and rounds once to bf16 (deterministic; device-wide float atomics
+//            across the 8 XCDs measured 12x slower than this two-pass form).
 #include "device_common.h"
 #include "launchers.h"
 #include "quant_device.h"
@@ -123,10 +125,44 @@ __device__ __forceinline__ void store_stage(const Stage<ROWS, SK>& st, uint8_t* 
   }
 }
 
+// ---- direct-to-LDS loads ---------------------------------------------------
+// global_load_lds_dword{,x4}: every lane fetches 4 / 16 bytes from its own
+// global address and the wave writes them to LDS at M0 + lane * size, so one
+// instruction fills 256 B / 1 KB of LDS without passing through VGPRs.  They
+// are issued from inline assembly so that the compiler does not add a full
+// vmcnt(0) wait before every LDS read (it cannot tell which ring slot an LDS
+// DMA targets); the kernel waits explicitly with s_waitcnt vmcnt(n) + s_barrier.
+__device__ __attribute__((aligned(16))) const uint8_t kZeroPage[16] = {};
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_uniform) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_uniform)
+               : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_uniform) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_uniform)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 struct Args {
   const uint8_t* A;
   const uint8_t* SFA;
   int rows;
+  const int32_t* a_rows;   // optional: row m of the problem reads row a_rows[m] of A
+  int a_nrows;             // rows of A (bounds of a_rows entries)
   const int32_t* offsets;  // nullptr: one group holding every row
   int E;
   const uint8_t* W;
@@ -139,14 +175,23 @@ struct Args {
   uint8_t* out_sf;         // SILU: [rows, N/64]
   const int32_t* sorted_ids;  // COMBINE
   const float* topk_w;        // COMBINE
-  int topk;                   // COMBINE
-  float* acc_f32;             // COMBINE: [T, N]
+  float* y_f32;               // COMBINE: [T * topk, N], row f = flat (token, slot) index
 };
 
 constexpr int kMaxGroups = (int)kMaxExperts;
 
-template <int BM, int BN, int SK, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
+// Workgroups per CU the register budget is sized for: small tiles keep two
+// resident so that one's loads overlap the other's MFMAs.
+template <int BM, int BN>
+constexpr int wg_per_cu() { return BM * BN <= 128 * 128 ? 2 : 1; }
+
+// kDMA: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring filled by
+// direct-to-LDS loads.  Otherwise: register-staged double buffer, any K % 32.
+constexpr int kRing = 4;
+
+template <int BM, int BN, int SK, int EPI, bool kDMA>
+__global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped(Args p) {
+  static_assert(!kDMA || SK == 128, "the LDS ring uses 128-value stages");
   using Gm = Geo<SK>;
   constexpr int kRowBytes = Gm::kRowBytes, kRowScales = Gm::kRowScales;
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -154,7 +199,8 @@ __global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
   constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
   constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  constexpr int kSlots = kDMA ? kRing : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int wave_sum[4];
 
@@ -235,7 +281,13 @@ __global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
     const uint8_t* Wq = p.W + (int64_t)e * p.N * (K / 2);
     const uint8_t* Ws = p.WSF + (int64_t)e * p.N * (K / 32);
 
-    auto amap = [&](int i) { return m0 + i; };
+    // A row of problem row m0 + i (-1: beyond this group / the problem)
+    auto amap = [&](int i) -> int {
+      const int m = m0 + i;
+      if (m >= nvalid_a) return -1;
+      return p.a_rows ? p.a_rows[m] : m;
+    };
+    const int a_lim = p.a_rows ? p.a_nrows : nvalid_a;
     auto bmap = [&](int i) -> int {
       if constexpr (EPI == kEpiSilu) {
         // LDS row i: wave column half wc = i / WN, column tile jn = (i % WN) / 32;
@@ -256,55 +308,143 @@ __global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
       for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
 
     const int nst = (K + SK - 1) / SK;
+    if constexpr (kDMA) {
+      // per-lane sources of this tile's DMA instructions (zero page when invalid)
+      constexpr int kCodeI = (BM + BN) / 64;    // 1 KB code instructions per wave per stage
+      constexpr int kScaleI = (BM + BN) / 256;  // 256 B scale instructions per wave per stage
+      constexpr int kL = kCodeI + kScaleI;      // loads per wave per stage
+      const uint8_t* csrc[kCodeI];
+      uint32_t cstep[kCodeI], cdst[kCodeI];
+      const uint8_t* ssrc[kScaleI];
+      uint32_t sstep[kScaleI], sdst[kScaleI];
+#pragma unroll
+      for (int j = 0; j < kCodeI; j++) {
+        const int q = wave * kCodeI + j;  // instruction index in the stage
+        const bool isA = q < BM / 16;
+        const int qq = isA ? q : q - BM / 16;
+        const int row = qq * 16 + (lane >> 2);  // tile row of this lane's chunk
+        const int c = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);  // logical chunk
+        int gr = isA ? amap(row) : bmap(row);
+        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
+        const uint8_t* base = isA ? p.A : Wq;
+        csrc[j] = ok ? base + (int64_t)gr * (K / 2) + c * 16 : kZeroPage;
+        cstep[j] = ok ? (uint32_t)(SK / 2) : 0u;
+        cdst[j] = (isA ? 0 : kA) + qq * 1024;
+      }
+#pragma unroll
+      for (int j = 0; j < kScaleI; j++) {
+        const int q = wave * kScaleI + j;
+        const bool isA = q < BM / 64;
+        const int qq = isA ? q : q - BM / 64;
+        const int row = qq * 64 + lane;
+        int gr = isA ? amap(row) : bmap(row);
+        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
+        const uint8_t* base = isA ? p.SFA : Ws;
+        ssrc[j] = ok ? base + (int64_t)gr * (K / 32) : kZeroPage;
+        sstep[j] = ok ? (uint32_t)(SK / 32) : 0u;
+        sdst[j] = kA + kB + (isA ? 0 : BM * kRowScales) + qq * 256;
+      }
+      const uint32_t lds0 = lds_offset(smem);
+      auto issue = [&](int st) {
+        const uint32_t slot = lds0 + (uint32_t)((st % kRing) * kStage);
+#pragma unroll
+        for (int j = 0; j < kCodeI; j++)
+          lds_dma16(csrc[j] + cstep[j] * (uint32_t)st, __builtin_amdgcn_readfirstlane(slot + cdst[j]));
+#pragma unroll
+        for (int j = 0; j < kScaleI; j++)
+          lds_dma4(ssrc[j] + sstep[j] * (uint32_t)st, __builtin_amdgcn_readfirstlane(slot + sdst[j]));
+      };
+      for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
+      for (int s = 0; s < nst; s++) {
+        const int ahead = min(kRing - 2, nst - 1 - s);  // stages issued after s
+        if (ahead >= 2) wait_vmcnt<2 * kL>();
+        else if (ahead == 1) wait_vmcnt<kL>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
+        if (s + kRing - 1 < nst) issue(s + kRing - 1);
+        const uint8_t* st = smem + (s % kRing) * kStage;
+        const uint8_t* qa = st;
+        const uint8_t* qb = st + kA;
+        const uint8_t* sa = st + kA + kB;
+        const uint8_t* sb = sa + BM * kRowScales;
+#pragma unroll
+        for (int j = 0; j < SK / 64; j++) {
+          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
+          v8i fb[TN];
+          int xb[TN];
+  #pragma unroll
+          for (int i = 0; i < TN; i++) {
+            const int r = wn * WN + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
+            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            xb[i] = sb[r * kRowScales + c];
+          }
+  #pragma unroll
+          for (int i = 0; i < TM; i++) {
+            const int r = wm * WM + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
+            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            const int xa = sa[r * kRowScales + c];
+  #pragma unroll
+            for (int jn = 0; jn < TN; jn++)
+              acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
+                                                                           0, xb[jn]);
+          }
+        }
+      }
+      __syncthreads();  // all waves are done with the ring before it is reused
+    } else {
     Stage<BM, SK> ra;
-    Stage<BN, SK> rb;
-    load_stage<BM, SK>(ra, p.A, p.SFA, amap, nvalid_a, K, 0, sc_aligned, tid);
-    load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
-    store_stage<BM, SK>(ra, smem, smem + kA + kB, tid);
-    store_stage<BN, SK>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
-    __syncthreads();
-
-    for (int s = 0; s < nst; s++) {
-      const bool more = s + 1 < nst;
-      if (more) {
-        load_stage<BM, SK>(ra, p.A, p.SFA, amap, nvalid_a, K, (s + 1) * SK, sc_aligned, tid);
-        load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
-      }
-      const uint8_t* st = smem + (s & 1) * kStage;
-      const uint8_t* qa = st;
-      const uint8_t* qb = st + kA;
-      const uint8_t* sa = st + kA + kB;
-      const uint8_t* sb = sa + BM * kRowScales;
-#pragma unroll
-      for (int j = 0; j < SK / 64; j++) {
-        const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
-        v8i fb[TN];
-        int xb[TN];
-#pragma unroll
-        for (int i = 0; i < TN; i++) {
-          const int r = wn * WN + i * 32 + lr;
-          const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
-          fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          xb[i] = sb[r * kRowScales + c];
-        }
-#pragma unroll
-        for (int i = 0; i < TM; i++) {
-          const int r = wm * WM + i * 32 + lr;
-          const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
-          const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          const int xa = sa[r * kRowScales + c];
-#pragma unroll
-          for (int jn = 0; jn < TN; jn++)
-            acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
-                                                                         0, xb[jn]);
-        }
-      }
-      if (more) {
-        uint8_t* nx = smem + ((s + 1) & 1) * kStage;
-        store_stage<BM, SK>(ra, nx, nx + kA + kB, tid);
-        store_stage<BN, SK>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
-      }
+      Stage<BN, SK> rb;
+      load_stage<BM, SK>(ra, p.A, p.SFA, amap, a_lim, K, 0, sc_aligned, tid);
+      load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
+      store_stage<BM, SK>(ra, smem, smem + kA + kB, tid);
+      store_stage<BN, SK>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
       __syncthreads();
+  
+      for (int s = 0; s < nst; s++) {
+        const bool more = s + 1 < nst;
+        if (more) {
+          load_stage<BM, SK>(ra, p.A, p.SFA, amap, a_lim, K, (s + 1) * SK, sc_aligned, tid);
+          load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
+        }
+        const uint8_t* st = smem + (s & 1) * kStage;
+        const uint8_t* qa = st;
+        const uint8_t* qb = st + kA;
+        const uint8_t* sa = st + kA + kB;
+        const uint8_t* sb = sa + BM * kRowScales;
+  #pragma unroll
+        for (int j = 0; j < SK / 64; j++) {
+          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
+          v8i fb[TN];
+          int xb[TN];
+  #pragma unroll
+          for (int i = 0; i < TN; i++) {
+            const int r = wn * WN + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
+            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            xb[i] = sb[r * kRowScales + c];
+          }
+  #pragma unroll
+          for (int i = 0; i < TM; i++) {
+            const int r = wm * WM + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
+            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            const int xa = sa[r * kRowScales + c];
+  #pragma unroll
+            for (int jn = 0; jn < TN; jn++)
+              acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
+                                                                           0, xb[jn]);
+          }
+        }
+        if (more) {
+          uint8_t* nx = smem + ((s + 1) & 1) * kStage;
+          store_stage<BM, SK>(ra, nx, nx + kA + kB, tid);
+          store_stage<BN, SK>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
+        }
+        __syncthreads();
+      }
+  
     }
 
     // ---- epilogues.  acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) + 4g + r%4,
@@ -323,6 +463,8 @@ __global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
           }
         }
     } else if constexpr (EPI == kEpiCombine) {
+      // y[f] = topk_weight[f] * row, f = flat (token, slot) index of the row; the
+      // top-k sum is done afterwards in a fixed order (deterministic, no atomics)
 #pragma unroll
       for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -331,11 +473,11 @@ __global__ void __launch_bounds__(kThreads, 1) mxfp4_grouped(Args p) {
           if (m >= nvalid_a) continue;
           const int f = p.sorted_ids[m];
           const float w = p.topk_w[f];
-          float* dst = p.acc_f32 + (int64_t)(f / p.topk) * p.N;
+          float* dst = p.y_f32 + (int64_t)f * p.N;
 #pragma unroll
           for (int jn = 0; jn < TN; jn++) {
             const int n = tn * BN + wn * WN + jn * 32 + lr;
-            if (n < p.N) atomicAdd(dst + n, w * acc[i][jn][r]);
+            if (n < p.N) dst[n] = w * acc[i][jn][r];
           }
         }
       }
@@ -393,9 +535,12 @@ int cu_count() {
 
 template <int BM, int BN, int SK, int EPI>
 hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
-  int64_t grid = cu_count();
+  int64_t grid = (int64_t)cu_count() * wg_per_cu<BM, BN>();
   if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
-  mxfp4_grouped<BM, BN, SK, EPI><<<(unsigned)grid, kThreads, 0, stream>>>(a);
+  if (a.K % 128 == 0)
+    mxfp4_grouped<BM, BN, 128, EPI, true><<<(unsigned)grid, kThreads, 0, stream>>>(a);
+  else
+    mxfp4_grouped<BM, BN, SK, EPI, false><<<(unsigned)grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -406,28 +551,30 @@ hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              hipStream_t stream) {
   if (M == 0) return hipSuccess;
   Args a{};
-  a.A = A; a.SFA = SFA; a.rows = (int)M; a.offsets = nullptr; a.E = 1;
+  a.A = A; a.SFA = SFA; a.rows = (int)M; a.a_rows = nullptr; a.a_nrows = (int)M;
+  a.offsets = nullptr; a.E = 1;
   a.W = B; a.WSF = SFB; a.N = (int)N; a.K = (int)K; a.alpha = alpha; a.out = D;
   const int64_t items = ((M + 255) / 256) * ((N + 255) / 256);
   return launch<256, 256, 128, kEpiStore>(a, items, stream);
 }
 
-hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* offsets, int64_t E,
-                                int64_t rows, const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
-                                int epilogue, uint16_t* out, uint8_t* out_q, uint8_t* out_sf,
-                                const int32_t* sorted_ids, const float* topk_w, int64_t topk, float* acc_f32,
-                                hipStream_t stream) {
+hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* a_rows, int64_t a_nrows,
+                                const int32_t* offsets, int64_t E, int64_t rows, const uint8_t* W,
+                                const uint8_t* Wsf, int64_t N, int64_t K, int epilogue, uint16_t* out,
+                                uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids, const float* topk_w,
+                                float* y_f32, hipStream_t stream) {
   Args a{};
-  a.A = Aq; a.SFA = Asf; a.rows = (int)rows; a.offsets = offsets; a.E = (int)E;
+  a.A = Aq; a.SFA = Asf; a.rows = (int)rows; a.a_rows = a_rows; a.a_nrows = (int)a_nrows;
+  a.offsets = offsets; a.E = (int)E;
   a.W = W; a.WSF = Wsf; a.N = (int)N; a.K = (int)K; a.alpha = nullptr;
   a.out = out; a.out_q = out_q; a.out_sf = out_sf;
-  a.sorted_ids = sorted_ids; a.topk_w = topk_w; a.topk = (int)topk; a.acc_f32 = acc_f32;
-  constexpr int BM = 128, BN = 256;
+  a.sorted_ids = sorted_ids; a.topk_w = topk_w; a.y_f32 = y_f32;
+  constexpr int BM = 128, BN = 128;
   const int64_t max_items = ((rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
   switch (epilogue) {
-    case kEpiStore: return launch<BM, BN, 256, kEpiStore>(a, max_items, stream);
-    case kEpiSilu: return launch<BM, BN, 256, kEpiSilu>(a, max_items, stream);
-    default: return launch<BM, BN, 256, kEpiCombine>(a, max_items, stream);
+    case kEpiStore: return launch<BM, BN, 128, kEpiStore>(a, max_items, stream);
+    case kEpiSilu: return launch<BM, BN, 128, kEpiSilu>(a, max_items, stream);
+    default: return launch<BM, BN, 128, kEpiCombine>(a, max_items, stream);
   }
 }
 

@@ -124,12 +124,15 @@ __device__ __forceinline__ v8h dequant8(uint32_t word, _Float16 s) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// splits == 1: D = bf16(alpha * acc).  splits > 1: workgroup (tile, s) sums
+// the s-th contiguous range of K stages and writes its FP32 partial tile to
+// part[s][M][N]; a second kernel adds the partials in split order.
 template <int BM, int BN>
 __global__ void __launch_bounds__(kThreads, 1)
     nvfp4_gemm_tiled(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA,
                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
                      const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N,
-                     int64_t K, int tiles_n) {
+                     int64_t K, int tiles_n, int splits, float* __restrict__ part) {
   constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
   constexpr int kABytes = BM * kStageBytes, kBBytes = BN * kStageBytes;
@@ -140,7 +143,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
+  const int split = blockIdx.x % splits;
+  const int tile = blockIdx.x / splits;
+  const int tile_m = tile / tiles_n, tile_n = tile % tiles_n;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
   v16f acc[TM][TN];
@@ -149,11 +154,15 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
     for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
 
-  const int nstages = (int)((K + kStageK - 1) / kStageK);
+  const int total_stages = (int)((K + kStageK - 1) / kStageK);
+  const int s_begin = (int)((int64_t)total_stages * split / splits);
+  const int s_end = (int)((int64_t)total_stages * (split + 1) / splits);
+  const int nstages = s_end - s_begin;
+  const int kbase = s_begin * kStageK;
   StageRegs<BM> ra;
   StageRegs<BN> rb;
-  load_stage<BM>(ra, A, SFA, m0, M, K, 0, tid);
-  load_stage<BN>(rb, B, SFB, n0, N, K, 0, tid);
+  load_stage<BM>(ra, A, SFA, m0, M, K, kbase, tid);
+  load_stage<BN>(rb, B, SFB, n0, N, K, kbase, tid);
   {
     uint8_t* s = smem;
     store_stage<BM>(ra, s, s + kABytes + kBBytes, tid);
@@ -167,8 +176,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   for (int s = 0; s < nstages; s++) {
     const bool more = (s + 1) < nstages;
     if (more) {
-      load_stage<BM>(ra, A, SFA, m0, M, K, (s + 1) * kStageK, tid);
-      load_stage<BN>(rb, B, SFB, n0, N, K, (s + 1) * kStageK, tid);
+      load_stage<BM>(ra, A, SFA, m0, M, K, kbase + (s + 1) * kStageK, tid);
+      load_stage<BN>(rb, B, SFB, n0, N, K, kbase + (s + 1) * kStageK, tid);
     }
     const uint8_t* st = smem + (s & 1) * kStage;
     const uint8_t* sq_a = st;
@@ -220,19 +229,100 @@ __global__ void __launch_bounds__(kThreads, 1)
     __syncthreads();
   }
 
-  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  if (splits == 1) {
+    const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
 #pragma unroll
-  for (int i = 0; i < TM; i++) {
+    for (int i = 0; i < TM; i++) {
 #pragma unroll
-    for (int jn = 0; jn < TN; jn++) {
-      const int n = n0 + wn * WN + jn * 32 + lr;
+      for (int jn = 0; jn < TN; jn++) {
+        const int n = n0 + wn * WN + jn * 32 + lr;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M && n < N) D[(int64_t)m * N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][jn][r]);
+        for (int r = 0; r < 16; r++) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m < M && n < N) D[(int64_t)m * N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][jn][r]);
+        }
+      }
+    }
+  } else {
+    float* dst = part + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+#pragma unroll
+      for (int jn = 0; jn < TN; jn++) {
+        const int n = n0 + wn * WN + jn * 32 + lr;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][jn][r];
+        }
       }
     }
   }
+}
+
+// D = bf16(alpha * sum_s part[s]), partials added in split order (deterministic).
+__global__ void __launch_bounds__(256)
+    splitk_reduce(const float* __restrict__ part, int splits, const float* __restrict__ alpha_ptr,
+                  uint16_t* __restrict__ D, int64_t MN) {
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < MN / 4; q += stride) {
+    float4 acc = reinterpret_cast<const float4*>(part)[q];
+    for (int s = 1; s < splits; s++) {
+      const float4 v = reinterpret_cast<const float4*>(part + (int64_t)s * MN)[q];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    reinterpret_cast<uint2*>(D)[q] = make_uint2(pack_bf16x2(alpha * acc.x, alpha * acc.y),
+                                                pack_bf16x2(alpha * acc.z, alpha * acc.w));
+  }
+}
+
+struct Plan {
+  int bm, bn, splits;
+};
+
+// Tile shape and K split for an M x N x K problem on `cus` compute units: the
+// estimated time is (rounds of work items) x (work per item) / (tile
+// efficiency) plus the FP32 partial traffic of a split.  Efficiencies are the
+// measured fractions of MFMA peak of the two tile shapes.
+Plan plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t stages = (K + kStageK - 1) / kStageK;
+  Plan best{256, 256, 1};
+  double best_t = 1e300;
+  const int shapes[2][2] = {{256, 256}, {128, 128}};
+  const double eff[2] = {0.33, 0.2};
+  for (int c = 0; c < 2; c++) {
+    const int bm = shapes[c][0], bn = shapes[c][1];
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    for (int s = 1; s <= 8; s++) {
+      if (s > 1 && stages / s < 8) break;  // keep at least 8 stages (1024 K values) per split
+      const int64_t items = tiles * s;
+      const int64_t rounds = (items + cus - 1) / cus;
+      const double flops = 2.0 * bm * bn * (double)K / s;
+      double t = rounds * flops / (9.8e12 * eff[c]);
+      if (s > 1) t += (2.0 * s * M * N * 4) / 4.0e12 + 3e-6;
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best = Plan{bm, bn, s};
+      }
+    }
+  }
+  return best;
+}
+
+int device_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    n = (hipGetDevice(&dev) == hipSuccess &&
+         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ? v
+            : 256;
+  }
+  return n;
 }
 
 }  // namespace
@@ -240,23 +330,32 @@ __global__ void __launch_bounds__(kThreads, 1)
 hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                              const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (M == 0) return hipSuccess;
   if (M <= kSkinnyMaxM) return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, stream);
-  constexpr int BM = 256, BN = 256;
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  nvfp4_gemm_tiled<BM, BN><<<tiles_m * tiles_n, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M,
-                                                                       (int)N, K, tiles_n);
+  Plan pl = plan_tiled(M, N, K, device_cus());
+  if (pl.splits > 1 && ws_bytes < (size_t)pl.splits * M * N * sizeof(float)) pl.splits = 1;
+  float* part = static_cast<float*>(ws);
+  const int tiles_m = (int)((M + pl.bm - 1) / pl.bm);
+  const int tiles_n = (int)((N + pl.bn - 1) / pl.bn);
+  const unsigned grid = (unsigned)(tiles_m * tiles_n * pl.splits);
+  if (pl.bm == 256)
+    nvfp4_gemm_tiled<256, 256><<<grid, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                              tiles_n, pl.splits, part);
+  else
+    nvfp4_gemm_tiled<128, 128><<<grid, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                              tiles_n, pl.splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t q = M * N / 4;
+  const unsigned rgrid = (unsigned)((q + 255) / 256 > 16384 ? 16384 : (q + 255) / 256);
+  splitk_reduce<<<rgrid, 256, 0, stream>>>(part, pl.splits, alpha, D, M * N);
   return hipGetLastError();
 }
 
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M <= kSkinnyMaxM) return 0;
+  const Plan pl = plan_tiled(M, N, K, device_cus());
+  return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 
 }  // namespace bsfp4

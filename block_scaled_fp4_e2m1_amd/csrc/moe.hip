@@ -7,8 +7,8 @@
 // reads the whole id list (L2-resident): it counts the ids below its expert
 // (its row offset), then stably compacts the flat indices equal to it with
 // block-wide prefix sums.  No atomics, no workspace, deterministic output.
-// The combine of the down projection accumulates into an FP32 buffer that is
-// cleared first and rounded to bf16 last by the two elementwise kernels here.
+// The combine of the down projection sums each token's top-k weighted FP32
+// rows in slot order and rounds once to bf16 (topk_sum_bf16).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -91,33 +91,26 @@ __global__ void __launch_bounds__(kPrepThreads)
   }
 }
 
-__global__ void __launch_bounds__(256) fill_zero_f32(float* __restrict__ p, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
-    if (i + 4 <= n) {
-      *reinterpret_cast<float4*>(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-      for (int64_t j = i; j < n; j++) p[j] = 0.0f;
-    }
-  }
-}
-
+// out[t, n] = bf16(sum_{j < topk} y[t*topk + j, n]), summed in slot order.
+// Each thread produces 4 consecutive columns (128-bit loads of each slot row).
 __global__ void __launch_bounds__(256)
-    f32_to_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
-  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
-    if (i + 4 <= n) {
-      const float4 v = *reinterpret_cast<const float4*>(src + i);
-      *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-    } else {
-      for (int64_t j = i; j < n; j++) dst[j] = (uint16_t)float_to_bf16_rne(src[j]);
+    topk_sum_bf16(const float* __restrict__ y, uint16_t* __restrict__ out, int64_t T, int topk, int N) {
+  const int64_t quads = T * (int64_t)(N / 4);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
+    const int64_t t = q / (N / 4);
+    const int n = (int)(q - t * (N / 4)) * 4;
+    const float* src = y + (t * topk) * (int64_t)N + n;
+    float4 s = *reinterpret_cast<const float4*>(src);
+    for (int j = 1; j < topk; j++) {
+      const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)j * N);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
     }
+    *reinterpret_cast<uint2*>(out + t * N + n) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
   }
-}
-
-unsigned elementwise_grid(int64_t n) {
-  const int64_t want = (n / 4 + 255) / 256;
-  return (unsigned)(want < 1 ? 1 : (want > 8192 ? 8192 : want));
 }
 
 }  // namespace
@@ -129,13 +122,11 @@ hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
-  fill_zero_f32<<<elementwise_grid(n), 256, 0, stream>>>(p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_f32_to_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream) {
-  f32_to_bf16<<<elementwise_grid(n), 256, 0, stream>>>(src, dst, n);
+hipError_t launch_topk_sum(const float* y, uint16_t* out, int64_t T, int64_t topk, int64_t N, hipStream_t stream) {
+  const int64_t quads = T * (N / 4);
+  const int64_t want = (quads + 255) / 256;
+  const unsigned grid = (unsigned)(want < 1 ? 1 : (want > 16384 ? 16384 : want));
+  topk_sum_bf16<<<grid, 256, 0, stream>>>(y, out, T, (int)topk, (int)N);
   return hipGetLastError();
 }
 

@@ -175,26 +175,33 @@ BSFP4_API bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t 
                           int32_t* sorted_tokens, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
- * mxfp4_moe_grouped_gemm: for every expert e, rows [off[e], off[e+1]) of the
- * expert-sorted MXFP4 activations times expert e's MXFP4 weights
- * ("[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on SM12x": MXFP4 x MXFP4 grouped
- * GEMM over per-expert weights).  alpha is 1.  A persistent grid walks the
- * list of (expert, row tile, column tile) work items.
- *   Aq, Asf          device [rows, K/2], [rows, K/32]; rows = T*topk
- *   expert_offsets   device int32 [E+1] (from fp4_moe_prep)
+ * mxfp4_moe_grouped_gemm: for every expert e, problem rows [off[e], off[e+1])
+ * times expert e's MXFP4 weights ("[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on
+ * SM12x": MXFP4 x MXFP4 grouped GEMM over per-expert weights).  alpha is 1.
+ * A persistent grid walks the list of (expert, column tile, row tile) items.
+ *   Aq, Asf          device [a_rows_total, K/2] codes, [a_rows_total, K/32]
+ *                    E8M0 scales
+ *   a_row_index      device int32 [rows] or NULL: problem row m reads row
+ *                    a_row_index[m] of Aq (e.g. the token of a sorted row, so
+ *                    activations are quantised once per token); entries outside
+ *                    [0, a_rows_total) read as zero.  NULL: row m reads row m
+ *                    and a_rows_total must equal rows.
+ *   expert_offsets   device int32 [E+1] (from fp4_moe_prep), 1 <= E <= 1024
+ *   rows             problem rows (T*topk for a routed layer)
  *   W, Wsf           device [E, N, K/2], [E, N, K/32]
- *   N % 64 == 0, K % 128 == 0
+ *   N % 32 == 0 (N % 64 == 0 for SILU_MUL_QUANT), K % 32 == 0
  *   epilogue         one of bsfp4_moe_epilogue; its fields in `ep`:
  *     BSFP4_MOE_STORE_BF16:  ep.out = bf16 [rows, N]
  *     BSFP4_MOE_SILU_MUL_QUANT: act = bf16(silu(h[:, :N/2]) * h[:, N/2:])
- *         with h the bf16-rounded GEMM row, then MXFP4-quantised into
- *         ep.out_q [rows, N/4] and ep.out_sf [rows, N/64]
- *         (the fused `silu_and_mul_scaled_fp4_experts_quant` pattern of
- *         the vLLM page's `csrc/ops.h`, in its MXFP4 form)
+ *         with h the bf16-rounded GEMM row, MXFP4-quantised into
+ *         ep.out_q [rows, N/4] and ep.out_sf [rows, N/64] (the fused
+ *         `silu_and_mul_scaled_fp4_experts_quant` pattern of the vLLM `sm103`
+ *         branch comparison page, `csrc/ops.h`, in its MXFP4 form)
  *     BSFP4_MOE_WEIGHTED_COMBINE: ep.out = bf16 [T, N] with
- *         out[t] = bf16(sum_j w[t,j] * Y[row(t,j)]), summed in FP32;
- *         uses ep.sorted_ids, ep.topk_weights [T*topk], ep.num_tokens,
- *         ep.topk, and T*N*4 bytes of workspace
+ *         out[t] = bf16(sum_j w[t,j] * Y[row(t,j)]): each row's product with
+ *         its routing weight is kept in FP32 (workspace, rows*N*4 bytes) and
+ *         the top-k rows of a token are summed in slot order (deterministic);
+ *         uses ep.sorted_ids, ep.topk_weights [T*topk], ep.num_tokens, ep.topk
  *   ws               device workspace of
  *                    mxfp4_moe_grouped_gemm_workspace_size(...) bytes
  * ------------------------------------------------------------------------- */
@@ -217,10 +224,11 @@ typedef struct bsfp4_moe_epilogue_args {
 BSFP4_API size_t mxfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K,
                                              int epilogue, int64_t num_tokens);
 BSFP4_API bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf,
-                                    const int32_t* expert_offsets, int64_t E, int64_t rows,
-                                    const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
-                                    int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
-                                    size_t ws_bytes, void* stream);
+                                              int64_t a_rows_total, const int32_t* a_row_index,
+                                              const int32_t* expert_offsets, int64_t E, int64_t rows,
+                                              const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                              int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
+                                              size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -89,6 +89,22 @@ def test_nvfp4_gemm_sweep_small(M):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(512, 4096, 7168, 124), (2048, 4096, 7168, 125),
+                                        (256, 14336, 4096, 110), (128, 4096, 7168, 126)])
+def test_nvfp4_gemm_split_k_shapes(M, N, K, seed):
+    """Mid-M shapes run with 128x128 tiles and/or a K split reduced in FP32."""
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=seed, b_std=0.02)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    rows = None if M <= 512 else np.unique(np.concatenate([[0, M - 1],
+                                                           np.random.default_rng(2).choice(M, 62, replace=False)]))
+    _check(got, aq, sfa, bq, sfb, alpha, rows=rows)
+
+
+def test_nvfp4_gemm_split_k_deterministic():
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(256, 256, 7168, seed=8)
+    assert np.array_equal(_run(aq, sfa, bq, sfb, alpha), _run(aq, sfa, bq, sfb, alpha))
+
+
 def test_nvfp4_gemm_large_workload_sampled():
     """4096 x 4096 x 7168: every output of 48 sampled rows (incl. first/last)."""
     aq, sfa, bq, sfb, alpha = nvfp4_problem(4096, 4096, 7168, seed=120)

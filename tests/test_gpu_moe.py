@@ -73,17 +73,25 @@ def _gpu_stages(x, ids, w, W13q, W13sf, W2q, W2sf):
     E = W13q.shape[0]
     T, topk = ids.shape
     offs, sids, stok = bs.moe_prep(dev_i32(ids), E)
-    xq, xsf = bs.quantize(dev_bf16(x), "mxfp4", row_map=stok)
+    dx = dev_bf16(x)
+    # experts quant as a row gather (one quantised row per routed pair) ...
+    xq_rows, xsf_rows = bs.quantize(dx, "mxfp4", row_map=stok)
+    # ... and the layer's form: each token quantised once, rows read by token
+    xq_tok, xsf_tok = bs.quantize(dx, "mxfp4")
     dW13, dW13sf = dev_u8(W13q), dev_u8(W13sf)
-    h1 = bs.mxfp4_moe_grouped_gemm(xq, xsf, offs, dW13, dW13sf, bs.MOE_STORE_BF16)
-    aq, asf = bs.mxfp4_moe_grouped_gemm(xq, xsf, offs, dW13, dW13sf, bs.MOE_SILU_MUL_QUANT)
+    h1 = bs.mxfp4_moe_grouped_gemm(xq_tok, xsf_tok, offs, dW13, dW13sf, bs.MOE_STORE_BF16,
+                                   a_row_index=stok)
+    h1_rows = bs.mxfp4_moe_grouped_gemm(xq_rows, xsf_rows, offs, dW13, dW13sf, bs.MOE_STORE_BF16)
+    aq, asf = bs.mxfp4_moe_grouped_gemm(xq_tok, xsf_tok, offs, dW13, dW13sf, bs.MOE_SILU_MUL_QUANT,
+                                        a_row_index=stok)
     out = bs.mxfp4_moe_grouped_gemm(aq, asf, offs, dev_u8(W2q), dev_u8(W2sf), bs.MOE_WEIGHTED_COMBINE,
                                     sorted_ids=sids, topk_weights=dev_f32(w.reshape(-1)),
                                     num_tokens=T, topk=topk)
     torch.cuda.synchronize()
-    return dict(offsets=offs.cpu().numpy(), sorted_ids=sids.cpu().numpy(), xq=xq.cpu().numpy(),
-                xsf=xsf.cpu().numpy(), h1=host_bf16_bits(h1), aq=aq.cpu().numpy(), asf=asf.cpu().numpy(),
-                out=host_bf16_bits(out))
+    return dict(offsets=offs.cpu().numpy(), sorted_ids=sids.cpu().numpy(), xq=xq_rows.cpu().numpy(),
+                xsf=xsf_rows.cpu().numpy(), xq_tok=xq_tok.cpu().numpy(), xsf_tok=xsf_tok.cpu().numpy(),
+                h1=host_bf16_bits(h1), h1_rows=host_bf16_bits(h1_rows), aq=aq.cpu().numpy(),
+                asf=asf.cpu().numpy(), out=host_bf16_bits(out))
 
 
 def _check_stages(x, ids, w, W13q, W13sf, W2q, W2sf, g):
@@ -92,6 +100,10 @@ def _check_stages(x, ids, w, W13q, W13sf, W2q, W2sf, g):
     assert np.array_equal(g["offsets"], offs) and np.array_equal(g["sorted_ids"], sids)
     xq, xsf = OM.experts_quant(x, sids, topk)
     assert np.array_equal(g["xq"], xq) and np.array_equal(g["xsf"], xsf)
+    tq, tsf = OQ.mxfp4_quantize(x)
+    assert np.array_equal(g["xq_tok"], tq) and np.array_equal(g["xsf_tok"], tsf)
+    # reading activations by token index gives the same products as the gathered copy
+    assert np.array_equal(g["h1"], g["h1_rows"])
     # gate_up GEMM on the GPU's (identical) quantised activations
     ref_h1 = F.bf16_rne_from_f64(OM.grouped_gemm_f64(g["xq"], g["xsf"], offs, W13q, W13sf))
     ok, worst, nbad = TOL.check_bf16(g["h1"], ref_h1)
