@@ -30,8 +30,8 @@
 //            pattern of the vLLM `sm103` branch comparison page, MXFP4 form);
 //   COMBINE  y[f] = topk_weight[f] * row in FP32 for the row's flat (token, slot)
 //            index f; a second kernel sums each token's top-k rows in slot order
-//            and rounds once to bf16 (deterministic; device-wide float atomics
-//            across the 8 XCDs measured 12x slower than this two-pass form).
+//            and rounds once to bf16 (deterministic; the same layer with device-wide
+//            float atomics for the combine measured about 2x slower).
 #include "device_common.h"
 #include "launchers.h"
 #include "quant_device.h"

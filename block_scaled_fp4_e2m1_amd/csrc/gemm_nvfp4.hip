@@ -32,13 +32,15 @@
 // a stage the K index assigned to a lane's values is a fixed permutation shared
 // by A and B, which leaves the sum unchanged; each lane's eight values always
 // lie inside one 16-element scale block.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "launchers.h"
 
 namespace bsfp4 {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kStageK = 128;              // K elements per stage
 constexpr int kStageBytes = kStageK / 2;  // 64 code bytes per row per stage
 constexpr int kStageBlocks = kStageK / 16;  // 8 E4M3 scales per row per stage
@@ -48,22 +50,22 @@ constexpr int kStageBlocks = kStageK / 16;  // 8 E4M3 scales per row per stage
 // consecutive rows touch 8 (or 16) distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
-template <int ROWS>
+template <int ROWS, int NT>
 struct StageRegs {
-  static constexpr int kChunks = ROWS * 4 / kThreads;  // 16-byte code chunks per thread
+  static constexpr int kChunks = ROWS * 4 / NT;  // 16-byte code chunks per thread
   uint4 code[kChunks];
   uint32_t sc[2];  // 8 scale bytes of row `tid` (threads < ROWS)
 };
 
-template <int ROWS>
-__device__ __forceinline__ void load_stage(StageRegs<ROWS>& st, const uint8_t* __restrict__ q,
+template <int ROWS, int NT>
+__device__ __forceinline__ void load_stage(StageRegs<ROWS, NT>& st, const uint8_t* __restrict__ q,
                                            const uint8_t* __restrict__ sf, int row0, int nrows,
                                            int64_t K, int k0, int tid) {
   const int64_t row_bytes = K / 2;
   const int64_t row_blocks = K / 16;
 #pragma unroll
-  for (int i = 0; i < StageRegs<ROWS>::kChunks; i++) {
-    const int idx = tid + i * kThreads;
+  for (int i = 0; i < StageRegs<ROWS, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
     const int r = idx >> 2, c = idx & 3;
     const int64_t kb = (int64_t)k0 / 2 + c * 16;  // byte offset in the row
     if (row0 + r < nrows && kb < row_bytes) {
@@ -88,12 +90,12 @@ __device__ __forceinline__ void load_stage(StageRegs<ROWS>& st, const uint8_t* _
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void store_stage(const StageRegs<ROWS>& st, uint8_t* lds_q, uint8_t* lds_s,
+template <int ROWS, int NT>
+__device__ __forceinline__ void store_stage(const StageRegs<ROWS, NT>& st, uint8_t* lds_q, uint8_t* lds_s,
                                             int tid) {
 #pragma unroll
-  for (int i = 0; i < StageRegs<ROWS>::kChunks; i++) {
-    const int idx = tid + i * kThreads;
+  for (int i = 0; i < StageRegs<ROWS, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
     const int r = idx >> 2, c = idx & 3;
     *reinterpret_cast<uint4*>(lds_q + r * kStageBytes + swz(r, c) * 16) = st.code[i];
   }
@@ -127,13 +129,14 @@ __device__ __forceinline__ v8h dequant8(uint32_t word, _Float16 s) {
 // splits == 1: D = bf16(alpha * acc).  splits > 1: workgroup (tile, s) sums
 // the s-th contiguous range of K stages and writes its FP32 partial tile to
 // part[s][M][N]; a second kernel adds the partials in split order.
-template <int BM, int BN>
-__global__ void __launch_bounds__(kThreads, 1)
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
     nvfp4_gemm_tiled(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA,
                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
                      const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N,
                      int64_t K, int tiles_n, int splits, float* __restrict__ part) {
-  constexpr int WM = BM / 2, WN = BN / 2;     // wave tile
+  constexpr int NT = 64 * WGM * WGN;          // threads
+  constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
   constexpr int TM = WM / 32, TN = WN / 32;   // 32x32 MFMA tiles per wave
   constexpr int kABytes = BM * kStageBytes, kBBytes = BN * kStageBytes;
   constexpr int kStage = kABytes + kBBytes + (BM + BN) * kStageBlocks;
@@ -142,7 +145,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int split = blockIdx.x % splits;
   const int tile = blockIdx.x / splits;
   const int tile_m = tile / tiles_n, tile_n = tile % tiles_n;
@@ -159,14 +162,14 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int s_end = (int)((int64_t)total_stages * (split + 1) / splits);
   const int nstages = s_end - s_begin;
   const int kbase = s_begin * kStageK;
-  StageRegs<BM> ra;
-  StageRegs<BN> rb;
-  load_stage<BM>(ra, A, SFA, m0, M, K, kbase, tid);
-  load_stage<BN>(rb, B, SFB, n0, N, K, kbase, tid);
+  StageRegs<BM, NT> ra;
+  StageRegs<BN, NT> rb;
+  load_stage<BM, NT>(ra, A, SFA, m0, M, K, kbase, tid);
+  load_stage<BN, NT>(rb, B, SFB, n0, N, K, kbase, tid);
   {
     uint8_t* s = smem;
-    store_stage<BM>(ra, s, s + kABytes + kBBytes, tid);
-    store_stage<BN>(rb, s + kABytes, s + kABytes + kBBytes + BM * kStageBlocks, tid);
+    store_stage<BM, NT>(ra, s, s + kABytes + kBBytes, tid);
+    store_stage<BN, NT>(rb, s + kABytes, s + kABytes + kBBytes + BM * kStageBlocks, tid);
   }
   __syncthreads();
 
@@ -176,8 +179,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   for (int s = 0; s < nstages; s++) {
     const bool more = (s + 1) < nstages;
     if (more) {
-      load_stage<BM>(ra, A, SFA, m0, M, K, kbase + (s + 1) * kStageK, tid);
-      load_stage<BN>(rb, B, SFB, n0, N, K, kbase + (s + 1) * kStageK, tid);
+      load_stage<BM, NT>(ra, A, SFA, m0, M, K, kbase + (s + 1) * kStageK, tid);
+      load_stage<BN, NT>(rb, B, SFB, n0, N, K, kbase + (s + 1) * kStageK, tid);
     }
     const uint8_t* st = smem + (s & 1) * kStage;
     const uint8_t* sq_a = st;
@@ -223,8 +226,8 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     if (more) {
       uint8_t* nx = smem + ((s + 1) & 1) * kStage;
-      store_stage<BM>(ra, nx, nx + kABytes + kBBytes, tid);
-      store_stage<BN>(rb, nx + kABytes, nx + kABytes + kBBytes + BM * kStageBlocks, tid);
+      store_stage<BM, NT>(ra, nx, nx + kABytes + kBBytes, tid);
+      store_stage<BN, NT>(rb, nx + kABytes, nx + kABytes + kBBytes + BM * kStageBlocks, tid);
     }
     __syncthreads();
   }
@@ -254,6 +257,185 @@ __global__ void __launch_bounds__(kThreads, 1)
         for (int r = 0; r < 16; r++) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (m < M && n < N) dst[(int64_t)m * N + n] = acc[i][jn][r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantise-once variant.  Each workgroup converts every E2M1 value of its
+// tile exactly once, while writing a K stage into LDS, and the waves then read
+// ready fp16 fragments: with 128x128 wave tiles this is ~2 VALU instructions per
+// MFMA instead of ~9 when every wave dequantises the fragments it reads (each
+// fragment is read by two waves).  The fp4 stages are prefetched from HBM
+// kLook stages ahead into registers; LDS holds two fp16 stages of 64 K values
+// (256 rows x 128 B per operand, 16-byte chunks swizzled so that the 8 or 16
+// lanes of one ds_read_b128 phase hit distinct banks).
+constexpr int kF16StageK = 64;   // K values per fp16 LDS stage
+constexpr int kLook = 3;         // fp4 stages in flight ahead of the one computed
+
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+template <int ROWS, int NT>
+struct Fp4Stage {
+  static constexpr int kChunks = ROWS * 2 / NT;  // 16-byte (32-value) chunks per thread
+  uint4 code[kChunks];
+  uint32_t sc[kChunks];                          // the chunk's two E4M3 scale bytes
+};
+
+template <int ROWS, int NT>
+__device__ __forceinline__ void fp4_stage_load(Fp4Stage<ROWS, NT>& st, const uint8_t* __restrict__ q,
+                                               const uint8_t* __restrict__ sf, int row0, int nrows,
+                                               int64_t K, int64_t k0, int tid) {
+  const int64_t row_bytes = K / 2, row_blocks = K / 16;
+#pragma unroll
+  for (int i = 0; i < Fp4Stage<ROWS, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
+    const int r = idx >> 1, c = idx & 1;
+    const int64_t kb = k0 / 2 + c * 16;
+    const bool ok = row0 + r < nrows && kb < row_bytes;
+    const int64_t row = ok ? row0 + r : 0;
+    st.code[i] = ok ? *reinterpret_cast<const uint4*>(q + row * row_bytes + kb) : make_uint4(0, 0, 0, 0);
+    st.sc[i] = ok ? *reinterpret_cast<const uint16_t*>(sf + row * row_blocks + k0 / 16 + 2 * c) : 0u;
+  }
+}
+
+// Dequantise the thread's chunks and write them as fp16 into the LDS stage
+// (row-major, 64 values = 128 B per row, chunk position swizzled).
+template <int ROWS, int NT>
+__device__ __forceinline__ void fp4_stage_store_f16(const Fp4Stage<ROWS, NT>& st, uint8_t* lds, int tid) {
+#pragma unroll
+  for (int i = 0; i < Fp4Stage<ROWS, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
+    const int r = idx >> 1, c = idx & 1;
+    const v2h s01 = e4m3x2_to_f16x2(st.sc[i]);
+    const uint32_t w[4] = {st.code[i].x, st.code[i].y, st.code[i].z, st.code[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {  // 8 values per word; words 0,1 use scale 0, words 2,3 scale 1
+      const v8h f = dequant8(w[j], j < 2 ? s01.x : s01.y);
+      *reinterpret_cast<v8h*>(lds + r * 128 + swz8(r, c * 4 + j) * 16) = f;
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN, 1)
+    nvfp4_gemm_f16lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA,
+                      const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
+                      const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N,
+                      int64_t K, int tiles_m, int tiles_n, int splits, float* __restrict__ part) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int kA = BM * 128, kB = BN * 128;  // fp16 stage bytes per operand
+  constexpr int kStage = kA + kB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int g = lane >> 5, lr = lane & 31;
+
+  // work item -> (tile, split).  Workgroups are dispatched round-robin over the
+  // 8 XCDs; consecutive items go to one XCD, and items are ordered in bands of 4
+  // tile rows so an XCD's items share few A and B panels in its L2.
+  const int items = tiles_m * tiles_n * splits;
+  int item = blockIdx.x;
+  if (items % 8 == 0) item = (int)(blockIdx.x % 8) * (items / 8) + (int)(blockIdx.x / 8);
+  const int split = item % splits;
+  const int tile = item / splits;
+  constexpr int kBand = 4;
+  const int band_tiles = kBand * tiles_n;
+  const int band = tile / band_tiles, in_band = tile % band_tiles;
+  const int band_rows = min(kBand, tiles_m - band * kBand);
+  const int tile_m = band * kBand + in_band % band_rows;
+  const int tile_n = in_band / band_rows;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
+
+  const int total = (int)((K + kF16StageK - 1) / kF16StageK);
+  const int sb = (int)((int64_t)total * split / splits);
+  const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
+  const int64_t kbase = (int64_t)sb * kF16StageK;
+
+  Fp4Stage<BM, NT> ra[kLook];
+  Fp4Stage<BN, NT> rb[kLook];
+#pragma unroll
+  for (int t = 0; t < kLook; t++) {
+    if (t < nst) {
+      fp4_stage_load<BM, NT>(ra[t], A, SFA, m0, M, K, kbase + t * kF16StageK, tid);
+      fp4_stage_load<BN, NT>(rb[t], B, SFB, n0, N, K, kbase + t * kF16StageK, tid);
+    }
+  }
+  if (nst > 0) {
+    fp4_stage_store_f16<BM, NT>(ra[0], smem, tid);
+    fp4_stage_store_f16<BN, NT>(rb[0], smem + kA, tid);
+  }
+  __syncthreads();
+
+  for (int s = 0; s < nst; s++) {
+    // the register set of stage s+1 (loaded kLook-1 iterations ago) -> LDS slot (s+1)%2
+    // (every wave finished reading that slot before the barrier that ended s-1)
+#pragma unroll
+    for (int t = 0; t < kLook; t++) {
+      if (t == (s + 1) % kLook && s + 1 < nst) {
+        uint8_t* nx = smem + ((s + 1) & 1) * kStage;
+        fp4_stage_store_f16<BM, NT>(ra[t], nx, tid);
+        fp4_stage_store_f16<BN, NT>(rb[t], nx + kA, tid);
+      }
+    }
+    // stage s's register set is free: prefetch stage s + kLook into it
+#pragma unroll
+    for (int t = 0; t < kLook; t++) {
+      if (t == s % kLook && s + kLook < nst) {
+        fp4_stage_load<BM, NT>(ra[t], A, SFA, m0, M, K, kbase + (int64_t)(s + kLook) * kF16StageK, tid);
+        fp4_stage_load<BN, NT>(rb[t], B, SFB, n0, N, K, kbase + (int64_t)(s + kLook) * kF16StageK, tid);
+      }
+    }
+    const uint8_t* qa = smem + (s & 1) * kStage;
+    const uint8_t* qb = qa + kA;
+#pragma unroll
+    for (int kk = 0; kk < kF16StageK / 16; kk++) {
+      const int c = 2 * kk + g;  // fp16 chunk: K values 16kk + 8g .. +8
+      v8h fb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const int r = wn * WN + j * 32 + lr;
+        fb[j] = *reinterpret_cast<const v8h*>(qb + r * 128 + swz8(r, c) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int r = wm * WM + i * 32 + lr;
+        const v8h fa = *reinterpret_cast<const v8h*>(qa + r * 128 + swz8(r, c) * 16);
+#pragma unroll
+        for (int j = 0; j < TN; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  float* dst = part + (int64_t)split * M * N;
+#pragma unroll
+  for (int i = 0; i < TM; i++) {
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      const int n = n0 + wn * WN + j * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < M && n < N) {
+          if (splits == 1)
+            D[(int64_t)m * N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][j][r]);
+          else
+            dst[(int64_t)m * N + n] = acc[i][j][r];
         }
       }
     }
@@ -327,6 +509,22 @@ int device_cus() {
 
 }  // namespace
 
+// 256x256 tiles: the dequantise-once kernel with 8 waves of 128x64 by default.
+// BSFP4_NVFP4_KERNEL selects an alternative for measurements: "lds4" (same
+// kernel, 4 waves of 128x128), "reg8" / "reg4" (per-wave register
+// dequantisation, 8 or 4 waves).
+static int nvfp4_variant() {
+  static const int v = [] {
+    const char* e = getenv("BSFP4_NVFP4_KERNEL");
+    if (!e) return 0;
+    if (!strcmp(e, "lds4")) return 1;
+    if (!strcmp(e, "reg8")) return 2;
+    if (!strcmp(e, "reg4")) return 3;
+    return 0;
+  }();
+  return v;
+}
+
 hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                              const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -338,12 +536,28 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
   const int tiles_m = (int)((M + pl.bm - 1) / pl.bm);
   const int tiles_n = (int)((N + pl.bn - 1) / pl.bn);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * pl.splits);
-  if (pl.bm == 256)
-    nvfp4_gemm_tiled<256, 256><<<grid, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                              tiles_n, pl.splits, part);
-  else
-    nvfp4_gemm_tiled<128, 128><<<grid, kThreads, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                              tiles_n, pl.splits, part);
+  if (pl.bm == 256) {
+    switch (nvfp4_variant()) {
+      case 1:
+        nvfp4_gemm_f16lds<256, 256, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                                    tiles_m, tiles_n, pl.splits, part);
+        break;
+      case 2:
+        nvfp4_gemm_tiled<256, 256, 2, 4><<<grid, 512, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                                   tiles_n, pl.splits, part);
+        break;
+      case 3:
+        nvfp4_gemm_tiled<256, 256, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                                   tiles_n, pl.splits, part);
+        break;
+      default:
+        nvfp4_gemm_f16lds<256, 256, 2, 4><<<grid, 512, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                                    tiles_m, tiles_n, pl.splits, part);
+    }
+  } else {
+    nvfp4_gemm_tiled<128, 128, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
+                                                               tiles_n, pl.splits, part);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t q = M * N / 4;
