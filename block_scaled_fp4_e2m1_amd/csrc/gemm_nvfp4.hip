@@ -32,6 +32,7 @@
 // a stage the K index assigned to a lane's values is a fixed permutation shared
 // by A and B, which leaves the sum unchanged; each lane's eight values always
 // lie inside one 16-element scale block.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -266,59 +267,153 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 // ---------------------------------------------------------------------------
 // Dequantise-once variant.  Each workgroup converts every E2M1 value of its
 // tile exactly once, while writing a K stage into LDS, and the waves then read
-// ready fp16 fragments: with 128x128 wave tiles this is ~2 VALU instructions per
-// MFMA instead of ~9 when every wave dequantises the fragments it reads (each
-// fragment is read by two waves).  The fp4 stages are prefetched from HBM
-// kLook stages ahead into registers; LDS holds two fp16 stages of 64 K values
-// (256 rows x 128 B per operand, 16-byte chunks swizzled so that the 8 or 16
-// lanes of one ds_read_b128 phase hit distinct banks).
+// ready fp16 fragments (each fragment is read by two or four waves, which with
+// per-wave dequantisation costs ~9 VALU instructions per MFMA; here ~2).
+//
+// Memory side.  Codes and scales are fetched in groups of 128 K values (two
+// LDS stages) with buffer loads: four consecutive lanes read the four 16-byte
+// chunks of one row's 64 bytes, so every load instruction touches 16 cache
+// lines instead of 32, and the scale bytes of those chunks come from one line
+// per row.  Rows outside the matrix and K beyond the tile's range read as zero
+// (buffer range check, no branches).  Lane m of a quad takes chunk
+// 2*((i + m/2) % 2) + m%2 in its i-th load, so each lane holds chunks of both
+// LDS stages of the group and the dequantisation work is balanced.
+//
+// Pipeline.  A group's registers hold two LDS stages.  While the waves run the
+// MFMAs of stage s from LDS slot s%2 they dequantise stage s+1 into the other
+// slot (word by word between the MFMAs); one barrier per stage.  The next
+// group is loaded at the top of the current one, a full stage before its
+// first use.
+// LDS: two fp16 stages, rows of 64 values padded to 144 B, so 16 lanes reading
+// (or writing) the same 16-byte chunk of 16 consecutive rows hit distinct bank
+// groups and every fragment address is a per-lane base plus a constant.
+// The MFMA takes the B fragment as its first operand, so each lane ends with
+// four consecutive output columns of one row: the epilogue scales by alpha,
+// rounds to bf16 and writes 8-byte vectors (FP32 16-byte vectors for split-K
+// partials).
 constexpr int kF16StageK = 64;   // K values per fp16 LDS stage
-constexpr int kLook = 3;         // fp4 stages in flight ahead of the one computed
+constexpr int kGroupK = 128;     // K values per load group
+constexpr int kF16Pitch = 144;   // LDS bytes per row of a stage (128 + 16 padding)
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every operand: loads return 0
 
-__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
 
-template <int ROWS, int NT>
-struct Fp4Stage {
-  static constexpr int kChunks = ROWS * 2 / NT;  // 16-byte (32-value) chunks per thread
+// The thread's chunks of one load group: chunk i is row (tid + i*NT)/4 of the
+// workgroup's BM + BN rows (A rows first).
+template <int BM, int BN, int NT>
+struct Fp4Group {
+  static constexpr int kChunks = (BM + BN) * 4 / NT;
+  static_assert((BM * 4) % NT == 0 && kChunks % 2 == 0, "operand split per load");
   uint4 code[kChunks];
-  uint32_t sc[kChunks];                          // the chunk's two E4M3 scale bytes
+  uint32_t sc[kChunks];  // the chunk's two E4M3 scale bytes
 };
 
-template <int ROWS, int NT>
-__device__ __forceinline__ void fp4_stage_load(Fp4Stage<ROWS, NT>& st, const uint8_t* __restrict__ q,
-                                               const uint8_t* __restrict__ sf, int row0, int nrows,
-                                               int64_t K, int64_t k0, int tid) {
-  const int64_t row_bytes = K / 2, row_blocks = K / 16;
+// Per-lane part of the buffer offsets; load i adds i*NT/4 rows (uniform) and
+// its chunk's column.  Rows outside the matrix get kOOB.
+template <int BM, int BN, int NT>
+struct Fp4GroupOffsets {
+  int64_t K;
+  int r0, m, mrows, nrows;  // lane's row in load 0, lane in quad, valid A / B rows of the tile
+  __device__ __forceinline__ Fp4GroupOffsets(int m0, int M, int n0, int N, int64_t K_, int tid)
+      : K(K_), r0(tid >> 2), m(tid & 3), mrows(M - m0), nrows(N - n0) {}
+  __device__ __forceinline__ int chunk(int i) const { return (i & 1) ? (m ^ 2) : m; }
+};
+
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void fp4_group_load(Fp4Group<BM, BN, NT>& g, __amdgpu_buffer_rsrc_t ra_q,
+                                               __amdgpu_buffer_rsrc_t ra_s, __amdgpu_buffer_rsrc_t rb_q,
+                                               __amdgpu_buffer_rsrc_t rb_s, const Fp4GroupOffsets<BM, BN, NT>& o,
+                                               int64_t k0, int64_t k_end) {
+  constexpr int kA = BM * 4 / NT;  // loads of A rows
 #pragma unroll
-  for (int i = 0; i < Fp4Stage<ROWS, NT>::kChunks; i++) {
-    const int idx = tid + i * NT;
-    const int r = idx >> 1, c = idx & 1;
-    const int64_t kb = k0 / 2 + c * 16;
-    const bool ok = row0 + r < nrows && kb < row_bytes;
-    const int64_t row = ok ? row0 + r : 0;
-    st.code[i] = ok ? *reinterpret_cast<const uint4*>(q + row * row_bytes + kb) : make_uint4(0, 0, 0, 0);
-    st.sc[i] = ok ? *reinterpret_cast<const uint16_t*>(sf + row * row_blocks + k0 / 16 + 2 * c) : 0u;
+  for (int i = 0; i < Fp4Group<BM, BN, NT>::kChunks; i++) {
+    const bool is_a = i < kA;
+    const int r = o.r0 + (is_a ? i : i - kA) * (NT / 4);  // row inside the operand's tile rows
+    const int c = o.chunk(i);
+    const bool live = r < (is_a ? o.mrows : o.nrows) && k0 + c * 32 < k_end;
+    // offsets are relative to the tile's first row (the buffer base)
+    const uint32_t oc = live ? (uint32_t)(r * (o.K / 2) + c * 16 + k0 / 2) : kOOB;
+    const uint32_t os = live ? (uint32_t)(r * (o.K / 16) + c * 2 + k0 / 16) : kOOB;
+    g.code[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is_a ? ra_q : rb_q, (int)oc, 0, 0));
+    g.sc[i] = __builtin_amdgcn_raw_buffer_load_b16(is_a ? ra_s : rb_s, (int)os, 0, 0);
   }
 }
 
-// Dequantise the thread's chunks and write them as fp16 into the LDS stage
-// (row-major, 64 values = 128 B per row, chunk position swizzled).
-template <int ROWS, int NT>
-__device__ __forceinline__ void fp4_stage_store_f16(const Fp4Stage<ROWS, NT>& st, uint8_t* lds, int tid) {
+// Word W of the thread's stage-H share of group g -> 8 fp16 values in LDS stage
+// `lds`.  The share is chunk pair j = W/4: load 2j or 2j+1, whichever holds
+// stage H for this lane.
+template <int W, int H, int BM, int BN, int NT>
+__device__ __forceinline__ void group_word_store(const Fp4Group<BM, BN, NT>& g, uint8_t* lds, int tid) {
+  constexpr int j = W / 4, w = W % 4;
+  const int m = tid & 3;
+  const bool odd = ((m >> 1) ^ H) & 1;  // this lane's stage-H chunk is load 2j+1
+  const uint4 c0 = g.code[2 * j], c1 = g.code[2 * j + 1];
+  const uint32_t word = w == 0 ? (odd ? c1.x : c0.x)
+                      : w == 1 ? (odd ? c1.y : c0.y)
+                      : w == 2 ? (odd ? c1.z : c0.z)
+                               : (odd ? c1.w : c0.w);
+  const uint32_t scp = odd ? g.sc[2 * j + 1] : g.sc[2 * j];
+  const v2h s01 = e4m3x2_to_f16x2(scp);  // words 0,1 take scale 0; words 2,3 scale 1
+  // row of load 2j (+NT/4 rows for load 2j+1); position of the chunk in the stage row
+  const int r = ((tid + 2 * j * NT) >> 2) + (odd ? NT / 4 : 0);
+  *reinterpret_cast<v8h*>(lds + r * kF16Pitch + ((m & 1) * 4 + w) * 16) = dequant8(word, w < 2 ? s01.x : s01.y);
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void f16_stage_compute(const uint8_t* qa, const uint8_t* qb,
+                                                  v16f (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                                  const Fp4Group<BM, BN, 64 * WGM * WGN>& g, uint8_t* nx, int tid,
+                                                  bool store_h1) {
+  // store_h1: dequantise this group's stage 1 (else the next group's stage 0,
+  // which the caller passes as g)
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int TM = BM / WGM / 32, TN = BN / WGN / 32;
+  constexpr int kWords = 4 * Fp4Group<BM, BN, NT>::kChunks / 2;  // words of one stage per thread
+  constexpr int kWordsPerStep = kWords / 4;
+  constexpr int kMfma = TM * TN;
+  static_assert(kWordsPerStep >= 1 && kWordsPerStep <= kMfma, "word spread");
+  // The dequantisation of the next stage is spread word by word between the
+  // MFMAs; scheduling fences keep this order (the compiler would otherwise
+  // hoist all LDS reads and VALU work above the MFMAs).
 #pragma unroll
-  for (int i = 0; i < Fp4Stage<ROWS, NT>::kChunks; i++) {
-    const int idx = tid + i * NT;
-    const int r = idx >> 1, c = idx & 1;
-    const v2h s01 = e4m3x2_to_f16x2(st.sc[i]);
-    const uint32_t w[4] = {st.code[i].x, st.code[i].y, st.code[i].z, st.code[i].w};
+  for (int kk = 0; kk < kF16StageK / 16; kk++) {
+    v8h fa[TM], fb[TN];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {  // 8 values per word; words 0,1 use scale 0, words 2,3 scale 1
-      const v8h f = dequant8(w[j], j < 2 ? s01.x : s01.y);
-      *reinterpret_cast<v8h*>(lds + r * 128 + swz8(r, c * 4 + j) * 16) = f;
+    for (int j = 0; j < TN; j++) fb[j] = *reinterpret_cast<const v8h*>(qb + j * 32 * kF16Pitch + kk * 32);
+#pragma unroll
+    for (int i = 0; i < TM; i++) fa[i] = *reinterpret_cast<const v8h*>(qa + i * 32 * kF16Pitch + kk * 32);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kMfma; t++) {
+      const int i = t / TN, j = t % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int w = 0; w < kWordsPerStep; w++) {
+        if (t == (w * kMfma) / kWordsPerStep) {
+          switch (kk * kWordsPerStep + w) {  // compile-time after unrolling
+#define BSFP4_W(x)                                                              \
+  case x:                                                                       \
+    if constexpr (x < kWords) {                                                 \
+      if (store_h1)                                                             \
+        group_word_store<x, 1, BM, BN, NT>(g, nx, tid);                         \
+      else                                                                      \
+        group_word_store<x, 0, BM, BN, NT>(g, nx, tid);                         \
+    }                                                                           \
+    break;
+            BSFP4_W(0) BSFP4_W(1) BSFP4_W(2) BSFP4_W(3) BSFP4_W(4) BSFP4_W(5) BSFP4_W(6) BSFP4_W(7)
+            BSFP4_W(8) BSFP4_W(9) BSFP4_W(10) BSFP4_W(11) BSFP4_W(12) BSFP4_W(13) BSFP4_W(14) BSFP4_W(15)
+#undef BSFP4_W
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
+// Requires M*K/2 and N*K/2 < 2^31 (buffer offsets), K % 32 == 0, N % 4 == 0.
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN, 1)
     nvfp4_gemm_f16lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA,
@@ -328,8 +423,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int kA = BM * 128, kB = BN * 128;  // fp16 stage bytes per operand
-  constexpr int kStage = kA + kB;
+  constexpr int kStage = (BM + BN) * kF16Pitch;  // fp16 stage bytes (A rows then B rows)
+  static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -362,80 +457,75 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   const int total = (int)((K + kF16StageK - 1) / kF16StageK);
   const int sb = (int)((int64_t)total * split / splits);
   const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
-  const int64_t kbase = (int64_t)sb * kF16StageK;
 
-  Fp4Stage<BM, NT> ra[kLook];
-  Fp4Stage<BN, NT> rb[kLook];
-#pragma unroll
-  for (int t = 0; t < kLook; t++) {
-    if (t < nst) {
-      fp4_stage_load<BM, NT>(ra[t], A, SFA, m0, M, K, kbase + t * kF16StageK, tid);
-      fp4_stage_load<BN, NT>(rb[t], B, SFB, n0, N, K, kbase + t * kF16StageK, tid);
-    }
-  }
   if (nst > 0) {
-    fp4_stage_store_f16<BM, NT>(ra[0], smem, tid);
-    fp4_stage_store_f16<BN, NT>(rb[0], smem + kA, tid);
-  }
-  __syncthreads();
+    // buffers start at the tile's first row; the range check uses what is left
+    const __amdgpu_buffer_rsrc_t ra_q = make_rsrc(A + (int64_t)m0 * (K / 2), (int64_t)(M - m0) * (K / 2));
+    const __amdgpu_buffer_rsrc_t ra_s = make_rsrc(SFA + (int64_t)m0 * (K / 16), (int64_t)(M - m0) * (K / 16));
+    const __amdgpu_buffer_rsrc_t rb_q = make_rsrc(B + (int64_t)n0 * (K / 2), (int64_t)(N - n0) * (K / 2));
+    const __amdgpu_buffer_rsrc_t rb_s = make_rsrc(SFB + (int64_t)n0 * (K / 16), (int64_t)(N - n0) * (K / 16));
+    const Fp4GroupOffsets<BM, BN, NT> off(m0, M, n0, N, K, tid);
+    const int64_t kbase = (int64_t)sb * kF16StageK;
+    const int64_t k_end = min(K, kbase + (int64_t)nst * kF16StageK);
+    const int ngroups = (nst + 1) / 2;
+    const uint8_t* fra = smem + (wm * WM + lr) * kF16Pitch + g * 16;
+    const uint8_t* frb = smem + (BM + wn * WN + lr) * kF16Pitch + g * 16;
 
-  for (int s = 0; s < nst; s++) {
-    // the register set of stage s+1 (loaded kLook-1 iterations ago) -> LDS slot (s+1)%2
-    // (every wave finished reading that slot before the barrier that ended s-1)
+    Fp4Group<BM, BN, NT> cur;
+    fp4_group_load<BM, BN, NT>(cur, ra_q, ra_s, rb_q, rb_s, off, kbase, k_end);
+    {
+      constexpr int kWords = 4 * Fp4Group<BM, BN, NT>::kChunks / 2;
 #pragma unroll
-    for (int t = 0; t < kLook; t++) {
-      if (t == (s + 1) % kLook && s + 1 < nst) {
-        uint8_t* nx = smem + ((s + 1) & 1) * kStage;
-        fp4_stage_store_f16<BM, NT>(ra[t], nx, tid);
-        fp4_stage_store_f16<BN, NT>(rb[t], nx + kA, tid);
-      }
-    }
-    // stage s's register set is free: prefetch stage s + kLook into it
-#pragma unroll
-    for (int t = 0; t < kLook; t++) {
-      if (t == s % kLook && s + kLook < nst) {
-        fp4_stage_load<BM, NT>(ra[t], A, SFA, m0, M, K, kbase + (int64_t)(s + kLook) * kF16StageK, tid);
-        fp4_stage_load<BN, NT>(rb[t], B, SFB, n0, N, K, kbase + (int64_t)(s + kLook) * kF16StageK, tid);
-      }
-    }
-    const uint8_t* qa = smem + (s & 1) * kStage;
-    const uint8_t* qb = qa + kA;
-#pragma unroll
-    for (int kk = 0; kk < kF16StageK / 16; kk++) {
-      const int c = 2 * kk + g;  // fp16 chunk: K values 16kk + 8g .. +8
-      v8h fb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; j++) {
-        const int r = wn * WN + j * 32 + lr;
-        fb[j] = *reinterpret_cast<const v8h*>(qb + r * 128 + swz8(r, c) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; i++) {
-        const int r = wm * WM + i * 32 + lr;
-        const v8h fa = *reinterpret_cast<const v8h*>(qa + r * 128 + swz8(r, c) * 16);
-#pragma unroll
-        for (int j = 0; j < TN; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb[j], acc[i][j], 0, 0, 0);
+      for (int w = 0; w < kWords; w++) {
+        switch (w) {
+#define BSFP4_W(x) \
+  case x:          \
+    if constexpr (x < kWords) group_word_store<x, 0, BM, BN, NT>(cur, smem, tid); \
+    break;
+          BSFP4_W(0) BSFP4_W(1) BSFP4_W(2) BSFP4_W(3) BSFP4_W(4) BSFP4_W(5) BSFP4_W(6) BSFP4_W(7)
+          BSFP4_W(8) BSFP4_W(9) BSFP4_W(10) BSFP4_W(11) BSFP4_W(12) BSFP4_W(13) BSFP4_W(14) BSFP4_W(15)
+#undef BSFP4_W
+        }
       }
     }
     __syncthreads();
+
+    for (int gi = 0; gi < ngroups; gi++) {
+      Fp4Group<BM, BN, NT> nxt;
+      fp4_group_load<BM, BN, NT>(nxt, ra_q, ra_s, rb_q, rb_s, off, kbase + (int64_t)(gi + 1) * kGroupK, k_end);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the group
+      // stage 2gi (slot 0): dequantise stage 2gi+1 of this group into slot 1
+      f16_stage_compute<BM, BN, WGM, WGN>(fra, frb, acc, cur, smem + kStage, tid, true);
+      __syncthreads();
+      // stage 2gi+1 (slot 1): dequantise stage 0 of the next group into slot 0.
+      // With an odd stage count the last one reads zeros (its K range lies past
+      // k_end, so its codes and scales were loaded as zero) and adds nothing;
+      // the loop keeps a single exit, which keeps register allocation sane.
+      f16_stage_compute<BM, BN, WGM, WGN>(fra + kStage, frb + kStage, acc, nxt, smem, tid, false);
+      __syncthreads();
+      cur = nxt;
+    }
   }
 
+  // lane: output row m (its MFMA column), registers 4q..4q+3: columns n..n+3
+  // (N % 4 == 0: the 4 columns are all in range or all out)
   const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
   float* dst = part + (int64_t)split * M * N;
 #pragma unroll
   for (int i = 0; i < TM; i++) {
+    const int m = m0 + wm * WM + i * 32 + lr;
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-      const int n = n0 + wn * WN + j * 32 + lr;
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M && n < N) {
-          if (splits == 1)
-            D[(int64_t)m * N + n] = (uint16_t)float_to_bf16_rne(alpha * acc[i][j][r]);
-          else
-            dst[(int64_t)m * N + n] = acc[i][j][r];
+      for (int q = 0; q < 4; q++) {
+        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
+        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (splits == 1) {
+          const uint2 o = make_uint2(pack_bf16x2(alpha * v0, alpha * v1), pack_bf16x2(alpha * v2, alpha * v3));
+          if (m < M && n < N) *reinterpret_cast<uint2*>(D + (int64_t)m * N + n) = o;
+        } else {
+          if (m < M && n < N) *reinterpret_cast<float4*>(dst + (int64_t)m * N + n) = make_float4(v0, v1, v2, v3);
         }
       }
     }
@@ -470,14 +560,23 @@ struct Plan {
 // estimated time is (rounds of work items) x (work per item) / (tile
 // efficiency) plus the FP32 partial traffic of a split.  Efficiencies are the
 // measured fractions of MFMA peak of the two tile shapes.
+// Test and measurement overrides, read on every call: BSFP4_NVFP4_TILE=256|128
+// forces the tile shape, BSFP4_NVFP4_SPLITS=n the number of K splits.
+int env_int(const char* name) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : 0;
+}
+
 Plan plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t stages = (K + kStageK - 1) / kStageK;
   Plan best{256, 256, 1};
   double best_t = 1e300;
   const int shapes[2][2] = {{256, 256}, {128, 128}};
   const double eff[2] = {0.33, 0.2};
+  const int force_tile = env_int("BSFP4_NVFP4_TILE"), force_splits = env_int("BSFP4_NVFP4_SPLITS");
   for (int c = 0; c < 2; c++) {
     const int bm = shapes[c][0], bn = shapes[c][1];
+    if (force_tile && force_tile != bm) continue;
     const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     for (int s = 1; s <= 8; s++) {
       if (s > 1 && stages / s < 8) break;  // keep at least 8 stages (1024 K values) per split
@@ -492,6 +591,7 @@ Plan plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
       }
     }
   }
+  if (force_splits > 0) best.splits = (int)std::max<int64_t>(1, std::min<int64_t>(force_splits, stages));
   return best;
 }
 
@@ -513,15 +613,17 @@ int device_cus() {
 // BSFP4_NVFP4_KERNEL selects an alternative for measurements: "lds4" (same
 // kernel, 4 waves of 128x128), "reg8" / "reg4" (per-wave register
 // dequantisation, 8 or 4 waves).
-static int nvfp4_variant() {
-  static const int v = [] {
-    const char* e = getenv("BSFP4_NVFP4_KERNEL");
-    if (!e) return 0;
-    if (!strcmp(e, "lds4")) return 1;
-    if (!strcmp(e, "reg8")) return 2;
-    if (!strcmp(e, "reg4")) return 3;
-    return 0;
-  }();
+// The dequantise-once kernel addresses operands with 32-bit buffer offsets
+// (M*K/2 and N*K/2 below 2^31); larger operands take the register-dequant
+// kernel.
+static int nvfp4_variant(int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_NVFP4_KERNEL");
+  int v = 0;
+  if (e && !strcmp(e, "lds4")) v = 1;
+  if (e && !strcmp(e, "reg8")) v = 2;
+  if (e && !strcmp(e, "reg4")) v = 3;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((v == 0 || v == 1) && (M * (K / 2) >= lim || N * (K / 2) >= lim)) v = 2;
   return v;
 }
 
@@ -537,7 +639,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
   const int tiles_n = (int)((N + pl.bn - 1) / pl.bn);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * pl.splits);
   if (pl.bm == 256) {
-    switch (nvfp4_variant()) {
+    switch (nvfp4_variant(M, N, K)) {
       case 1:
         nvfp4_gemm_f16lds<256, 256, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
                                                                     tiles_m, tiles_n, pl.splits, part);

@@ -139,3 +139,34 @@ def test_nvfp4_gemm_output_guard_band(M):
     h = buf.cpu().numpy()
     assert np.all(h[:4096] == 0x7E57) and np.all(h[4096 + M * N:] == 0x7E57)
     _check(host_bf16_bits(out), aq, sfa, bq, sfb, alpha)
+
+
+# The 256x256 kernels (dequantise-once and register-dequant forms) forced onto
+# ragged shapes: partial tiles in M and N, K not a multiple of the 64/128 stage,
+# odd numbers of K stages per split, and several split counts.
+FORCED = [
+    # (M, N, K, splits)
+    (65, 96, 160, 1), (300, 544, 1056, 1), (257, 288, 96, 1), (513, 768, 2048, 3),
+    (256, 256, 7168, 1), (300, 288, 1088, 2), (97, 1056, 4160, 5),
+]
+
+
+@pytest.mark.parametrize("variant", ["", "lds4", "reg8", "reg4"])
+@pytest.mark.parametrize("M,N,K,splits", FORCED)
+def test_nvfp4_gemm_forced_256_tiles(monkeypatch, variant, M, N, K, splits):
+    monkeypatch.setenv("BSFP4_NVFP4_TILE", "256")
+    monkeypatch.setenv("BSFP4_NVFP4_SPLITS", str(splits))
+    if variant:
+        monkeypatch.setenv("BSFP4_NVFP4_KERNEL", variant)
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=300 + M + splits)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(300, 544, 1056, 1), (513, 768, 2048, 3)])
+def test_nvfp4_gemm_forced_128_tiles(monkeypatch, M, N, K, splits):
+    monkeypatch.setenv("BSFP4_NVFP4_TILE", "128")
+    monkeypatch.setenv("BSFP4_NVFP4_SPLITS", str(splits))
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=400 + M)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
