@@ -285,8 +285,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 // group is loaded at the top of the current one, a full stage before its
 // first use.
 // LDS: two fp16 stages, rows of 64 values padded to 144 B, so 16 lanes reading
-// (or writing) the same 16-byte chunk of 16 consecutive rows hit distinct bank
-// groups and every fragment address is a per-lane base plus a constant.
+// the same 16-byte chunk of 16 consecutive rows hit distinct bank groups and
+// every fragment address is a per-lane base plus a constant; see f16_row for
+// the write side.
 // The MFMA takes the B fragment as its first operand, so each lane ends with
 // four consecutive output columns of one row: the epilogue scales by alpha,
 // rounds to bf16 and writes 8-byte vectors (FP32 16-byte vectors for split-K
@@ -295,6 +296,14 @@ constexpr int kF16StageK = 64;   // K values per fp16 LDS stage
 constexpr int kGroupK = 128;     // K values per load group
 constexpr int kF16Pitch = 144;   // LDS bytes per row of a stage (128 + 16 padding)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every operand: loads return 0
+
+// LDS byte offset of row R (A rows 0..BM-1, then B rows) in an fp16 stage.
+// 128-bit LDS writes are served 8 lanes (128 B, 32 banks) at a time: a quad
+// writes 16-byte units of rows R and R+128, and the next quad those of R+1 and
+// R+129.  Shifting every other 128-row block by 32 B puts the 8 units of such
+// a lane group in distinct 32-bank positions (the 144-byte pitch moves each
+// row by one unit).  Fragment reads stay inside one 128-row block.
+__device__ __forceinline__ int f16_row(int R) { return R * kF16Pitch + ((R + 128) >> 8) * 32; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -358,7 +367,7 @@ __device__ __forceinline__ void group_word_store(const Fp4Group<BM, BN, NT>& g, 
   const v2h s01 = e4m3x2_to_f16x2(scp);  // words 0,1 take scale 0; words 2,3 scale 1
   // row of load 2j (+NT/4 rows for load 2j+1); position of the chunk in the stage row
   const int r = ((tid + 2 * j * NT) >> 2) + (odd ? NT / 4 : 0);
-  *reinterpret_cast<v8h*>(lds + r * kF16Pitch + ((m & 1) * 4 + w) * 16) = dequant8(word, w < 2 ? s01.x : s01.y);
+  *reinterpret_cast<v8h*>(lds + f16_row(r) + ((m & 1) * 4 + w) * 16) = dequant8(word, w < 2 ? s01.x : s01.y);
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -423,7 +432,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int kStage = (BM + BN) * kF16Pitch;  // fp16 stage bytes (A rows then B rows)
+  constexpr int kStage = (BM + BN) * kF16Pitch + ((BM + BN) / 256) * 32;  // fp16 stage (A rows then B rows)
+  static_assert(BM % 256 == 0 && BN % 256 == 0, "row placement assumes 256-row blocks");
   static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
@@ -468,8 +478,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
     const int64_t kbase = (int64_t)sb * kF16StageK;
     const int64_t k_end = min(K, kbase + (int64_t)nst * kF16StageK);
     const int ngroups = (nst + 1) / 2;
-    const uint8_t* fra = smem + (wm * WM + lr) * kF16Pitch + g * 16;
-    const uint8_t* frb = smem + (BM + wn * WN + lr) * kF16Pitch + g * 16;
+    // 32-row fragment blocks never straddle a 128-row boundary
+    const uint8_t* fra = smem + f16_row(wm * WM + lr) + g * 16;
+    const uint8_t* frb = smem + f16_row(BM + wn * WN + lr) + g * 16;
 
     Fp4Group<BM, BN, NT> cur;
     fp4_group_load<BM, BN, NT>(cur, ra_q, ra_s, rb_q, rb_s, off, kbase, k_end);
