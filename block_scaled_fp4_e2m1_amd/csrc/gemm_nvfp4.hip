@@ -297,13 +297,17 @@ constexpr int kGroupK = 128;     // K values per load group
 constexpr int kF16Pitch = 144;   // LDS bytes per row of a stage (128 + 16 padding)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every operand: loads return 0
 
-// LDS byte offset of row R (A rows 0..BM-1, then B rows) in an fp16 stage.
-// 128-bit LDS writes are served 8 lanes (128 B, 32 banks) at a time: a quad
-// writes 16-byte units of rows R and R+128, and the next quad those of R+1 and
-// R+129.  Shifting every other 128-row block by 32 B puts the 8 units of such
-// a lane group in distinct 32-bank positions (the 144-byte pitch moves each
-// row by one unit).  Fragment reads stay inside one 128-row block.
-__device__ __forceinline__ int f16_row(int R) { return R * kF16Pitch + ((R + 128) >> 8) * 32; }
+// LDS byte offset of row R (A rows 0..BM-1, then B rows) in an fp16 stage of
+// a workgroup of NT threads.  128-bit LDS writes are served 8 lanes (128 B,
+// 32 banks) at a time: a quad writes 16-byte units of rows R and R + NT/4, the
+// next quad those of R+1 and R+1+NT/4.  Shifting alternate NT/4-row blocks by
+// 32 B puts the 8 units of such a lane group in distinct 32-bank positions
+// (the 144-byte pitch moves each row by one unit).  The shift boundaries are
+// multiples of 32 rows, so a 32-row fragment block never straddles one.
+template <int NT>
+__device__ __forceinline__ constexpr int f16_row(int R) {
+  return R * kF16Pitch + ((R + NT / 4) / (NT / 2)) * 32;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -367,14 +371,16 @@ __device__ __forceinline__ void group_word_store(const Fp4Group<BM, BN, NT>& g, 
   const v2h s01 = e4m3x2_to_f16x2(scp);  // words 0,1 take scale 0; words 2,3 scale 1
   // row of load 2j (+NT/4 rows for load 2j+1); position of the chunk in the stage row
   const int r = ((tid + 2 * j * NT) >> 2) + (odd ? NT / 4 : 0);
-  *reinterpret_cast<v8h*>(lds + f16_row(r) + ((m & 1) * 4 + w) * 16) = dequant8(word, w < 2 ? s01.x : s01.y);
+  *reinterpret_cast<v8h*>(lds + f16_row<NT>(r) + ((m & 1) * 4 + w) * 16) = dequant8(word, w < 2 ? s01.x : s01.y);
 }
 
+// qa / qb: the stage slot plus the lane's row and K-half offset; fragment i of
+// A is row block wm*WM + 32i, fragment j of B row block BM + wn*WN + 32j.
 template <int BM, int BN, int WGM, int WGN>
 __device__ __forceinline__ void f16_stage_compute(const uint8_t* qa, const uint8_t* qb,
                                                   v16f (&acc)[BM / WGM / 32][BN / WGN / 32],
                                                   const Fp4Group<BM, BN, 64 * WGM * WGN>& g, uint8_t* nx, int tid,
-                                                  bool store_h1) {
+                                                  bool store_h1, int wm, int wn) {
   // store_h1: dequantise this group's stage 1 (else the next group's stage 0,
   // which the caller passes as g)
   constexpr int NT = 64 * WGM * WGN;
@@ -390,9 +396,11 @@ __device__ __forceinline__ void f16_stage_compute(const uint8_t* qa, const uint8
   for (int kk = 0; kk < kF16StageK / 16; kk++) {
     v8h fa[TM], fb[TN];
 #pragma unroll
-    for (int j = 0; j < TN; j++) fb[j] = *reinterpret_cast<const v8h*>(qb + j * 32 * kF16Pitch + kk * 32);
+    for (int j = 0; j < TN; j++)
+      fb[j] = *reinterpret_cast<const v8h*>(qb + f16_row<NT>(BM + wn * (BN / WGN) + j * 32) + kk * 32);
 #pragma unroll
-    for (int i = 0; i < TM; i++) fa[i] = *reinterpret_cast<const v8h*>(qa + i * 32 * kF16Pitch + kk * 32);
+    for (int i = 0; i < TM; i++)
+      fa[i] = *reinterpret_cast<const v8h*>(qa + f16_row<NT>(wm * (BM / WGM) + i * 32) + kk * 32);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kMfma; t++) {
@@ -432,8 +440,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int kStage = (BM + BN) * kF16Pitch + ((BM + BN) / 256) * 32;  // fp16 stage (A rows then B rows)
-  static_assert(BM % 256 == 0 && BN % 256 == 0, "row placement assumes 256-row blocks");
+  constexpr int kStage = f16_row<NT>(BM + BN);  // fp16 stage bytes (A rows then B rows)
   static_assert(2 * kStage <= 160 * 1024, "two stages must fit in LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
 
@@ -478,9 +485,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
     const int64_t kbase = (int64_t)sb * kF16StageK;
     const int64_t k_end = min(K, kbase + (int64_t)nst * kF16StageK);
     const int ngroups = (nst + 1) / 2;
-    // 32-row fragment blocks never straddle a 128-row boundary
-    const uint8_t* fra = smem + f16_row(wm * WM + lr) + g * 16;
-    const uint8_t* frb = smem + f16_row(BM + wn * WN + lr) + g * 16;
+    // lane offset inside a 32-row fragment block (blocks never straddle a shift)
+    const uint8_t* fra = smem + lr * kF16Pitch + g * 16;
+    const uint8_t* frb = fra;
 
     Fp4Group<BM, BN, NT> cur;
     fp4_group_load<BM, BN, NT>(cur, ra_q, ra_s, rb_q, rb_s, off, kbase, k_end);
@@ -506,13 +513,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
       fp4_group_load<BM, BN, NT>(nxt, ra_q, ra_s, rb_q, rb_s, off, kbase + (int64_t)(gi + 1) * kGroupK, k_end);
       __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the group
       // stage 2gi (slot 0): dequantise stage 2gi+1 of this group into slot 1
-      f16_stage_compute<BM, BN, WGM, WGN>(fra, frb, acc, cur, smem + kStage, tid, true);
+      f16_stage_compute<BM, BN, WGM, WGN>(fra, frb, acc, cur, smem + kStage, tid, true, wm, wn);
       __syncthreads();
       // stage 2gi+1 (slot 1): dequantise stage 0 of the next group into slot 0.
       // With an odd stage count the last one reads zeros (its K range lies past
       // k_end, so its codes and scales were loaded as zero) and adds nothing;
       // the loop keeps a single exit, which keeps register allocation sane.
-      f16_stage_compute<BM, BN, WGM, WGN>(fra + kStage, frb + kStage, acc, nxt, smem, tid, false);
+      f16_stage_compute<BM, BN, WGM, WGN>(fra + kStage, frb + kStage, acc, nxt, smem, tid, false, wm, wn);
       __syncthreads();
       cur = nxt;
     }
@@ -567,42 +574,47 @@ struct Plan {
   int bm, bn, splits;
 };
 
-// Tile shape and K split for an M x N x K problem on `cus` compute units: the
-// estimated time is (rounds of work items) x (work per item) / (tile
-// efficiency) plus the FP32 partial traffic of a split.  Efficiencies are the
-// measured fractions of MFMA peak of the two tile shapes.
-// Test and measurement overrides, read on every call: BSFP4_NVFP4_TILE=256|128
-// forces the tile shape, BSFP4_NVFP4_SPLITS=n the number of K splits.
+// Tile shape and K split for an M x N x K problem on `cus` compute units.
+// Estimated time = (rounds of work items) x (flops per item) / (measured rate
+// of one workgroup of that tile shape) + the FP32 partial-sum traffic of a
+// split and its reduce kernel.  Rates (TFLOP/s per workgroup, dequantise-once
+// kernels on gfx950): 256x256 ~4.0, 256x128 ~3.0, 128x128 ~1.6 with two
+// workgroups per CU.
+// Test and measurement overrides, read on every call: BSFP4_NVFP4_TILE=256|128|
+// 256x128 forces the tile shape, BSFP4_NVFP4_SPLITS=n the number of K splits.
+const char* env_str(const char* name) { return getenv(name); }
 int env_int(const char* name) {
   const char* e = getenv(name);
   return e ? atoi(e) : 0;
 }
 
-Plan plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
-  const int64_t stages = (K + kStageK - 1) / kStageK;
+Plan plan_tiled(int64_t M, int64_t N, int64_t K, int cus, bool allow_256x128) {
+  const int64_t stages = (K + 63) / 64;
+  struct Cand { int bm, bn, per_cu; double rate; const char* name; };
+  const Cand cands[3] = {{256, 256, 1, 4.0e12, "256"}, {256, 128, 1, 3.0e12, "256x128"},
+                         {128, 128, 2, 1.6e12, "128"}};
+  const char* force_tile = env_str("BSFP4_NVFP4_TILE");
+  const int force_splits = env_int("BSFP4_NVFP4_SPLITS");
   Plan best{256, 256, 1};
   double best_t = 1e300;
-  const int shapes[2][2] = {{256, 256}, {128, 128}};
-  const double eff[2] = {0.33, 0.2};
-  const int force_tile = env_int("BSFP4_NVFP4_TILE"), force_splits = env_int("BSFP4_NVFP4_SPLITS");
-  for (int c = 0; c < 2; c++) {
-    const int bm = shapes[c][0], bn = shapes[c][1];
-    if (force_tile && force_tile != bm) continue;
-    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    for (int s = 1; s <= 8; s++) {
-      if (s > 1 && stages / s < 8) break;  // keep at least 8 stages (1024 K values) per split
-      const int64_t items = tiles * s;
-      const int64_t rounds = (items + cus - 1) / cus;
-      const double flops = 2.0 * bm * bn * (double)K / s;
-      double t = rounds * flops / (9.8e12 * eff[c]);
-      if (s > 1) t += (2.0 * s * M * N * 4) / 4.0e12 + 3e-6;
+  for (const Cand& c : cands) {
+    if (force_tile && strcmp(force_tile, c.name)) continue;
+    if (c.bm != c.bn && !allow_256x128) continue;
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    for (int sp = 1; sp <= 8; sp++) {
+      if (sp > 1 && stages / sp < 4) break;  // keep at least 4 stages (256 K values) per split
+      if (force_splits > 0 && sp != std::min<int64_t>(force_splits, stages)) continue;
+      const int64_t items = tiles * sp;
+      const int64_t slots = (int64_t)cus * c.per_cu;
+      const int64_t rounds = (items + slots - 1) / slots;
+      double t = rounds * (2.0 * c.bm * c.bn * (double)K / sp) / c.rate;
+      if (sp > 1) t += (2.0 * sp * M * N * 4 + 2.0 * M * N) / 4.0e12 + 3e-6;
       if (t < best_t * 0.999) {
         best_t = t;
-        best = Plan{bm, bn, s};
+        best = Plan{c.bm, c.bn, sp};
       }
     }
   }
-  if (force_splits > 0) best.splits = (int)std::max<int64_t>(1, std::min<int64_t>(force_splits, stages));
   return best;
 }
 
@@ -643,34 +655,30 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (M <= kSkinnyMaxM) return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, stream);
-  Plan pl = plan_tiled(M, N, K, device_cus());
+  const int v = nvfp4_variant(M, N, K);
+  Plan pl = plan_tiled(M, N, K, device_cus(), v < 2);
   if (pl.splits > 1 && ws_bytes < (size_t)pl.splits * M * N * sizeof(float)) pl.splits = 1;
   float* part = static_cast<float*>(ws);
   const int tiles_m = (int)((M + pl.bm - 1) / pl.bm);
   const int tiles_n = (int)((N + pl.bn - 1) / pl.bn);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * pl.splits);
-  if (pl.bm == 256) {
-    switch (nvfp4_variant(M, N, K)) {
-      case 1:
-        nvfp4_gemm_f16lds<256, 256, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                                    tiles_m, tiles_n, pl.splits, part);
-        break;
-      case 2:
-        nvfp4_gemm_tiled<256, 256, 2, 4><<<grid, 512, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                                   tiles_n, pl.splits, part);
-        break;
-      case 3:
-        nvfp4_gemm_tiled<256, 256, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                                   tiles_n, pl.splits, part);
-        break;
-      default:
-        nvfp4_gemm_f16lds<256, 256, 2, 4><<<grid, 512, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                                    tiles_m, tiles_n, pl.splits, part);
+#define BSFP4_ARGS A, SFA, B, SFB, alpha, D, (int)M, (int)N, K
+  if (pl.bm == 256 && pl.bn == 256) {
+    switch (v) {
+      case 1: nvfp4_gemm_f16lds<256, 256, 2, 2><<<grid, 256, 0, stream>>>(BSFP4_ARGS, tiles_m, tiles_n, pl.splits, part); break;
+      case 2: nvfp4_gemm_tiled<256, 256, 2, 4><<<grid, 512, 0, stream>>>(BSFP4_ARGS, tiles_n, pl.splits, part); break;
+      case 3: nvfp4_gemm_tiled<256, 256, 2, 2><<<grid, 256, 0, stream>>>(BSFP4_ARGS, tiles_n, pl.splits, part); break;
+      default: nvfp4_gemm_f16lds<256, 256, 2, 4><<<grid, 512, 0, stream>>>(BSFP4_ARGS, tiles_m, tiles_n, pl.splits, part);
     }
+  } else if (pl.bm == 256) {  // 256x128 (planned only for the dequantise-once kernels)
+    nvfp4_gemm_f16lds<256, 128, 2, 2><<<grid, 256, 0, stream>>>(BSFP4_ARGS, tiles_m, tiles_n, pl.splits, part);
   } else {
-    nvfp4_gemm_tiled<128, 128, 2, 2><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, K,
-                                                               tiles_n, pl.splits, part);
+    if (v >= 2)
+      nvfp4_gemm_tiled<128, 128, 2, 2><<<grid, 256, 0, stream>>>(BSFP4_ARGS, tiles_n, pl.splits, part);
+    else
+      nvfp4_gemm_f16lds<128, 128, 2, 2><<<grid, 256, 0, stream>>>(BSFP4_ARGS, tiles_m, tiles_n, pl.splits, part);
   }
+#undef BSFP4_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t q = M * N / 4;
@@ -681,7 +689,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
 
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
   if (M <= kSkinnyMaxM) return 0;
-  const Plan pl = plan_tiled(M, N, K, device_cus());
+  const Plan pl = plan_tiled(M, N, K, device_cus(), nvfp4_variant(M, N, K) < 2);
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }
 

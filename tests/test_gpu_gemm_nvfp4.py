@@ -163,9 +163,16 @@ def test_nvfp4_gemm_forced_256_tiles(monkeypatch, variant, M, N, K, splits):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
-@pytest.mark.parametrize("M,N,K,splits", [(300, 544, 1056, 1), (513, 768, 2048, 3)])
-def test_nvfp4_gemm_forced_128_tiles(monkeypatch, M, N, K, splits):
-    monkeypatch.setenv("BSFP4_NVFP4_TILE", "128")
+@pytest.mark.parametrize("tile", ["128", "256x128"])
+@pytest.mark.parametrize("variant", ["", "reg8"])
+@pytest.mark.parametrize("M,N,K,splits", [(300, 544, 1056, 1), (513, 768, 2048, 3), (97, 1056, 4160, 5),
+                                          (257, 288, 96, 1), (129, 160, 3072, 2)])
+def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, splits):
+    if variant and tile == "256x128":
+        pytest.skip("the register-dequant kernels have no 256x128 tile")
+    monkeypatch.setenv("BSFP4_NVFP4_TILE", tile)
+    if variant:
+        monkeypatch.setenv("BSFP4_NVFP4_KERNEL", variant)
     monkeypatch.setenv("BSFP4_NVFP4_SPLITS", str(splits))
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=400 + M)
     got = _run(aq, sfa, bq, sfb, alpha)
