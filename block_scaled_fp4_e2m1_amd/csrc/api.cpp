@@ -194,17 +194,22 @@ bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8
 // ------------------------------------------------------------------ W4A16
 
 size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  // rows run in chunks of at most kSkinnyMaxM; the partials of one chunk are
+  // reduced before the next chunk starts on the same stream
+  const int64_t mc = M < bsfp4::kSkinnyMaxM ? M : bsfp4::kSkinnyMaxM;
+  size_t need = bsfp4::skinny_workspace(mc, N, K, false);
+  const int64_t tail = M % bsfp4::kSkinnyMaxM;
+  if (M > bsfp4::kSkinnyMaxM && tail > 0) {
+    const size_t t = bsfp4::skinny_workspace(tail, N, K, false);
+    if (t > need) need = t;
+  }
+  return need;
 }
 
 bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                         uint16_t* D, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
                         void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (M < 0 || N <= 0 || K <= 0)
     return fail(BSFP4_ERR_SHAPE, "need M >= 0, N > 0, K > 0 (M=%lld N=%lld K=%lld)", (long long)M,
                 (long long)N, (long long)K);
@@ -219,12 +224,19 @@ bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
   REQUIRE_PTR(B);
   REQUIRE_PTR(SFB);
   if (alpha != nullptr && !aligned(alpha, 4)) return fail(BSFP4_ERR_ALIGNMENT, "alpha is not 4-byte aligned");
+  const size_t need = w4a16_gemm_workspace_size(M, N, K);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+  }
   if (M == 0) return ok();
   if (bsfp4_status s = check_device()) return s;
   // rows in chunks of kSkinnyMaxM (the weight stream is re-read once per chunk)
   for (int64_t m0 = 0; m0 < M; m0 += bsfp4::kSkinnyMaxM) {
     const int64_t mc = (M - m0 < bsfp4::kSkinnyMaxM) ? (M - m0) : bsfp4::kSkinnyMaxM;
-    hipError_t e = bsfp4::launch_skinny_w4a16(A + m0 * K, B, SFB, alpha, D + m0 * N, mc, N, K, as_stream(stream));
+    hipError_t e = bsfp4::launch_skinny_w4a16(A + m0 * K, B, SFB, alpha, D + m0 * N, mc, N, K,
+                                              static_cast<float*>(ws), as_stream(stream));
     if (e != hipSuccess) return launched(e, "w4a16_gemm launch");
   }
   return ok();

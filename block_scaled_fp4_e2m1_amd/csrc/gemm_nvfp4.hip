@@ -654,7 +654,8 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (M <= kSkinnyMaxM) return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+  if (M <= kSkinnyMaxM)
+    return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), stream);
   const int v = nvfp4_variant(M, N, K);
   Plan pl = plan_tiled(M, N, K, device_cus(), v < 2);
   if (pl.splits > 1 && ws_bytes < (size_t)pl.splits * M * N * sizeof(float)) pl.splits = 1;
@@ -687,8 +688,16 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
   return hipGetLastError();
 }
 
+hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,
+                                hipStream_t stream) {
+  const int64_t q = MN / 4;
+  const unsigned rgrid = (unsigned)((q + 255) / 256 > 16384 ? 16384 : (q + 255) / 256);
+  splitk_reduce<<<rgrid < 1 ? 1 : rgrid, 256, 0, stream>>>(part, splits, alpha, D, MN);
+  return hipGetLastError();
+}
+
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
-  if (M <= kSkinnyMaxM) return 0;
+  if (M <= kSkinnyMaxM) return skinny_workspace(M, N, K, true);
   const Plan pl = plan_tiled(M, N, K, device_cus(), nvfp4_variant(M, N, K) < 2);
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
 }

@@ -26,6 +26,8 @@
 //
 // Exactness: E2M1 x E4M3 products are exact in fp16 (W4A4: both operands) and
 // in bf16 (W4A16 weights: at most 6 significant bits, range [2^-10, 2688]).
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -197,6 +199,309 @@ __global__ void __launch_bounds__(512)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K form for M <= 32 (one or two 16-row M tiles).  Work item = 64 output
+// columns x a K range of KR = 128*NL values; the ranges of one column block are
+// summed afterwards by splitk_reduce in range order (deterministic).
+//   * every lane issues all of its weight loads for the range at once (NL
+//     128-bit code loads and NL 2-byte scale loads, buffer loads that read zero
+//     past K), four lanes covering 64 contiguous bytes of a weight row;
+//   * meanwhile the workgroup writes the activations of the range into LDS as
+//     fp16 (NVFP4 activations, dequantised once per workgroup) or bf16, so the
+//     MFMA loop reads them with one ds_read_b128 per step;
+//   * wave w owns output columns 16w..16w+15 of the block; lane (c, g) feeds
+//     weight row c and the K values 128j + 32g + 8s (step s of load j) to
+//     v_mfma_f32_16x16x32 as its A operand, the activations of the same K values
+//     as B operand, so the lane ends with four consecutive columns of one row.
+constexpr int kSkinnyCols = 64;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t skinny_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int AKIND, int MT, int NL>
+__global__ void __launch_bounds__(256)
+    skinny_split(const void* __restrict__ Aptr, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
+                 const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
+                 int M, int N, int K, int ksplit, float* __restrict__ part) {
+  constexpr int KR = 128 * NL;
+  constexpr int kPitch = 2 * KR + 16;  // LDS bytes per activation row (odd number of 16-byte units)
+  __shared__ __attribute__((aligned(16))) uint8_t act[MT * 16 * kPitch];
+  constexpr uint32_t kOOB = 0x80000000u;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cb = blockIdx.x / ksplit, split = blockIdx.x % ksplit;
+  const int n0 = cb * kSkinnyCols;
+  const int k_lo = split * KR;
+  const int k_hi = min(K, k_lo + KR);
+  const int c = lane & 15, g = lane >> 4;
+
+  // ---- activation loads first (few, L2-resident): the per-wave memory queue
+  // returns in order, so loads issued after the weight stream would wait for it
+  constexpr int kItems = MT * 16 * (KR / 32);  // (row, 32-value chunk) items
+  constexpr int kPer = (kItems + 255) / 256;
+  uint4 aq[kPer][AKIND == 0 ? 1 : 4];
+  uint32_t as2[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; u++) {
+    const int it = tid + 256 * u;
+    const int row = it / (KR / 32), ch = it % (KR / 32);
+    const int k = k_lo + 32 * ch;
+    const bool ok = it < kItems && row < M && k < k_hi;
+    as2[u] = 0;
+    if constexpr (AKIND == 0) {
+      const uint8_t* A = static_cast<const uint8_t*>(Aptr);
+      aq[u][0] = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        aq[u][0] = *reinterpret_cast<const uint4*>(A + (int64_t)row * (K / 2) + k / 2);
+        as2[u] = *reinterpret_cast<const uint16_t*>(SFA + (int64_t)row * (K / 16) + k / 16);
+      }
+    } else {
+      const uint16_t* A = static_cast<const uint16_t*>(Aptr);
+#pragma unroll
+      for (int h = 0; h < 4; h++)
+        aq[u][h] = ok ? *reinterpret_cast<const uint4*>(A + (int64_t)row * K + k + 8 * h) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // ---- weight loads for the whole range (in flight while A is staged)
+  const int n = n0 + 16 * wave + c;
+  const __amdgpu_buffer_rsrc_t rq = skinny_rsrc(B, (int64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = skinny_rsrc(SFB, (int64_t)N * (K / 16));
+  uint4 code[NL];
+  uint32_t sc[NL];
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    const int k = k_lo + 128 * j + 32 * g;
+    const bool ok = n < N && k < k_hi;
+    const uint32_t oc = ok ? (uint32_t)((int64_t)n * (K / 2) + k / 2) : kOOB;
+    const uint32_t os = ok ? (uint32_t)((int64_t)n * (K / 16) + k / 16) : kOOB;
+    code[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)oc, 0, 0));
+    sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)os, 0, 0);
+  }
+
+  // ---- activations of the range -> LDS (rows >= M and K >= k_hi as zeros)
+#pragma unroll
+  for (int u = 0; u < kPer; u++) {
+    const int it = tid + 256 * u;
+    if (it >= kItems) break;
+    const int row = it / (KR / 32), ch = it % (KR / 32);
+    uint8_t* dst = act + row * kPitch + ch * 64;
+    if constexpr (AKIND == 0) {
+      const _Float16 s0 = e4m3_to_f16(as2[u] & 0xFFu), s1 = e4m3_to_f16(as2[u] >> 8);
+      *reinterpret_cast<v8h*>(dst) = dq8_f16(aq[u][0].x, s0);
+      *reinterpret_cast<v8h*>(dst + 16) = dq8_f16(aq[u][0].y, s0);
+      *reinterpret_cast<v8h*>(dst + 32) = dq8_f16(aq[u][0].z, s1);
+      *reinterpret_cast<v8h*>(dst + 48) = dq8_f16(aq[u][0].w, s1);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; h++) *reinterpret_cast<uint4*>(dst + 16 * h) = aq[u][h];
+    }
+  }
+  __syncthreads();
+
+  // ---- MFMA loop: load j, step s covers K values 128j + 32g + 8s .. +8 of the range
+  v4f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; t++) acc[t] = v4f{};
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const uint32_t word = s == 0 ? code[j].x : s == 1 ? code[j].y : s == 2 ? code[j].z : code[j].w;
+      const uint32_t sbyte = (sc[j] >> (8 * (s >> 1))) & 0xFFu;
+      const int koff = 2 * (128 * j + 32 * g + 8 * s);
+      if constexpr (AKIND == 0) {
+        const v8h fb = dq8_f16(word, e4m3_to_f16(sbyte));
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+          const v8h fa = *reinterpret_cast<const v8h*>(act + (t * 16 + c) * kPitch + koff);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb, fa, acc[t], 0, 0, 0);
+        }
+      } else {
+        const v8bf fb = dq8_bf16(word, e4m3_to_f32(sbyte));
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+          const v8bf fa = *reinterpret_cast<const v8bf*>(act + (t * 16 + c) * kPitch + koff);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- lane holds D[m = 16t + c][n0 + 16*wave + 4g + r], r = 0..3
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  const int ncol = n0 + 16 * wave + 4 * g;
+#pragma unroll
+  for (int t = 0; t < MT; t++) {
+    const int m = t * 16 + c;
+    if (m >= M || ncol >= N) continue;
+    if (ksplit == 1) {
+      *reinterpret_cast<uint2*>(D + (int64_t)m * N + ncol) =
+          make_uint2(pack_bf16x2(alpha * acc[t][0], alpha * acc[t][1]), pack_bf16x2(alpha * acc[t][2], alpha * acc[t][3]));
+    } else {
+      *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + ncol) =
+          make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single-pass form for NVFP4 activations with M <= 16: one workgroup per 16
+// output columns, its waves splitting K into ranges of 128*NL values.  Every
+// lane loads both its weight row's codes/scales and the matching activation
+// codes/scales for its whole range at once (the activations are L2-resident:
+// every workgroup reads the same few rows), dequantises both operands in
+// registers, and the waves' partial tiles are summed in LDS in wave order.  No
+// second kernel and no workspace: for these sizes a split-K reduce launch
+// costs more than the repeated activation dequantisation.
+template <int NL>
+__global__ void __launch_bounds__(512)
+    skinny_onepass(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
+                   const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
+                   int M, int N, int K) {
+  constexpr int KR = 128 * NL;
+  constexpr uint32_t kOOB = 0x80000000u;
+  __shared__ float red[8][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int c = lane & 15, g = lane >> 4;
+  const int k_lo = wave * KR;
+  const int n = n0 + c;
+  const __amdgpu_buffer_rsrc_t rbq = skinny_rsrc(B, (int64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rbs = skinny_rsrc(SFB, (int64_t)N * (K / 16));
+  const __amdgpu_buffer_rsrc_t raq = skinny_rsrc(A, (int64_t)M * (K / 2));
+  const __amdgpu_buffer_rsrc_t ras = skinny_rsrc(SFA, (int64_t)M * (K / 16));
+  uint4 ac[NL], bc[NL];
+  uint32_t as[NL], bsc[NL];
+  // activations first: the per-wave memory queue returns in order
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    const int k = k_lo + 128 * j + 32 * g;
+    const bool ok = c < M && k < K;
+    const uint32_t oc = ok ? (uint32_t)(c * (K / 2) + k / 2) : kOOB;
+    const uint32_t os = ok ? (uint32_t)(c * (K / 16) + k / 16) : kOOB;
+    ac[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(raq, (int)oc, 0, 0));
+    as[j] = __builtin_amdgcn_raw_buffer_load_b16(ras, (int)os, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+    const int k = k_lo + 128 * j + 32 * g;
+    const bool ok = n < N && k < K;
+    const uint32_t oc = ok ? (uint32_t)((int64_t)n * (K / 2) + k / 2) : kOOB;
+    const uint32_t os = ok ? (uint32_t)((int64_t)n * (K / 16) + k / 16) : kOOB;
+    bc[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbq, (int)oc, 0, 0));
+    bsc[j] = __builtin_amdgcn_raw_buffer_load_b16(rbs, (int)os, 0, 0);
+  }
+  v4f acc = v4f{};
+#pragma unroll
+  for (int j = 0; j < NL; j++) {
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const uint32_t wb = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+      const uint32_t wa = s == 0 ? ac[j].x : s == 1 ? ac[j].y : s == 2 ? ac[j].z : ac[j].w;
+      const v8h fb = dq8_f16(wb, e4m3_to_f16((bsc[j] >> (8 * (s >> 1))) & 0xFFu));
+      const v8h fa = dq8_f16(wa, e4m3_to_f16((as[j] >> (8 * (s >> 1))) & 0xFFu));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb, fa, acc, 0, 0, 0);
+    }
+  }
+  // acc[r] = partial D[m = c][n0 + 4g + r] of this wave's K range
+#pragma unroll
+  for (int r = 0; r < 4; r++) red[wave][4 * g + r][c] = acc[r];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * 8; idx += blockDim.x) {  // (row, column pair); a single wave loops
+    const int m = idx >> 3, np = (idx & 7) * 2;
+    if (m < M) {
+      float s0 = 0.0f, s1 = 0.0f;
+      for (int w = 0; w < nwaves; w++) {
+        s0 += red[w][np][m];
+        s1 += red[w][np + 1][m];
+      }
+      const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+      *reinterpret_cast<uint32_t*>(D + (int64_t)m * N + n0 + np) = pack_bf16x2(alpha * s0, alpha * s1);
+    }
+  }
+}
+
+// NL for the single-pass form (<= 8 waves of 128*NL values), 0 if K is too long.
+int onepass_nl(int64_t K) {
+  const int64_t kb = (K + 127) / 128;
+  const int opts[6] = {1, 2, 4, 7, 8, 14};
+  for (int o : opts)
+    if ((kb + o - 1) / o <= 8) return o;
+  return 0;
+}
+
+// Loads per lane per work item and the split count for an M <= 32 problem:
+// about two work items per CU, at most 16 loads (2048 K values) per lane.
+struct SkinnyPlan {
+  int nl, ksplit;
+};
+int env_skinny_per_cu() {
+  const char* e = getenv("BSFP4_SKINNY_PER_CU");
+  return e ? atoi(e) : 1;
+}
+SkinnyPlan skinny_plan(int64_t N, int64_t K, int cus, int mt) {
+  const int64_t blocks = (N + kSkinnyCols - 1) / kSkinnyCols;
+  const int64_t kb = (K + 127) / 128;  // 128-value blocks
+  const int per_cu = env_skinny_per_cu();
+  int64_t ks = (per_cu * cus + blocks - 1) / blocks;
+  if (ks < 1) ks = 1;
+  if (ks > kb) ks = kb;
+  int64_t nl = (kb + ks - 1) / ks;
+  // the activation tile (16*mt rows x 128*nl values, 2 bytes each) must fit in LDS
+  const int max_nl = mt >= 4 ? 8 : 16;
+  const int opts[5] = {2, 4, 8, 14, 16};
+  int pick = max_nl;
+  for (int o : opts)
+    if (o >= nl && o <= max_nl) { pick = o; break; }
+  const int64_t ksplit = (kb + pick - 1) / pick;
+  return SkinnyPlan{pick, (int)ksplit};
+}
+
+int skinny_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    n = (hipGetDevice(&dev) == hipSuccess &&
+         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ? v
+            : 256;
+  }
+  return n;
+}
+
+template <int AKIND, int MT, int NL>
+hipError_t launch_split_nl(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                           const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, int ksplit,
+                           float* part, hipStream_t stream) {
+  const unsigned grid = (unsigned)(((N + kSkinnyCols - 1) / kSkinnyCols) * ksplit);
+  skinny_split<AKIND, MT, NL><<<grid, 256, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, ksplit,
+                                                        part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ksplit == 1) return e;
+  return launch_splitk_reduce(part, ksplit, alpha, D, M * N, stream);
+}
+
+template <int AKIND, int MT>
+hipError_t launch_split(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                        const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
+                        hipStream_t stream) {
+  const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), MT);
+  switch (pl.nl) {
+    case 2: return launch_split_nl<AKIND, MT, 2>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
+    case 4: return launch_split_nl<AKIND, MT, 4>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
+    case 8: return launch_split_nl<AKIND, MT, 8>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
+    default:
+      if constexpr (MT < 4) {
+        if (pl.nl == 14)
+          return launch_split_nl<AKIND, MT, 14>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
+        return launch_split_nl<AKIND, MT, 16>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
+      }
+      return hipErrorInvalidValue;  // not planned: nl <= 8 for four M tiles
+  }
+}
+
 template <int AKIND, int MT>
 hipError_t launch_mt(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                      const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -210,9 +515,55 @@ hipError_t launch_mt(const void* A, const uint8_t* SFA, const uint8_t* B, const 
   return hipGetLastError();
 }
 
+template <int NL>
+hipError_t launch_onepass_nl(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                             const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int waves = (int)(((K + 127) / 128 + NL - 1) / NL);
+  skinny_onepass<NL><<<(unsigned)(N / 16), 64 * waves, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N,
+                                                                     (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_onepass(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                          const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  switch (onepass_nl(K)) {
+    case 1: return launch_onepass_nl<1>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    case 2: return launch_onepass_nl<2>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    case 4: return launch_onepass_nl<4>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    case 7: return launch_onepass_nl<7>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    case 8: return launch_onepass_nl<8>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    default: return launch_onepass_nl<14>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+  }
+}
+
+// The single-pass NVFP4 form applies for M <= 16 when K fits 8 waves and the
+// buffer offsets fit 31 bits.
+bool use_onepass(int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_SKINNY_SPLIT");  // measurement override: force the split-K form
+  if (e && e[0] == '1') return false;
+  return M <= 16 && onepass_nl(K) > 0 && N * (K / 2) < ((int64_t)1 << 31);
+}
+
+// Rows 33..64: the split form with four M tiles for bf16 activations (the
+// single-tile kernel would load them just in time); NVFP4 activations keep the
+// per-wave kernel unless BSFP4_SKINNY_MT4=1.
+bool split_mt4(int akind) {
+  const char* e = getenv("BSFP4_SKINNY_MT4");
+  if (e) return e[0] == '1';
+  return akind == 1;
+}
+
 template <int AKIND>
 hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
-                       const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
+                       hipStream_t stream) {
+  if (AKIND == 0 && use_onepass(M, N, K))
+    return launch_onepass(static_cast<const uint8_t*>(A), SFA, B, SFB, alpha, D, M, N, K, stream);
+  const bool offsets32 = N * (K / 2) < ((int64_t)1 << 31);  // buffer offsets of the split kernels
+  if (offsets32 && M <= 16) return launch_split<AKIND, 1>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
+  if (offsets32 && M <= 32) return launch_split<AKIND, 2>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
+  if (offsets32 && split_mt4(AKIND))
+    return launch_split<AKIND, 4>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
   if (M <= 16) return launch_mt<AKIND, 1>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
   if (M <= 32) return launch_mt<AKIND, 2>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
   return launch_mt<AKIND, 4>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
@@ -221,14 +572,22 @@ hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, cons
 }  // namespace
 
 hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
-                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                                hipStream_t stream) {
-  return launch_kind<0>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+  return launch_kind<0>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
 }
 
 hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
-                               uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  return launch_kind<1>(A, nullptr, B, SFB, alpha, D, M, N, K, stream);
+                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, hipStream_t stream) {
+  return launch_kind<1>(A, nullptr, B, SFB, alpha, D, M, N, K, part, stream);
+}
+
+size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
+  if (M <= 0 || M > 64 || N * (K / 2) >= ((int64_t)1 << 31)) return 0;
+  if (fp4_activations && use_onepass(M, N, K)) return 0;
+  if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;
+  const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), M <= 16 ? 1 : M <= 32 ? 2 : 4);
+  return pl.ksplit > 1 ? (size_t)pl.ksplit * M * N * sizeof(float) : 0;
 }
 
 }  // namespace bsfp4

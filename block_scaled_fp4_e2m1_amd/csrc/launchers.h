@@ -25,13 +25,21 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              void* ws, size_t ws_bytes, hipStream_t stream);
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 
-// Small-M (M <= 64) split-K kernels with NVFP4 weights.
+// Small-M (M <= 64) kernels with NVFP4 weights.  Some forms split K over work
+// items and need `part` = skinny_workspace(M, N, K, activations are NVFP4)
+// bytes of FP32 partials (nullptr when that is 0).
 constexpr int64_t kSkinnyMaxM = 64;
 hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
-                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                                hipStream_t stream);
 hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
-                               uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, hipStream_t stream);
+size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations);
+
+// D = bf16(alpha * sum_s part[s]) over `splits` FP32 partials of MN elements
+// (MN % 4 == 0), summed in split order.
+hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,
+                                hipStream_t stream);
 
 // MXFP4 scaled-MFMA GEMMs (dense and grouped by expert).
 constexpr int kEpiStore = 0;    // bf16 rows

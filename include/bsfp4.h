@@ -146,7 +146,9 @@ BSFP4_API bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, c
  *   alpha     device float[1]; NULL means 1.0
  *   D         device bf16 [M, N]
  *   sizes     M >= 0, N % 32 == 0, K % 32 == 0
- *   ws        device workspace of w4a16_gemm_workspace_size(...) bytes
+ *   ws        device workspace of w4a16_gemm_workspace_size(...) bytes (may
+ *             be NULL when that size is 0); its contents need no
+ *             initialisation
  * ------------------------------------------------------------------------- */
 BSFP4_API size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 BSFP4_API bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,

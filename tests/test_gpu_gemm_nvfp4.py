@@ -177,3 +177,24 @@ def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, spli
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=400 + M)
     got = _run(aq, sfa, bq, sfb, alpha)
     _check(got, aq, sfa, bq, sfb, alpha)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (3, 96, 4000 - 4000 % 32), (16, 4096, 7168), (9, 1056, 16384),
+                                   (16, 288, 32), (5, 160, 1088)])
+@pytest.mark.parametrize("form", ["onepass", "split"])
+def test_nvfp4_gemm_small_m_forms(monkeypatch, form, M, N, K):
+    """Both small-M forms (single pass, split-K + reduce) on ragged shapes."""
+    if form == "split":
+        monkeypatch.setenv("BSFP4_SKINNY_SPLIT", "1")
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=500 + M + K)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
+@pytest.mark.parametrize("mt4", ["1", "0"])
+def test_nvfp4_gemm_rows_33_to_64(monkeypatch, mt4, M, N, K):
+    monkeypatch.setenv("BSFP4_SKINNY_MT4", mt4)
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=600 + M)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)

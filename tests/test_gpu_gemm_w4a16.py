@@ -58,3 +58,17 @@ def test_w4a16_every_scale_code_no_alpha():
     wq = synth.random_bytes(2, (N, K // 2))
     wsf = synth.random_e4m3_scales(3, (N, K // 16), 0x00, 0x7F)
     _run_check(a, wq, wsf, None)
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
+@pytest.mark.parametrize("mt4", ["1", "0"])
+def test_w4a16_rows_33_to_64(monkeypatch, mt4, M, N, K):
+    """Rows 33..64 through both kernels (split form with four M tiles, per-wave form)."""
+    monkeypatch.setenv("BSFP4_SKINNY_MT4", mt4)
+    _run_check(*_problem(M, N, K, 700 + M))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (16, 288, 4160), (29, 1056, 16384)])
+def test_w4a16_split_forms(M, N, K):
+    """Split-K form (one or two M tiles) incl. K longer than 16 loads per lane."""
+    _run_check(*_problem(M, N, K, 800 + M))
