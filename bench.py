@@ -78,11 +78,44 @@ class Timer:
         self.torch = torch
         self.flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
 
+    def graph(self, fn, calls=20, reps=5):
+        """`calls` back-to-back calls captured in one HIP graph and replayed
+        `reps` times between two events: the GPU time per call without the
+        host's per-launch cost (which exceeds a few-microsecond kernel).  The
+        replayed result is checked against the eager result of the same call
+        by the caller through `check`."""
+        t = self.torch
+        side = t.cuda.Stream()
+        side.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        t.cuda.current_stream().wait_stream(side)
+        t.cuda.synchronize()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        t.cuda.synchronize()
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+        del g
+        return {"median_us": us, "graph_replay": True, "calls_per_graph": calls}
+
     def run(self, fn, iters=20, warmup=3, cold=False):
         """cold: each call timed alone after a 512 MiB fill that evicts L2 and the
-        256 MB MALL (median/p10/p90 of per-call event times).  warm: `iters` calls
-        back to back between two events (their mean), as a pipeline would issue
-        them -- per-call event pairs would add the event overhead to each call."""
+        256 MB MALL (median/p10/p90 of per-call event times; the fill keeps the
+        GPU busy while the host enqueues the call).  warm: `iters` calls back to
+        back between two events (their mean), as a pipeline would issue them --
+        for kernels of a few microseconds this is bounded by the host's launch
+        cost; `graph` gives the GPU time."""
         t = self.torch
         for _ in range(warmup):
             fn()
@@ -258,9 +291,13 @@ def run_rows(torch, bs, synth, timer, only):
         _, _, aq, sfa, bq, sfb, alpha = nv_inputs(M, N, K, 100, 101)
         D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         fn = lambda: bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
+        fn()
+        eager = D.clone()
         rows["nvfp4_gemm_16x4096x7168"] = {
             "cold": _rate(timer.run(fn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
             "warm": _rate(timer.run(fn), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+            "graph": _rate(timer.graph(fn), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+            "graph_matches_eager": bool(torch.equal(D, eager)),
             "bound": "hbm", "algorithmic_bytes": _nv_bytes(M, N, K)}
 
     # a3 sweep at N=4096, K=7168
@@ -271,8 +308,9 @@ def run_rows(torch, bs, synth, timer, only):
             _, _, aq, sfa, bq, sfb, alpha = nv_inputs(M, N, K, 122 + i, 121)
             D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             fn = lambda: bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
-            sweep[f"M={M}"] = _rate(timer.run(fn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K))
-        rows["nvfp4_gemm_sweep_cold"] = sweep
+            sweep[f"M={M}"] = {"cold": _rate(timer.run(fn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
+                               "graph": _rate(timer.graph(fn), 2.0 * M * N * K, _nv_bytes(M, N, K))}
+        rows["nvfp4_gemm_sweep"] = sweep
 
     # a1 + a3: quantise bf16 activations, then the NVFP4 GEMM (M=256, N=14336, K=4096)
     if want("quant_then_gemm_256x14336x4096"):
@@ -292,7 +330,8 @@ def run_rows(torch, bs, synth, timer, only):
             "quant_cold": _rate(timer.run(qfn, cold=True), None, qbytes),
             "gemm_cold": _rate(timer.run(gfn, cold=True), 2.0 * M * N * K, _nv_bytes(M, N, K)),
             "pipeline_cold": _rate(timer.run(both, cold=True), 2.0 * M * N * K),
-            "pipeline_warm": _rate(timer.run(both), 2.0 * M * N * K)}
+            "pipeline_warm": _rate(timer.run(both), 2.0 * M * N * K),
+            "pipeline_graph": _rate(timer.graph(both), 2.0 * M * N * K)}
 
     # a5: W4A16 at M=64 and M=1, N=4096, K=7168 (HBM roofline)
     if want("w4a16_4096x7168"):
@@ -309,6 +348,7 @@ def run_rows(torch, bs, synth, timer, only):
             nbytes = 2 * M * K + N * K // 2 + N * K // 16 + 4 + 2 * M * N
             res[f"M={M}"] = {"cold": _rate(timer.run(fn, cold=True), 2.0 * M * N * K, nbytes),
                              "warm": _rate(timer.run(fn), 2.0 * M * N * K, nbytes),
+                             "graph": _rate(timer.graph(fn), 2.0 * M * N * K, nbytes),
                              "algorithmic_bytes": nbytes}
         rows["w4a16_4096x7168"] = res
 

@@ -32,6 +32,8 @@
 //            index f; a second kernel sums each token's top-k rows in slot order
 //            and rounds once to bf16 (deterministic; the same layer with device-wide
 //            float atomics for the combine measured about 2x slower).
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "quant_device.h"
@@ -39,7 +41,6 @@
 namespace bsfp4 {
 namespace {
 
-constexpr int kThreads = 256;
 
 // Stage geometry for SK K-values per stage: SK/2 code bytes (SK/32 chunks of 16
 // bytes) and SK/32 E8M0 bytes per row.
@@ -56,24 +57,24 @@ struct Geo {
   }
 };
 
-template <int ROWS, int SK>
+template <int ROWS, int SK, int NT>
 struct Stage {
-  static constexpr int kChunks = ROWS * Geo<SK>::kChunks / kThreads;
+  static constexpr int kChunks = ROWS * Geo<SK>::kChunks / NT;
   uint4 code[kChunks];
   uint32_t sc[Geo<SK>::kRowScales / 4];
 };
 
 // Loads one stage of ROWS rows.  Row i of the tile is global row rowmap(i);
 // rows at or beyond `nvalid` (and rowmap < 0) read as zero.
-template <int ROWS, int SK, class RowMap>
-__device__ __forceinline__ void load_stage(Stage<ROWS, SK>& st, const uint8_t* __restrict__ q,
+template <int ROWS, int SK, int NT, class RowMap>
+__device__ __forceinline__ void load_stage(Stage<ROWS, SK, NT>& st, const uint8_t* __restrict__ q,
                                            const uint8_t* __restrict__ sf, RowMap rowmap, int nvalid,
                                            int K, int k0, bool sc_aligned, int tid) {
   using Gm = Geo<SK>;
   const int row_bytes = K / 2, row_blocks = K / 32;
 #pragma unroll
-  for (int i = 0; i < Stage<ROWS, SK>::kChunks; i++) {
-    const int idx = tid + i * kThreads;
+  for (int i = 0; i < Stage<ROWS, SK, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
     const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
     const int gr = rowmap(r);
     const int kb = k0 / 2 + c * 16;
@@ -108,12 +109,12 @@ __device__ __forceinline__ void load_stage(Stage<ROWS, SK>& st, const uint8_t* _
   }
 }
 
-template <int ROWS, int SK>
-__device__ __forceinline__ void store_stage(const Stage<ROWS, SK>& st, uint8_t* lq, uint8_t* ls, int tid) {
+template <int ROWS, int SK, int NT>
+__device__ __forceinline__ void store_stage(const Stage<ROWS, SK, NT>& st, uint8_t* lq, uint8_t* ls, int tid) {
   using Gm = Geo<SK>;
 #pragma unroll
-  for (int i = 0; i < Stage<ROWS, SK>::kChunks; i++) {
-    const int idx = tid + i * kThreads;
+  for (int i = 0; i < Stage<ROWS, SK, NT>::kChunks; i++) {
+    const int idx = tid + i * NT;
     const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
     *reinterpret_cast<uint4*>(lq + r * Gm::kRowBytes + Gm::swz(r, c) * 16) = st.code[i];
   }
@@ -185,28 +186,53 @@ constexpr int kMaxGroups = (int)kMaxExperts;
 template <int BM, int BN>
 constexpr int wg_per_cu() { return BM * BN <= 128 * 128 ? 2 : 1; }
 
-// kDMA: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring filled by
-// direct-to-LDS loads.  Otherwise: register-staged double buffer, any K % 32.
+// DSG > 0: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring of codes
+// filled by direct-to-LDS loads.  The E8M0 scales come with each stage
+// (DSG = 1) or, when K % (128*DSG) == 0, in groups of DSG stages (16 or 8
+// bytes per row) through a separate two-slot LDS ring: a row's scales of one
+// stage are 4 bytes in their own cache line, so grouping cuts the memory
+// requests of the scale stream by DSG.  DSG = 0: register-staged double
+// buffer, any K % 32.
 constexpr int kRing = 4;
 
-template <int BM, int BN, int SK, int EPI, bool kDMA>
-__global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped(Args p) {
+// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the counter's immediate must
+// be a constant).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define BSFP4_WV(x) case x: wait_vmcnt<x>(); break;
+    BSFP4_WV(0) BSFP4_WV(1) BSFP4_WV(2) BSFP4_WV(3) BSFP4_WV(4) BSFP4_WV(5) BSFP4_WV(6) BSFP4_WV(7)
+    BSFP4_WV(8) BSFP4_WV(9) BSFP4_WV(10) BSFP4_WV(11) BSFP4_WV(12) BSFP4_WV(13) BSFP4_WV(14) BSFP4_WV(15)
+    BSFP4_WV(16) BSFP4_WV(17) BSFP4_WV(18) BSFP4_WV(19) BSFP4_WV(20) BSFP4_WV(21) BSFP4_WV(22) BSFP4_WV(23)
+    BSFP4_WV(24) BSFP4_WV(25) BSFP4_WV(26) BSFP4_WV(27) BSFP4_WV(28) BSFP4_WV(29) BSFP4_WV(30)
+#undef BSFP4_WV
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+template <int BM, int BN, int WGN, int SK, int EPI, int DSG>
+__global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_grouped(Args p) {
+  constexpr int NT = 128 * WGN;  // 2 x WGN waves
+  constexpr bool kDMA = DSG > 0;
   static_assert(!kDMA || SK == 128, "the LDS ring uses 128-value stages");
+  static_assert(DSG == 0 || DSG == 1 || DSG == 2 || DSG == 4, "scale group");
   using Gm = Geo<SK>;
   constexpr int kRowBytes = Gm::kRowBytes, kRowScales = Gm::kRowScales;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
-  constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
+  constexpr bool kGrouped = DSG >= 2;
+  constexpr int kStage = kA + kB + (kGrouped ? 0 : (BM + BN) * kRowScales);
+  constexpr int kScRow = 4 * DSG;                             // grouped: scale bytes per row per group
+  constexpr int kScSlot = kGrouped ? (BM + BN) * kScRow : 0;  // grouped: one scale-ring slot
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
   constexpr int kSlots = kDMA ? kRing : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage + 2 * kScSlot];
   __shared__ int tile_start[kMaxGroups + 1];
-  __shared__ int wave_sum[4];
+  __shared__ int wave_sum[NT / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, g = lane >> 5;
   const int ntn = (p.N + BN - 1) / BN;
   const int K = p.K;
@@ -247,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
       if (e < p.E) tile_start[e] = base;
       base += cnt[j];
     }
-    if (tid == 255) tile_start[p.E] = base;  // thread 255 owns the last groups
+    if (tid == NT - 1) tile_start[p.E] = base;  // the last thread owns the last groups
     __syncthreads();
     total = tile_start[p.E];
   }
@@ -275,7 +301,19 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
       nmt = (row_end - row0 + BM - 1) / BM;
     }
     const int local = t - (p.offsets ? tile_start[e] : 0);
-    const int tn = local / nmt, tmi = local % nmt;
+    int tn, tmi;
+    if (p.offsets == nullptr) {
+      // dense: bands of 4 row tiles, so that the 32 consecutive items an XCD
+      // receives form a 4 x 8 block of tiles (fewer A and B panels per L2)
+      const int band_items = 4 * ntn;
+      const int band = local / band_items, in_band = local % band_items;
+      const int band_rows = min(4, nmt - band * 4);
+      tmi = band * 4 + in_band % band_rows;
+      tn = in_band / band_rows;
+    } else {
+      tn = local / nmt;
+      tmi = local % nmt;
+    }
     const int m0 = row0 + tmi * BM;
     const int nvalid_a = row_end < p.rows ? row_end : p.rows;
     const uint8_t* Wq = p.W + (int64_t)e * p.N * (K / 2);
@@ -310,13 +348,22 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
     const int nst = (K + SK - 1) / SK;
     if constexpr (kDMA) {
       // per-lane sources of this tile's DMA instructions (zero page when invalid)
-      constexpr int kCodeI = (BM + BN) / 64;    // 1 KB code instructions per wave per stage
-      constexpr int kScaleI = (BM + BN) / 256;  // 256 B scale instructions per wave per stage
-      constexpr int kL = kCodeI + kScaleI;      // loads per wave per stage
+      constexpr int kWaves = NT / 64;
+      constexpr int kCodeI = (BM + BN) / 16 / kWaves;  // 1 KB code instructions per wave per stage
+      constexpr int kScaleI = kGrouped ? 0 : (BM + BN) / 64 / kWaves;  // 256 B scale instructions per wave per stage
+      // grouped scales: rows per instruction (16 B per lane, or 8 B per row as two 4-byte lanes)
+      constexpr int kScRowsPerI = DSG == 4 ? 64 : 32;
+      constexpr int kScGI = kGrouped ? (BM + BN) / kScRowsPerI / kWaves : 0;  // per wave per group
+      static_assert(kCodeI * kWaves * 16 == BM + BN && (kGrouped || kScaleI * kWaves * 64 == BM + BN) &&
+                        (!kGrouped || kScGI * kWaves * kScRowsPerI == BM + BN),
+                    "DMA instructions must cover the tile rows exactly");
+      constexpr int kL = kCodeI + kScaleI;      // ring loads per wave per stage
       const uint8_t* csrc[kCodeI];
       uint32_t cstep[kCodeI], cdst[kCodeI];
-      const uint8_t* ssrc[kScaleI];
-      uint32_t sstep[kScaleI], sdst[kScaleI];
+      const uint8_t* ssrc[kScaleI > 0 ? kScaleI : 1];
+      uint32_t sstep[kScaleI > 0 ? kScaleI : 1], sdst[kScaleI > 0 ? kScaleI : 1];
+      const uint8_t* gsrc[kScGI > 0 ? kScGI : 1];
+      uint32_t gstep[kScGI > 0 ? kScGI : 1], gdst[kScGI > 0 ? kScGI : 1];
 #pragma unroll
       for (int j = 0; j < kCodeI; j++) {
         const int q = wave * kCodeI + j;  // instruction index in the stage
@@ -344,7 +391,22 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
         sstep[j] = ok ? (uint32_t)(SK / 32) : 0u;
         sdst[j] = kA + kB + (isA ? 0 : BM * kRowScales) + qq * 256;
       }
+#pragma unroll
+      for (int j = 0; j < kScGI; j++) {
+        const int q = wave * kScGI + j;  // instruction index in the group
+        const int row_all = q * kScRowsPerI + (DSG == 4 ? lane : lane >> 1);  // 0..BM+BN-1
+        const bool isA = row_all < BM;
+        const int row = isA ? row_all : row_all - BM;
+        int gr = isA ? amap(row) : bmap(row);
+        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
+        const uint8_t* base = isA ? p.SFA : Ws;
+        const int half = DSG == 4 ? 0 : (lane & 1) * 4;
+        gsrc[j] = ok ? base + (int64_t)gr * (K / 32) + half : kZeroPage;
+        gstep[j] = ok ? (uint32_t)kScRow : 0u;
+        gdst[j] = (uint32_t)(q * kScRowsPerI * kScRow);  // LDS row r of the slot at r * kScRow
+      }
       const uint32_t lds0 = lds_offset(smem);
+      const uint32_t lds_sc = lds0 + (uint32_t)(kRing * kStage);
       auto issue = [&](int st) {
         const uint32_t slot = lds0 + (uint32_t)((st % kRing) * kStage);
 #pragma unroll
@@ -354,19 +416,69 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
         for (int j = 0; j < kScaleI; j++)
           lds_dma4(ssrc[j] + sstep[j] * (uint32_t)st, __builtin_amdgcn_readfirstlane(slot + sdst[j]));
       };
+      const int ngroups = kGrouped ? (nst + DSG - 1) / DSG : 0;
+      auto issue_scales = [&](int grp) {
+        const uint32_t slot = lds_sc + (uint32_t)((grp & 1) * kScSlot);
+#pragma unroll
+        for (int j = 0; j < kScGI; j++) {
+          if constexpr (DSG == 4)
+            lds_dma16(gsrc[j] + gstep[j] * (uint32_t)grp, __builtin_amdgcn_readfirstlane(slot + gdst[j]));
+          else
+            lds_dma4(gsrc[j] + gstep[j] * (uint32_t)grp, __builtin_amdgcn_readfirstlane(slot + gdst[j]));
+        }
+      };
+      // issue order: [scales 0] codes 0, 1, 2; at iteration t >= 0: codes t+3,
+      // then (grouped, t % DSG == 0) scales of group t/DSG + 1
+      if (kGrouped) issue_scales(0);
       for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
       for (int s = 0; s < nst; s++) {
-        const int ahead = min(kRing - 2, nst - 1 - s);  // stages issued after s
-        if (ahead >= 2) wait_vmcnt<2 * kL>();
-        else if (ahead == 1) wait_vmcnt<kL>();
-        else wait_vmcnt<0>();
+        // Wait until the codes of stage s (issued at iteration s-3; the
+        // prologue counts as iterations -3..-1) and its scale group q (issued
+        // at iteration (q-1)*DSG after that iteration's codes; group 0 first of
+        // all) have landed: count the loads issued after the later of the two.
+        int it_need = s - 3;
+        bool need_is_scale = false;
+        if constexpr (kGrouped) {
+          const int q = s / DSG;
+          const int its = q >= 1 ? (q - 1) * DSG : -4;
+          if (its >= it_need) {
+            it_need = its;
+            need_is_scale = true;
+          }
+        }
+        int after = 0;
+        if constexpr (kGrouped) {
+          if (!need_is_scale && it_need >= 0 && it_need % DSG == 0 && it_need / DSG + 1 < ngroups) after += kScGI;
+        }
+        for (int t = max(it_need + 1, -3); t < s; t++) {
+          if (t + 3 < nst) after += kL;
+          if constexpr (kGrouped) {
+            if (t >= 0 && t % DSG == 0 && t / DSG + 1 < ngroups) after += kScGI;
+          }
+        }
+        wait_vmcnt_dyn(after);
         __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
         if (s + kRing - 1 < nst) issue(s + kRing - 1);
+        if constexpr (kGrouped) {
+          if (s % DSG == 0 && s / DSG + 1 < ngroups) issue_scales(s / DSG + 1);
+        }
         const uint8_t* st = smem + (s % kRing) * kStage;
         const uint8_t* qa = st;
         const uint8_t* qb = st + kA;
-        const uint8_t* sa = st + kA + kB;
-        const uint8_t* sb = sa + BM * kRowScales;
+        const uint8_t* sa;
+        const uint8_t* sb;
+        int sc_pitch, sc_off;
+        if constexpr (kGrouped) {
+          sa = smem + kRing * kStage + ((s / DSG) & 1) * kScSlot;
+          sb = sa + BM * kScRow;
+          sc_pitch = kScRow;
+          sc_off = (s % DSG) * 4;
+        } else {
+          sa = st + kA + kB;
+          sb = sa + BM * kRowScales;
+          sc_pitch = kRowScales;
+          sc_off = 0;
+        }
 #pragma unroll
         for (int j = 0; j < SK / 64; j++) {
           const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
@@ -377,14 +489,14 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
             const int r = wn * WN + i * 32 + lr;
             const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
             fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            xb[i] = sb[r * kRowScales + c];
+            xb[i] = sb[r * sc_pitch + sc_off + c];
           }
   #pragma unroll
           for (int i = 0; i < TM; i++) {
             const int r = wm * WM + i * 32 + lr;
             const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
             const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            const int xa = sa[r * kRowScales + c];
+            const int xa = sa[r * sc_pitch + sc_off + c];
   #pragma unroll
             for (int jn = 0; jn < TN; jn++)
               acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
@@ -394,19 +506,19 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
       }
       __syncthreads();  // all waves are done with the ring before it is reused
     } else {
-    Stage<BM, SK> ra;
-      Stage<BN, SK> rb;
-      load_stage<BM, SK>(ra, p.A, p.SFA, amap, a_lim, K, 0, sc_aligned, tid);
-      load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
-      store_stage<BM, SK>(ra, smem, smem + kA + kB, tid);
-      store_stage<BN, SK>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
+    Stage<BM, SK, NT> ra;
+      Stage<BN, SK, NT> rb;
+      load_stage<BM, SK, NT>(ra, p.A, p.SFA, amap, a_lim, K, 0, sc_aligned, tid);
+      load_stage<BN, SK, NT>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
+      store_stage<BM, SK, NT>(ra, smem, smem + kA + kB, tid);
+      store_stage<BN, SK, NT>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
       __syncthreads();
   
       for (int s = 0; s < nst; s++) {
         const bool more = s + 1 < nst;
         if (more) {
-          load_stage<BM, SK>(ra, p.A, p.SFA, amap, a_lim, K, (s + 1) * SK, sc_aligned, tid);
-          load_stage<BN, SK>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
+          load_stage<BM, SK, NT>(ra, p.A, p.SFA, amap, a_lim, K, (s + 1) * SK, sc_aligned, tid);
+          load_stage<BN, SK, NT>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
         }
         const uint8_t* st = smem + (s & 1) * kStage;
         const uint8_t* qa = st;
@@ -439,8 +551,8 @@ __global__ void __launch_bounds__(kThreads, (wg_per_cu<BM, BN>())) mxfp4_grouped
         }
         if (more) {
           uint8_t* nx = smem + ((s + 1) & 1) * kStage;
-          store_stage<BM, SK>(ra, nx, nx + kA + kB, tid);
-          store_stage<BN, SK>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
+          store_stage<BM, SK, NT>(ra, nx, nx + kA + kB, tid);
+          store_stage<BN, SK, NT>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
         }
         __syncthreads();
       }
@@ -533,15 +645,39 @@ int cu_count() {
   return n;
 }
 
-template <int BM, int BN, int SK, int EPI>
+// Scale grouping of the DMA path: per-stage scales by default (grouping cuts
+// the scale requests 2-4x but measured 3-12% slower on the dense 4096 x 4096 x
+// 7168 problem); BSFP4_MXFP4_SCALE_GROUP=2|4 selects it.
+int scale_group(int K) {
+  const char* e = getenv("BSFP4_MXFP4_SCALE_GROUP");
+  const int cap = e ? atoi(e) : 1;
+  if (cap >= 4 && K % 512 == 0) return 4;
+  if (cap >= 2 && K % 256 == 0) return 2;
+  return 1;
+}
+
+template <int BM, int BN, int WGN, int SK, int EPI>
 hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
+  constexpr int NT = 128 * WGN;
   int64_t grid = (int64_t)cu_count() * wg_per_cu<BM, BN>();
   if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
-  if (a.K % 128 == 0)
-    mxfp4_grouped<BM, BN, 128, EPI, true><<<(unsigned)grid, kThreads, 0, stream>>>(a);
-  else
-    mxfp4_grouped<BM, BN, SK, EPI, false><<<(unsigned)grid, kThreads, 0, stream>>>(a);
+  if (a.K % 128 == 0) {
+    switch (scale_group(a.K)) {
+      case 4: mxfp4_grouped<BM, BN, WGN, 128, EPI, 4><<<(unsigned)grid, NT, 0, stream>>>(a); break;
+      case 2: mxfp4_grouped<BM, BN, WGN, 128, EPI, 2><<<(unsigned)grid, NT, 0, stream>>>(a); break;
+      default: mxfp4_grouped<BM, BN, WGN, 128, EPI, 1><<<(unsigned)grid, NT, 0, stream>>>(a); break;
+    }
+  } else {
+    mxfp4_grouped<BM, BN, WGN, SK, EPI, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
+  }
   return hipGetLastError();
+}
+
+// Waves per workgroup of the dense 256x256 kernel: 8 (2 x 4, two per SIMD) by
+// default, BSFP4_MXFP4_WAVES=4 for 2 x 2.
+int dense_waves() {
+  const char* e = getenv("BSFP4_MXFP4_WAVES");
+  return (e && e[0] == '4') ? 4 : 8;
 }
 
 }  // namespace
@@ -555,7 +691,8 @@ hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
   a.offsets = nullptr; a.E = 1;
   a.W = B; a.WSF = SFB; a.N = (int)N; a.K = (int)K; a.alpha = alpha; a.out = D;
   const int64_t items = ((M + 255) / 256) * ((N + 255) / 256);
-  return launch<256, 256, 128, kEpiStore>(a, items, stream);
+  if (dense_waves() == 4) return launch<256, 256, 2, 128, kEpiStore>(a, items, stream);
+  return launch<256, 256, 4, 128, kEpiStore>(a, items, stream);
 }
 
 hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* a_rows, int64_t a_nrows,
@@ -572,9 +709,9 @@ hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int
   constexpr int BM = 128, BN = 128;
   const int64_t max_items = ((rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
   switch (epilogue) {
-    case kEpiStore: return launch<BM, BN, 128, kEpiStore>(a, max_items, stream);
-    case kEpiSilu: return launch<BM, BN, 128, kEpiSilu>(a, max_items, stream);
-    default: return launch<BM, BN, 128, kEpiCombine>(a, max_items, stream);
+    case kEpiStore: return launch<BM, BN, 2, 128, kEpiStore>(a, max_items, stream);
+    case kEpiSilu: return launch<BM, BN, 2, 128, kEpiSilu>(a, max_items, stream);
+    default: return launch<BM, BN, 2, 128, kEpiCombine>(a, max_items, stream);
   }
 }
 
