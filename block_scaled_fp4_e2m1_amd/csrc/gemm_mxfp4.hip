@@ -127,30 +127,46 @@ __device__ __forceinline__ void store_stage(const Stage<ROWS, SK, NT>& st, uint8
 }
 
 // ---- direct-to-LDS loads ---------------------------------------------------
-// global_load_lds_dword{,x4}: every lane fetches 4 / 16 bytes from its own
-// global address and the wave writes them to LDS at M0 + lane * size, so one
-// instruction fills 256 B / 1 KB of LDS without passing through VGPRs.  They
-// are issued from inline assembly so that the compiler does not add a full
-// vmcnt(0) wait before every LDS read (it cannot tell which ring slot an LDS
-// DMA targets); the kernel waits explicitly with s_waitcnt vmcnt(n) + s_barrier.
-__device__ __attribute__((aligned(16))) const uint8_t kZeroPage[16] = {};
-
+// buffer_load_dword{,x4} ... lds: every lane fetches 4 / 16 bytes and the wave
+// writes them to LDS at M0 + lane * size, so one instruction fills 256 B / 1 KB
+// of LDS without passing through VGPRs.  They are issued from inline assembly
+// so that the compiler does not add a full vmcnt(0) wait before every LDS read
+// (it cannot tell which ring slot an LDS DMA targets); the kernel waits
+// explicitly with s_waitcnt vmcnt(n) + s_barrier.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_uniform) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// Addressing: a buffer resource (SGPRs), a per-lane 32-bit offset and a
+// uniform SGPR offset; lanes whose offset is past the buffer's size read zeros.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buf_lds16(v4u32 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_uniform) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(g), "s"(lds_uniform)
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_uniform)
                : "memory");
 }
 
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_uniform) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+__device__ __forceinline__ void buf_lds4(v4u32 rsrc, uint32_t voff, uint32_t soff, uint32_t lds_uniform) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :
-               : "v"(g), "s"(lds_uniform)
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_uniform)
                : "memory");
+}
+
+// Raw buffer resource over [p, p + bytes) (bytes < 2^31), uniform.
+__device__ __forceinline__ v4u32 make_rsrc4(const void* p, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return v4u32{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+constexpr uint32_t kBufOOB = 0x80000000u;  // lane offset past every buffer: reads zero
+
+__device__ __forceinline__ v4u32 uniform4(v4u32 v) {
+  return v4u32{(uint32_t)__builtin_amdgcn_readfirstlane((int)v.x), (uint32_t)__builtin_amdgcn_readfirstlane((int)v.y),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)v.z), (uint32_t)__builtin_amdgcn_readfirstlane((int)v.w)};
 }
 
 template <int N>
@@ -186,52 +202,30 @@ constexpr int kMaxGroups = (int)kMaxExperts;
 template <int BM, int BN>
 constexpr int wg_per_cu() { return BM * BN <= 128 * 128 ? 2 : 1; }
 
-// DSG > 0: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring of codes
-// filled by direct-to-LDS loads.  The E8M0 scales come with each stage
-// (DSG = 1) or, when K % (128*DSG) == 0, in groups of DSG stages (16 or 8
-// bytes per row) through a separate two-slot LDS ring: a row's scales of one
-// stage are 4 bytes in their own cache line, so grouping cuts the memory
-// requests of the scale stream by DSG.  DSG = 0: register-staged double
-// buffer, any K % 32.
+// kDMA: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring filled by
+// direct-to-LDS buffer loads.  Otherwise: register-staged double buffer, any
+// K % 32.
 constexpr int kRing = 4;
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 31] (the counter's immediate must
-// be a constant).
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-#define BSFP4_WV(x) case x: wait_vmcnt<x>(); break;
-    BSFP4_WV(0) BSFP4_WV(1) BSFP4_WV(2) BSFP4_WV(3) BSFP4_WV(4) BSFP4_WV(5) BSFP4_WV(6) BSFP4_WV(7)
-    BSFP4_WV(8) BSFP4_WV(9) BSFP4_WV(10) BSFP4_WV(11) BSFP4_WV(12) BSFP4_WV(13) BSFP4_WV(14) BSFP4_WV(15)
-    BSFP4_WV(16) BSFP4_WV(17) BSFP4_WV(18) BSFP4_WV(19) BSFP4_WV(20) BSFP4_WV(21) BSFP4_WV(22) BSFP4_WV(23)
-    BSFP4_WV(24) BSFP4_WV(25) BSFP4_WV(26) BSFP4_WV(27) BSFP4_WV(28) BSFP4_WV(29) BSFP4_WV(30)
-#undef BSFP4_WV
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
-template <int BM, int BN, int WGN, int SK, int EPI, int DSG>
+// kLoaders: waves that issue the ring's loads (0: all).
+template <int BM, int BN, int WGN, int SK, int EPI, bool kDMA, int kLoaders>
 __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_grouped(Args p) {
   constexpr int NT = 128 * WGN;  // 2 x WGN waves
-  constexpr bool kDMA = DSG > 0;
   static_assert(!kDMA || SK == 128, "the LDS ring uses 128-value stages");
-  static_assert(DSG == 0 || DSG == 1 || DSG == 2 || DSG == 4, "scale group");
   using Gm = Geo<SK>;
   constexpr int kRowBytes = Gm::kRowBytes, kRowScales = Gm::kRowScales;
   constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
-  constexpr bool kGrouped = DSG >= 2;
-  constexpr int kStage = kA + kB + (kGrouped ? 0 : (BM + BN) * kRowScales);
-  constexpr int kScRow = 4 * DSG;                             // grouped: scale bytes per row per group
-  constexpr int kScSlot = kGrouped ? (BM + BN) * kScRow : 0;  // grouped: one scale-ring slot
+  constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
   constexpr int kSlots = kDMA ? kRing : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage + 2 * kScSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int wave_sum[NT / 64];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, g = lane >> 5;
   const int ntn = (p.N + BN - 1) / BN;
@@ -347,160 +341,117 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
 
     const int nst = (K + SK - 1) / SK;
     if constexpr (kDMA) {
-      // per-lane sources of this tile's DMA instructions (zero page when invalid)
+      // Direct-to-LDS ring, filled by kLoad waves (all waves, or the first
+      // kLoaders).  Per stage: (BM+BN)/16 code loads of 16 rows x 64 B and
+      // (BM+BN)/64 scale loads of 64 rows x 4 B; each lane keeps one 32-bit
+      // offset per load (kBufOOB for rows outside the problem), the stage's K
+      // offset goes in the SGPR offset.
       constexpr int kWaves = NT / 64;
-      constexpr int kCodeI = (BM + BN) / 16 / kWaves;  // 1 KB code instructions per wave per stage
-      constexpr int kScaleI = kGrouped ? 0 : (BM + BN) / 64 / kWaves;  // 256 B scale instructions per wave per stage
-      // grouped scales: rows per instruction (16 B per lane, or 8 B per row as two 4-byte lanes)
-      constexpr int kScRowsPerI = DSG == 4 ? 64 : 32;
-      constexpr int kScGI = kGrouped ? (BM + BN) / kScRowsPerI / kWaves : 0;  // per wave per group
-      static_assert(kCodeI * kWaves * 16 == BM + BN && (kGrouped || kScaleI * kWaves * 64 == BM + BN) &&
-                        (!kGrouped || kScGI * kWaves * kScRowsPerI == BM + BN),
-                    "DMA instructions must cover the tile rows exactly");
-      constexpr int kL = kCodeI + kScaleI;      // ring loads per wave per stage
-      const uint8_t* csrc[kCodeI];
-      uint32_t cstep[kCodeI], cdst[kCodeI];
-      const uint8_t* ssrc[kScaleI > 0 ? kScaleI : 1];
-      uint32_t sstep[kScaleI > 0 ? kScaleI : 1], sdst[kScaleI > 0 ? kScaleI : 1];
-      const uint8_t* gsrc[kScGI > 0 ? kScGI : 1];
-      uint32_t gstep[kScGI > 0 ? kScGI : 1], gdst[kScGI > 0 ? kScGI : 1];
+      constexpr int kLoad = kLoaders > 0 ? kLoaders : kWaves;
+      constexpr int kCodeI = (BM + BN) / 16 / kLoad;
+      constexpr int kScaleI = (BM + BN) / 64 / kLoad;
+      static_assert(kCodeI * kLoad * 16 == BM + BN && kScaleI * kLoad * 64 == BM + BN,
+                    "DMA loads must cover the tile rows exactly");
+      constexpr int kL = kCodeI + kScaleI;  // ring loads per loading wave per stage
+      const bool loader = wave < kLoad;
+      const v4u32 ra_q = make_rsrc4(p.A, (int64_t)a_lim * (K / 2));
+      const v4u32 ra_s = make_rsrc4(p.SFA, (int64_t)a_lim * (K / 32));
+      const v4u32 rw_q = make_rsrc4(Wq, (int64_t)p.N * (K / 2));
+      const v4u32 rw_s = make_rsrc4(Ws, (int64_t)p.N * (K / 32));
+      uint32_t cv[kCodeI], sv[kScaleI];
 #pragma unroll
       for (int j = 0; j < kCodeI; j++) {
-        const int q = wave * kCodeI + j;  // instruction index in the stage
+        const int q = (loader ? wave : 0) * kCodeI + j;  // load index in the stage
         const bool isA = q < BM / 16;
         const int qq = isA ? q : q - BM / 16;
         const int row = qq * 16 + (lane >> 2);  // tile row of this lane's chunk
         const int c = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);  // logical chunk
-        int gr = isA ? amap(row) : bmap(row);
+        const int gr = isA ? amap(row) : bmap(row);
         const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        const uint8_t* base = isA ? p.A : Wq;
-        csrc[j] = ok ? base + (int64_t)gr * (K / 2) + c * 16 : kZeroPage;
-        cstep[j] = ok ? (uint32_t)(SK / 2) : 0u;
-        cdst[j] = (isA ? 0 : kA) + qq * 1024;
+        cv[j] = ok ? (uint32_t)(gr * (K / 2) + c * 16) : kBufOOB;
       }
 #pragma unroll
       for (int j = 0; j < kScaleI; j++) {
-        const int q = wave * kScaleI + j;
+        const int q = (loader ? wave : 0) * kScaleI + j;
         const bool isA = q < BM / 64;
         const int qq = isA ? q : q - BM / 64;
         const int row = qq * 64 + lane;
-        int gr = isA ? amap(row) : bmap(row);
+        const int gr = isA ? amap(row) : bmap(row);
         const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        const uint8_t* base = isA ? p.SFA : Ws;
-        ssrc[j] = ok ? base + (int64_t)gr * (K / 32) : kZeroPage;
-        sstep[j] = ok ? (uint32_t)(SK / 32) : 0u;
-        sdst[j] = kA + kB + (isA ? 0 : BM * kRowScales) + qq * 256;
-      }
-#pragma unroll
-      for (int j = 0; j < kScGI; j++) {
-        const int q = wave * kScGI + j;  // instruction index in the group
-        const int row_all = q * kScRowsPerI + (DSG == 4 ? lane : lane >> 1);  // 0..BM+BN-1
-        const bool isA = row_all < BM;
-        const int row = isA ? row_all : row_all - BM;
-        int gr = isA ? amap(row) : bmap(row);
-        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        const uint8_t* base = isA ? p.SFA : Ws;
-        const int half = DSG == 4 ? 0 : (lane & 1) * 4;
-        gsrc[j] = ok ? base + (int64_t)gr * (K / 32) + half : kZeroPage;
-        gstep[j] = ok ? (uint32_t)kScRow : 0u;
-        gdst[j] = (uint32_t)(q * kScRowsPerI * kScRow);  // LDS row r of the slot at r * kScRow
+        sv[j] = ok ? (uint32_t)(gr * (K / 32)) : kBufOOB;
       }
       const uint32_t lds0 = lds_offset(smem);
-      const uint32_t lds_sc = lds0 + (uint32_t)(kRing * kStage);
       auto issue = [&](int st) {
         const uint32_t slot = lds0 + (uint32_t)((st % kRing) * kStage);
 #pragma unroll
-        for (int j = 0; j < kCodeI; j++)
-          lds_dma16(csrc[j] + cstep[j] * (uint32_t)st, __builtin_amdgcn_readfirstlane(slot + cdst[j]));
+        for (int j = 0; j < kCodeI; j++) {
+          const int q = wave * kCodeI + j;
+          const bool isA = q < BM / 16;
+          const uint32_t dst = slot + (uint32_t)((isA ? 0 : kA) + (isA ? q : q - BM / 16) * 1024);
+          buf_lds16(uniform4(isA ? ra_q : rw_q), cv[j], (uint32_t)(st * (SK / 2)),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
+        }
 #pragma unroll
-        for (int j = 0; j < kScaleI; j++)
-          lds_dma4(ssrc[j] + sstep[j] * (uint32_t)st, __builtin_amdgcn_readfirstlane(slot + sdst[j]));
-      };
-      const int ngroups = kGrouped ? (nst + DSG - 1) / DSG : 0;
-      auto issue_scales = [&](int grp) {
-        const uint32_t slot = lds_sc + (uint32_t)((grp & 1) * kScSlot);
-#pragma unroll
-        for (int j = 0; j < kScGI; j++) {
-          if constexpr (DSG == 4)
-            lds_dma16(gsrc[j] + gstep[j] * (uint32_t)grp, __builtin_amdgcn_readfirstlane(slot + gdst[j]));
-          else
-            lds_dma4(gsrc[j] + gstep[j] * (uint32_t)grp, __builtin_amdgcn_readfirstlane(slot + gdst[j]));
+        for (int j = 0; j < kScaleI; j++) {
+          const int q = wave * kScaleI + j;
+          const bool isA = q < BM / 64;
+          const uint32_t dst =
+              slot + (uint32_t)(kA + kB + (isA ? 0 : BM * kRowScales) + (isA ? q : q - BM / 64) * 256);
+          buf_lds4(uniform4(isA ? ra_s : rw_s), sv[j], (uint32_t)(st * (SK / 32)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
         }
       };
-      // issue order: [scales 0] codes 0, 1, 2; at iteration t >= 0: codes t+3,
-      // then (grouped, t % DSG == 0) scales of group t/DSG + 1
-      if (kGrouped) issue_scales(0);
-      for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
+      if (loader)
+        for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
       for (int s = 0; s < nst; s++) {
-        // Wait until the codes of stage s (issued at iteration s-3; the
-        // prologue counts as iterations -3..-1) and its scale group q (issued
-        // at iteration (q-1)*DSG after that iteration's codes; group 0 first of
-        // all) have landed: count the loads issued after the later of the two.
-        int it_need = s - 3;
-        bool need_is_scale = false;
-        if constexpr (kGrouped) {
-          const int q = s / DSG;
-          const int its = q >= 1 ? (q - 1) * DSG : -4;
-          if (its >= it_need) {
-            it_need = its;
-            need_is_scale = true;
-          }
+        if (loader) {
+          const int ahead = min(kRing - 2, nst - 1 - s);  // stages issued after s
+          if (ahead >= 2) wait_vmcnt<2 * kL>();
+          else if (ahead == 1) wait_vmcnt<kL>();
+          else wait_vmcnt<0>();
         }
-        int after = 0;
-        if constexpr (kGrouped) {
-          if (!need_is_scale && it_need >= 0 && it_need % DSG == 0 && it_need / DSG + 1 < ngroups) after += kScGI;
-        }
-        for (int t = max(it_need + 1, -3); t < s; t++) {
-          if (t + 3 < nst) after += kL;
-          if constexpr (kGrouped) {
-            if (t >= 0 && t % DSG == 0 && t / DSG + 1 < ngroups) after += kScGI;
-          }
-        }
-        wait_vmcnt_dyn(after);
         __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
-        if (s + kRing - 1 < nst) issue(s + kRing - 1);
-        if constexpr (kGrouped) {
-          if (s % DSG == 0 && s / DSG + 1 < ngroups) issue_scales(s / DSG + 1);
-        }
+        if (loader && s + kRing - 1 < nst) issue(s + kRing - 1);
         const uint8_t* st = smem + (s % kRing) * kStage;
         const uint8_t* qa = st;
         const uint8_t* qb = st + kA;
-        const uint8_t* sa;
-        const uint8_t* sb;
-        int sc_pitch, sc_off;
-        if constexpr (kGrouped) {
-          sa = smem + kRing * kStage + ((s / DSG) & 1) * kScSlot;
-          sb = sa + BM * kScRow;
-          sc_pitch = kScRow;
-          sc_off = (s % DSG) * 4;
-        } else {
-          sa = st + kA + kB;
-          sb = sa + BM * kRowScales;
-          sc_pitch = kRowScales;
-          sc_off = 0;
-        }
+        const uint8_t* sa = st + kA + kB;
+        const uint8_t* sb = sa + BM * kRowScales;
+        // the 4 scale bytes of a fragment row as one dword (lanes g = 0 / 1 of a
+        // row read the same dword), shifted so that byte 2j is this lane's
+        // chunk 2j + g; the MFMA's op_sel picks byte 2j
+        static_assert(kRowScales == 4, "one scale dword per row per stage");
+        uint32_t xa4[TM], xb4[TN];
+#pragma unroll
+        for (int i = 0; i < TN; i++)
+          xb4[i] = *reinterpret_cast<const uint32_t*>(sb + (wn * WN + i * 32 + lr) * 4) >> (8 * g);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+          xa4[i] = *reinterpret_cast<const uint32_t*>(sa + (wm * WM + i * 32 + lr) * 4) >> (8 * g);
 #pragma unroll
         for (int j = 0; j < SK / 64; j++) {
           const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
           v8i fb[TN];
-          int xb[TN];
   #pragma unroll
           for (int i = 0; i < TN; i++) {
             const int r = wn * WN + i * 32 + lr;
             const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
             fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            xb[i] = sb[r * sc_pitch + sc_off + c];
           }
   #pragma unroll
           for (int i = 0; i < TM; i++) {
             const int r = wm * WM + i * 32 + lr;
             const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
             const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            const int xa = sa[r * sc_pitch + sc_off + c];
   #pragma unroll
-            for (int jn = 0; jn < TN; jn++)
-              acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
-                                                                           0, xb[jn]);
+            for (int jn = 0; jn < TN; jn++) {
+              if (j == 0)
+                acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0,
+                                                                             (int)xa4[i], 0, (int)xb4[jn]);
+              else
+                acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 2,
+                                                                             (int)xa4[i], 2, (int)xb4[jn]);
+            }
           }
         }
       }
@@ -645,15 +596,11 @@ int cu_count() {
   return n;
 }
 
-// Scale grouping of the DMA path: per-stage scales by default (grouping cuts
-// the scale requests 2-4x but measured 3-12% slower on the dense 4096 x 4096 x
-// 7168 problem); BSFP4_MXFP4_SCALE_GROUP=2|4 selects it.
-int scale_group(int K) {
-  const char* e = getenv("BSFP4_MXFP4_SCALE_GROUP");
-  const int cap = e ? atoi(e) : 1;
-  if (cap >= 4 && K % 512 == 0) return 4;
-  if (cap >= 2 && K % 256 == 0) return 2;
-  return 1;
+// Loader waves of the DMA ring (BSFP4_MXFP4_LOADERS, measurement override):
+// 0 = every wave issues its share.
+int loaders() {
+  const char* e = getenv("BSFP4_MXFP4_LOADERS");
+  return e ? atoi(e) : 0;
 }
 
 template <int BM, int BN, int WGN, int SK, int EPI>
@@ -662,13 +609,15 @@ hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
   int64_t grid = (int64_t)cu_count() * wg_per_cu<BM, BN>();
   if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
   if (a.K % 128 == 0) {
-    switch (scale_group(a.K)) {
-      case 4: mxfp4_grouped<BM, BN, WGN, 128, EPI, 4><<<(unsigned)grid, NT, 0, stream>>>(a); break;
-      case 2: mxfp4_grouped<BM, BN, WGN, 128, EPI, 2><<<(unsigned)grid, NT, 0, stream>>>(a); break;
-      default: mxfp4_grouped<BM, BN, WGN, 128, EPI, 1><<<(unsigned)grid, NT, 0, stream>>>(a); break;
-    }
+    const int l = loaders();
+    if (l == 2 && (BM + BN) / 64 % 2 == 0)
+      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, 2><<<(unsigned)grid, NT, 0, stream>>>(a);
+    else if (l == 4 && NT / 64 > 4 && (BM + BN) / 64 % 4 == 0)
+      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, (NT / 64 > 4 ? 4 : 0)><<<(unsigned)grid, NT, 0, stream>>>(a);
+    else
+      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
   } else {
-    mxfp4_grouped<BM, BN, WGN, SK, EPI, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
+    mxfp4_grouped<BM, BN, WGN, SK, EPI, false, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -63,12 +63,12 @@ def test_mxfp4_gemm_deterministic():
     assert np.array_equal(_run(aq, sfa, bq, sfb), _run(aq, sfa, bq, sfb))
 
 
-@pytest.mark.parametrize("sg", ["2", "4"])
+@pytest.mark.parametrize("sg", ["0", "2", "4"])
 @pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("M,N,K", [(300, 544, 2048), (256, 256, 1536), (77, 96, 4096)])
-def test_mxfp4_gemm_scale_groups(monkeypatch, sg, waves, M, N, K):
-    """The grouped-scale DMA path and both wave layouts of the dense kernel."""
-    monkeypatch.setenv("BSFP4_MXFP4_SCALE_GROUP", sg)
+def test_mxfp4_gemm_loader_waves(monkeypatch, sg, waves, M, N, K):
+    """Loader-wave splits of the DMA ring and both wave layouts of the dense kernel."""
+    monkeypatch.setenv("BSFP4_MXFP4_LOADERS", sg)
     monkeypatch.setenv("BSFP4_MXFP4_WAVES", waves)
     aq, sfa, bq, sfb = mxfp4_problem(M, N, K, seed=900 + M)
     _check(_run(aq, sfa, bq, sfb), aq, sfa, bq, sfb)
