@@ -235,6 +235,10 @@ __global__ void __launch_bounds__(256)
   const int k_lo = split * KR;
   const int k_hi = min(K, k_lo + KR);
   const int c = lane & 15, g = lane >> 4;
+  // activation rows 8-15 of each 16-row tile hold their 64-byte K chunks pairwise
+  // swapped (chunk ch at ch ^ 1), so the 16 lanes of one ds_read_b128 phase fall
+  // on distinct banks
+  const int swz = ((c >> 3) & 1) << 6;
 
   // ---- activation loads first (few, L2-resident): the per-wave memory queue
   // returns in order, so loads issued after the weight stream would wait for it
@@ -286,7 +290,7 @@ __global__ void __launch_bounds__(256)
     const int it = tid + 256 * u;
     if (it >= kItems) break;
     const int row = it / (KR / 32), ch = it % (KR / 32);
-    uint8_t* dst = act + row * kPitch + ch * 64;
+    uint8_t* dst = act + row * kPitch + ((ch ^ ((row >> 3) & 1)) * 64);
     if constexpr (AKIND == 0) {
       const _Float16 s0 = e4m3_to_f16(as2[u] & 0xFFu), s1 = e4m3_to_f16(as2[u] >> 8);
       *reinterpret_cast<v8h*>(dst) = dq8_f16(aq[u][0].x, s0);
@@ -310,7 +314,7 @@ __global__ void __launch_bounds__(256)
     for (int s = 0; s < 4; s++) {
       const uint32_t word = s == 0 ? code[j].x : s == 1 ? code[j].y : s == 2 ? code[j].z : code[j].w;
       const uint32_t sbyte = (sc[j] >> (8 * (s >> 1))) & 0xFFu;
-      const int koff = 2 * (128 * j + 32 * g + 8 * s);
+      const int koff = (2 * (128 * j + 32 * g + 8 * s)) ^ swz;
       if constexpr (AKIND == 0) {
         const v8h fb = dq8_f16(word, e4m3_to_f16(sbyte));
 #pragma unroll
