@@ -341,16 +341,17 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, int64
   if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
     float* y = static_cast<float*>(ws);
     hipError_t e = bsfp4::launch_mxfp4_grouped(Aq, Asf, a_row_index, a_rows_total, expert_offsets, E, rows, W, Wsf,
-                                               N, K, bsfp4::kEpiCombine, nullptr, nullptr, nullptr, ep->sorted_ids,
-                                               ep->topk_weights, y, st);
-    if (e == hipSuccess) e = bsfp4::launch_topk_sum(y, static_cast<uint16_t*>(ep->out), T, ep->topk, N, st);
+                                               N, K, bsfp4::kEpiCombine, nullptr, nullptr, nullptr, ep->sorted_ids, y,
+                                               st);
+    if (e == hipSuccess)
+      e = bsfp4::launch_topk_sum(y, ep->topk_weights, static_cast<uint16_t*>(ep->out), T, ep->topk, N, st);
     return launched(e, "mxfp4_moe_grouped_gemm launch");
   }
   return launched(bsfp4::launch_mxfp4_grouped(Aq, Asf, a_row_index, a_rows_total, expert_offsets, E, rows, W, Wsf,
                                               N, K,
                                               epilogue == BSFP4_MOE_STORE_BF16 ? bsfp4::kEpiStore : bsfp4::kEpiSilu,
                                               static_cast<uint16_t*>(ep->out), ep->out_q, ep->out_sf, nullptr,
-                                              nullptr, nullptr, st),
+                                              nullptr, st),
                   "mxfp4_moe_grouped_gemm launch");
 }
 

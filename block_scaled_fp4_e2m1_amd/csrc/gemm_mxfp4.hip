@@ -25,13 +25,17 @@
 //   SILU     the tile's columns are gate/up pairs: column blocks of 32 alternate
 //            gate rows [32b, 32b+32) and up rows [N/2 + 32b, ...) of W, so a lane
 //            holds gate and up of the same element; act = bf16(silu(h_g) * h_u)
-//            from the bf16-rounded h, staged in LDS and re-quantised to MXFP4 per
-//            32-element block (the fused `silu_and_mul_scaled_fp4_experts_quant`
-//            pattern of the vLLM `sm103` branch comparison page, MXFP4 form);
-//   COMBINE  y[f] = topk_weight[f] * row in FP32 for the row's flat (token, slot)
-//            index f; a second kernel sums each token's top-k rows in slot order
-//            and rounds once to bf16 (deterministic; the same layer with device-wide
-//            float atomics for the combine measured about 2x slower).
+//            from the bf16-rounded h (SiLU with the hardware exp2 and reciprocal),
+//            staged in LDS and re-quantised to MXFP4 per 32-element block with
+//            the hardware bf16 -> E2M1 conversion (the fused
+//            `silu_and_mul_scaled_fp4_experts_quant` pattern of the vLLM `sm103`
+//            branch comparison page, MXFP4 form);
+//   COMBINE  y[f] = row in FP32 for the row's flat (token, slot) index f; a
+//            second kernel sums topk_weight[f] * y[f] over each token's slots in
+//            slot order and rounds once to bf16 (deterministic; the same layer
+//            with device-wide float atomics for the combine measured about 2x
+//            slower).  The tile's f indices are loaded when the tile starts and
+//            reach the epilogue through LDS.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -191,11 +195,13 @@ struct Args {
   uint8_t* out_q;          // SILU: [rows, N/4]
   uint8_t* out_sf;         // SILU: [rows, N/64]
   const int32_t* sorted_ids;  // COMBINE
-  const float* topk_w;        // COMBINE
   float* y_f32;               // COMBINE: [T * topk, N], row f = flat (token, slot) index
 };
 
 constexpr int kMaxGroups = (int)kMaxExperts;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Workgroups per CU the register budget is sized for: small tiles keep two
 // resident so that one's loads overlap the other's MFMAs.
@@ -220,8 +226,16 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
   constexpr int kSlots = kDMA ? kRing : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
+  // SILU: each wave stages its WM x kActCols bf16 act tile in LDS with a row
+  // pitch of kActCols + 8 elements (an odd number of 16-byte chunks), so that
+  // the quantiser's 128-bit row reads by consecutive lanes are conflict-free
+  constexpr int kActCols = (TN / 2) * 32;
+  constexpr int kActPitch = kActCols + 8;
+  constexpr int kActBytes = EPI == kEpiSilu ? (NT / 64) * WM * kActPitch * 2 : 0;
+  constexpr int kSmem = kSlots * kStage > kActBytes ? kSlots * kStage : kActBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   __shared__ int tile_start[kMaxGroups + 1];
+  __shared__ int row_f[EPI == kEpiCombine ? BM : 1];
   __shared__ int wave_sum[NT / 64];
 
   const int tid = threadIdx.x;
@@ -332,6 +346,13 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
         return tn * BN + i;
       }
     };
+
+    // COMBINE: flat index of tile row tid, loaded before the K loop's loads so
+    // that it has arrived when the epilogue needs it
+    int rf = -1;
+    if constexpr (EPI == kEpiCombine) {
+      if (tid < BM && m0 + tid < nvalid_a) rf = p.sorted_ids[m0 + tid];
+    }
 
     v16f acc[TM][TN];
 #pragma unroll
@@ -526,54 +547,88 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
           }
         }
     } else if constexpr (EPI == kEpiCombine) {
-      // y[f] = topk_weight[f] * row, f = flat (token, slot) index of the row; the
-      // top-k sum is done afterwards in a fixed order (deterministic, no atomics)
+      // y[f] = row, f = flat (token, slot) index of the row; the weighted top-k
+      // sum is done afterwards in a fixed order (deterministic, no atomics)
+      if (tid < BM) row_f[tid] = rf;
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < TM; i++) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (m >= nvalid_a) continue;
-          const int f = p.sorted_ids[m];
-          const float w = p.topk_w[f];
+          const int f = row_f[wm * WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3)];
           float* dst = p.y_f32 + (int64_t)f * p.N;
 #pragma unroll
           for (int jn = 0; jn < TN; jn++) {
             const int n = tn * BN + wn * WN + jn * 32 + lr;
-            if (n < p.N) dst[n] = w * acc[i][jn][r];
+            if (n < p.N) dst[n] = acc[i][jn][r];
           }
         }
       }
     } else {
-      // SILU: act tile of this wave = WM rows x (TN/2)*32 columns, bf16, in LDS
-      constexpr int kActCols = (TN / 2) * 32;
-      uint16_t* act = reinterpret_cast<uint16_t*>(smem) + wave * (WM * kActCols);
+      // SILU: act tile of this wave = WM rows x kActCols columns, bf16, in LDS.
+      // Rows r and r+1 of a lane (r even) are converted together.
+      uint16_t* act = reinterpret_cast<uint16_t*>(smem) + wave * (WM * kActPitch);
+      constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
       for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int jp = 0; jp < TN / 2; jp++)
 #pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const float hg = bf16_bits_to_float(float_to_bf16_rne(acc[i][2 * jp][r]));
-            const float hu = bf16_bits_to_float(float_to_bf16_rne(acc[i][2 * jp + 1][r]));
-            const float a = hg / (1.0f + expf(-hg)) * hu;
+          for (int r = 0; r < 16; r += 2) {
+            float a2[2];
+#pragma unroll
+            for (int d = 0; d < 2; d++) {
+              // h as stored in bf16, then silu(g) * u = g * u / (1 + 2^(-g log2 e))
+              const bf16x2 h = bf16x2{(__bf16)acc[i][2 * jp][r + d], (__bf16)acc[i][2 * jp + 1][r + d]};
+              const float hg = (float)h.x, hu = (float)h.y;
+              const float e = __builtin_amdgcn_exp2f(-hg * kLog2e);
+              a2[d] = hg * __builtin_amdgcn_rcpf(1.0f + e) * hu;
+            }
+            const uint32_t pair = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a2[0], (__bf16)a2[1]});
             const int row = i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            act[row * kActCols + jp * 32 + lr] = (uint16_t)float_to_bf16_rne(a);
+            act[row * kActPitch + jp * 32 + lr] = (uint16_t)(pair & 0xFFFFu);
+            act[(row + 1) * kActPitch + jp * 32 + lr] = (uint16_t)(pair >> 16);
           }
       __syncthreads();
-      // each lane quantises (row, 32-column block) items of its wave's act tile
+      // each lane quantises (row, 32-column block) items of its wave's act tile:
+      // amax over the bf16 magnitudes (their bit patterns order like the
+      // values), E8M0 scale = smallest power of two >= amax / 6, then E2M1
+      // codes of value / scale two at a time
       const int act_w = p.N / 2;
       for (int it = lane; it < WM * (TN / 2); it += 64) {
         const int row = it / (TN / 2), jp = it % (TN / 2);
         const int m = m0 + wm * WM + row;
         const int b = tn * (BN / 64) + wn * (TN / 2) + jp;  // act block index
         if (m >= nvalid_a || 32 * b >= act_w) continue;
-        float v[32];
-        const uint16_t* src = act + row * kActCols + jp * 32;
+        const uint4* src = reinterpret_cast<const uint4*>(act + row * kActPitch + jp * 32);
+        uint32_t w[16];
 #pragma unroll
-        for (int k = 0; k < 32; k++) v[k] = bf16_bits_to_float(src[k]);
+        for (int q = 0; q < 4; q++) {
+          const uint4 v = src[q];
+          w[4 * q] = v.x;
+          w[4 * q + 1] = v.y;
+          w[4 * q + 2] = v.z;
+          w[4 * q + 3] = v.w;
+        }
+        u16x2 mx = u16x2{0, 0};
+#pragma unroll
+        for (int q = 0; q < 16; q++)
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[q] & 0x7FFF7FFFu));
+        const float amax = bf16_bits_to_float(mx.x > mx.y ? mx.x : mx.y);
+        const uint32_t sc = e8m0_ceil(amax / 6.0f);
+        const float scale = __uint_as_float(sc == 0 ? 0x00400000u : sc << 23);  // 2^(sc - 127)
         uint32_t packed[4];
-        const uint32_t sc = mxfp4_block32(v, packed);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          uint32_t word = 0;
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q]), scale, 0);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 1]), scale, 1);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 2]), scale, 2);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 3]), scale, 3);
+          packed[q] = word;
+        }
         *reinterpret_cast<uint4*>(p.out_q + (int64_t)m * (act_w / 2) + b * 16) =
             make_uint4(packed[0], packed[1], packed[2], packed[3]);
         p.out_sf[(int64_t)m * (act_w / 32) + b] = (uint8_t)sc;
@@ -647,14 +702,14 @@ hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
 hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* a_rows, int64_t a_nrows,
                                 const int32_t* offsets, int64_t E, int64_t rows, const uint8_t* W,
                                 const uint8_t* Wsf, int64_t N, int64_t K, int epilogue, uint16_t* out,
-                                uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids, const float* topk_w,
+                                uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids,
                                 float* y_f32, hipStream_t stream) {
   Args a{};
   a.A = Aq; a.SFA = Asf; a.rows = (int)rows; a.a_rows = a_rows; a.a_nrows = (int)a_nrows;
   a.offsets = offsets; a.E = (int)E;
   a.W = W; a.WSF = Wsf; a.N = (int)N; a.K = (int)K; a.alpha = nullptr;
   a.out = out; a.out_q = out_q; a.out_sf = out_sf;
-  a.sorted_ids = sorted_ids; a.topk_w = topk_w; a.y_f32 = y_f32;
+  a.sorted_ids = sorted_ids; a.y_f32 = y_f32;
   constexpr int BM = 128, BN = 128;
   const int64_t max_items = ((rows + BM - 1) / BM + E) * ((N + BN - 1) / BN);
   switch (epilogue) {

@@ -52,12 +52,13 @@ hipError_t launch_mxfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
 hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* a_rows, int64_t a_nrows,
                                 const int32_t* offsets, int64_t E, int64_t rows, const uint8_t* W,
                                 const uint8_t* Wsf, int64_t N, int64_t K, int epilogue, uint16_t* out,
-                                uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids, const float* topk_w,
+                                uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids,
                                 float* y_f32, hipStream_t stream);
 
 // MoE routing prep and the combine's helpers.
 hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* offsets,
                            int32_t* sorted_ids, int32_t* sorted_tokens, hipStream_t stream);
-hipError_t launch_topk_sum(const float* y, uint16_t* out, int64_t T, int64_t topk, int64_t N, hipStream_t stream);
+hipError_t launch_topk_sum(const float* y, const float* w, uint16_t* out, int64_t T, int64_t topk, int64_t N,
+                           hipStream_t stream);
 
 }  // namespace bsfp4

@@ -7,8 +7,9 @@
 // reads the whole id list (L2-resident): it counts the ids below its expert
 // (its row offset), then stably compacts the flat indices equal to it with
 // block-wide prefix sums.  No atomics, no workspace, deterministic output.
-// The combine of the down projection sums each token's top-k weighted FP32
-// rows in slot order and rounds once to bf16 (topk_sum_bf16).
+// The combine of the down projection sums each token's top-k FP32 rows, each
+// times its routing weight, in slot order and rounds once to bf16
+// (topk_sum_bf16).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -91,23 +92,29 @@ __global__ void __launch_bounds__(kPrepThreads)
   }
 }
 
-// out[t, n] = bf16(sum_{j < topk} y[t*topk + j, n]), summed in slot order.
-// Each thread produces 4 consecutive columns (128-bit loads of each slot row).
+// out[t, n] = bf16(sum_{j < topk} w[t*topk + j] * y[t*topk + j, n]): each
+// product rounded to FP32, summed in slot order.  Each thread produces 4
+// consecutive columns (128-bit loads of each slot row).
 __global__ void __launch_bounds__(256)
-    topk_sum_bf16(const float* __restrict__ y, uint16_t* __restrict__ out, int64_t T, int topk, int N) {
+    topk_sum_bf16(const float* __restrict__ y, const float* __restrict__ w, uint16_t* __restrict__ out,
+                  int64_t T, int topk, int N) {
   const int64_t quads = T * (int64_t)(N / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
     const int64_t t = q / (N / 4);
     const int n = (int)(q - t * (N / 4)) * 4;
     const float* src = y + (t * topk) * (int64_t)N + n;
-    float4 s = *reinterpret_cast<const float4*>(src);
+    const float* wt = w + t * topk;
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float w0 = wt[0];
+    float4 s = make_float4(w0 * v0.x, w0 * v0.y, w0 * v0.z, w0 * v0.w);
     for (int j = 1; j < topk; j++) {
       const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)j * N);
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+      const float wj = wt[j];
+      s.x += wj * v.x;
+      s.y += wj * v.y;
+      s.z += wj * v.z;
+      s.w += wj * v.w;
     }
     *reinterpret_cast<uint2*>(out + t * N + n) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
   }
@@ -122,11 +129,12 @@ hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int
   return hipGetLastError();
 }
 
-hipError_t launch_topk_sum(const float* y, uint16_t* out, int64_t T, int64_t topk, int64_t N, hipStream_t stream) {
+hipError_t launch_topk_sum(const float* y, const float* w, uint16_t* out, int64_t T, int64_t topk, int64_t N,
+                           hipStream_t stream) {
   const int64_t quads = T * (N / 4);
   const int64_t want = (quads + 255) / 256;
   const unsigned grid = (unsigned)(want < 1 ? 1 : (want > 16384 ? 16384 : want));
-  topk_sum_bf16<<<grid, 256, 0, stream>>>(y, out, T, (int)topk, (int)N);
+  topk_sum_bf16<<<grid, 256, 0, stream>>>(y, w, out, T, (int)topk, (int)N);
   return hipGetLastError();
 }
 
