@@ -200,10 +200,11 @@ BSFP4_API bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t 
  *         `silu_and_mul_scaled_fp4_experts_quant` pattern of the vLLM `sm103`
  *         branch comparison page, `csrc/ops.h`, in its MXFP4 form)
  *     BSFP4_MOE_WEIGHTED_COMBINE: ep.out = bf16 [T, N] with
- *         out[t] = bf16(sum_j w[t,j] * Y[row(t,j)]): each row's product with
- *         its routing weight is kept in FP32 (workspace, rows*N*4 bytes) and
- *         the top-k rows of a token are summed in slot order (deterministic);
- *         uses ep.sorted_ids, ep.topk_weights [T*topk], ep.num_tokens, ep.topk
+ *         out[t] = bf16(sum_j w[t,j] * Y[row(t,j)]): each GEMM row is kept in
+ *         FP32 (workspace, rows*N*4 bytes), then a token's top-k rows, each
+ *         times its routing weight (FP32 product), are summed in slot order
+ *         (deterministic); uses ep.sorted_ids, ep.topk_weights [T*topk],
+ *         ep.num_tokens, ep.topk
  *   ws               device workspace of
  *                    mxfp4_moe_grouped_gemm_workspace_size(...) bytes
  * ------------------------------------------------------------------------- */
