@@ -201,7 +201,6 @@ struct Args {
 constexpr int kMaxGroups = (int)kMaxExperts;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Workgroups per CU the register budget is sized for: small tiles keep two
 // resident so that one's loads overlap the other's MFMAs.
@@ -225,15 +224,13 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
   constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
+  // SILU takes the B fragment as the MFMA's first operand, so that a lane's
+  // accumulators run along a row (the act block of a row sits in two lanes);
+  // STORE and COMBINE keep A first: a lane holds one column of 16 rows and each
+  // store instruction writes 128 contiguous bytes of two rows.
+  constexpr bool kSwap = EPI == kEpiSilu;
   constexpr int kSlots = kDMA ? kRing : 2;
-  // SILU: each wave stages its WM x kActCols bf16 act tile in LDS with a row
-  // pitch of kActCols + 8 elements (an odd number of 16-byte chunks), so that
-  // the quantiser's 128-bit row reads by consecutive lanes are conflict-free
-  constexpr int kActCols = (TN / 2) * 32;
-  constexpr int kActPitch = kActCols + 8;
-  constexpr int kActBytes = EPI == kEpiSilu ? (NT / 64) * WM * kActPitch * 2 : 0;
-  constexpr int kSmem = kSlots * kStage > kActBytes ? kSlots * kStage : kActBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int row_f[EPI == kEpiCombine ? BM : 1];
   __shared__ int wave_sum[NT / 64];
@@ -467,11 +464,15 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   #pragma unroll
             for (int jn = 0; jn < TN; jn++) {
               if (j == 0)
-                acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0,
-                                                                             (int)xa4[i], 0, (int)xb4[jn]);
+                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fb[jn], fa, acc[i][jn], 4, 4, 0, (int)xb4[jn], 0, (int)xa4[i])
+                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fa, fb[jn], acc[i][jn], 4, 4, 0, (int)xa4[i], 0, (int)xb4[jn]);
               else
-                acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 2,
-                                                                             (int)xa4[i], 2, (int)xb4[jn]);
+                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fb[jn], fa, acc[i][jn], 4, 4, 2, (int)xb4[jn], 2, (int)xa4[i])
+                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fa, fb[jn], acc[i][jn], 4, 4, 2, (int)xa4[i], 2, (int)xb4[jn]);
             }
           }
         }
@@ -517,8 +518,10 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
             const int xa = sa[r * kRowScales + c];
   #pragma unroll
             for (int jn = 0; jn < TN; jn++)
-              acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0, xa,
-                                                                           0, xb[jn]);
+              acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jn], fa, acc[i][jn], 4, 4, 0,
+                                                                                   xb[jn], 0, xa)
+                                 : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0,
+                                                                                   xa, 0, xb[jn]);
           }
         }
         if (more) {
@@ -531,8 +534,10 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   
     }
 
-    // ---- epilogues.  acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) + 4g + r%4,
-    //      tile column wn*WN + 32jn + lr.
+    // ---- epilogues.  STORE / COMBINE (A first): acc[i][jn][r] = tile row
+    //      wm*WM + 32i + 8(r/4) + 4g + r%4, tile column wn*WN + 32jn + lr.
+    //      SILU (B first): acc[i][jn][r] = tile row wm*WM + 32i + lr, tile
+    //      column wn*WN + 32jn + 8(r/4) + 4g + r%4.
     if constexpr (EPI == kEpiStore) {
 #pragma unroll
       for (int i = 0; i < TM; i++)
@@ -567,71 +572,54 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
         }
       }
     } else {
-      // SILU: act tile of this wave = WM rows x kActCols columns, bf16, in LDS.
-      // Rows r and r+1 of a lane (r even) are converted together.
-      uint16_t* act = reinterpret_cast<uint16_t*>(smem) + wave * (WM * kActPitch);
+      // SILU: gate tile 2jp and up tile 2jp+1 hold the same act columns, so a
+      // lane has act values 8q + 4g + t (q, t < 4) of act block
+      // b = tn*(BN/64) + wn*(TN/2) + jp of row m, and lane l ^ 32 the other 16.
+      // act = bf16(silu(h_g) * h_u) from the bf16-rounded h (SiLU with the
+      // hardware exp2 and reciprocal); the block's amax is shared between the
+      // two lanes, E8M0 scale = smallest power of two >= amax / 6, E2M1 codes of
+      // value / scale two at a time; each lane assembles 8 of the block's 16
+      // code bytes with its partner's help and stores them.
       constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-      for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int jp = 0; jp < TN / 2; jp++)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float a2[2];
-#pragma unroll
-            for (int d = 0; d < 2; d++) {
-              // h as stored in bf16, then silu(g) * u = g * u / (1 + 2^(-g log2 e))
-              const bf16x2 h = bf16x2{(__bf16)acc[i][2 * jp][r + d], (__bf16)acc[i][2 * jp + 1][r + d]};
-              const float hg = (float)h.x, hu = (float)h.y;
-              const float e = __builtin_amdgcn_exp2f(-hg * kLog2e);
-              a2[d] = hg * __builtin_amdgcn_rcpf(1.0f + e) * hu;
-            }
-            const uint32_t pair = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a2[0], (__bf16)a2[1]});
-            const int row = i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            act[row * kActPitch + jp * 32 + lr] = (uint16_t)(pair & 0xFFFFu);
-            act[(row + 1) * kActPitch + jp * 32 + lr] = (uint16_t)(pair >> 16);
-          }
-      __syncthreads();
-      // each lane quantises (row, 32-column block) items of its wave's act tile:
-      // amax over the bf16 magnitudes (their bit patterns order like the
-      // values), E8M0 scale = smallest power of two >= amax / 6, then E2M1
-      // codes of value / scale two at a time
       const int act_w = p.N / 2;
-      for (int it = lane; it < WM * (TN / 2); it += 64) {
-        const int row = it / (TN / 2), jp = it % (TN / 2);
-        const int m = m0 + wm * WM + row;
-        const int b = tn * (BN / 64) + wn * (TN / 2) + jp;  // act block index
-        if (m >= nvalid_a || 32 * b >= act_w) continue;
-        const uint4* src = reinterpret_cast<const uint4*>(act + row * kActPitch + jp * 32);
-        uint32_t w[16];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const uint4 v = src[q];
-          w[4 * q] = v.x;
-          w[4 * q + 1] = v.y;
-          w[4 * q + 2] = v.z;
-          w[4 * q + 3] = v.w;
+      for (int i = 0; i < TM; i++) {
+        const int m = m0 + wm * WM + i * 32 + lr;
+#pragma unroll
+        for (int jp = 0; jp < TN / 2; jp++) {
+          const int b = tn * (BN / 64) + wn * (TN / 2) + jp;  // act block index
+          if (m >= nvalid_a || 32 * b >= act_w) continue;      // same for lanes l and l ^ 32
+          float a[16];
+          float amax = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const bf16x2 h = bf16x2{(__bf16)acc[i][2 * jp][r], (__bf16)acc[i][2 * jp + 1][r]};
+            const float hg = (float)h.x, hu = (float)h.y;
+            const float e = __builtin_amdgcn_exp2f(-hg * kLog2e);
+            a[r] = (float)(__bf16)(hg * __builtin_amdgcn_rcpf(1.0f + e) * hu);
+            amax = fmaxf(amax, fabsf(a[r]));
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          const uint32_t sc = e8m0_ceil(amax / 6.0f);
+          const float scale = __uint_as_float(sc == 0 ? 0x00400000u : sc << 23);  // 2^(sc - 127)
+          // piece q: codes of columns 8q + 4g .. +3 (two bytes, first column in the low nibble)
+          uint32_t piece[4];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            uint32_t w2 = 0;
+            w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, a[4 * q], a[4 * q + 1], scale, 0);
+            w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, a[4 * q + 2], a[4 * q + 3], scale, 1);
+            piece[q] = w2 & 0xFFFFu;
+          }
+          // block dword q = piece q of lane g = 0 | piece q of lane g = 1 << 16;
+          // lane g = 0 writes dwords 0, 1 and lane g = 1 dwords 2, 3
+          const uint32_t give = g == 0 ? (piece[2] | (piece[3] << 16)) : (piece[0] | (piece[1] << 16));
+          const uint32_t got = (uint32_t)__shfl_xor((int)give, 32, 64);
+          const uint2 out = g == 0 ? make_uint2(piece[0] | ((got & 0xFFFFu) << 16), piece[1] | (got & 0xFFFF0000u))
+                                   : make_uint2((got & 0xFFFFu) | (piece[2] << 16), (got >> 16) | (piece[3] << 16));
+          *reinterpret_cast<uint2*>(p.out_q + (int64_t)m * (act_w / 2) + b * 16 + 8 * g) = out;
+          if (g == 0) p.out_sf[(int64_t)m * (act_w / 32) + b] = (uint8_t)sc;
         }
-        u16x2 mx = u16x2{0, 0};
-#pragma unroll
-        for (int q = 0; q < 16; q++)
-          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[q] & 0x7FFF7FFFu));
-        const float amax = bf16_bits_to_float(mx.x > mx.y ? mx.x : mx.y);
-        const uint32_t sc = e8m0_ceil(amax / 6.0f);
-        const float scale = __uint_as_float(sc == 0 ? 0x00400000u : sc << 23);  // 2^(sc - 127)
-        uint32_t packed[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          uint32_t word = 0;
-          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q]), scale, 0);
-          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 1]), scale, 1);
-          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 2]), scale, 2);
-          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, __builtin_bit_cast(bf16x2, w[4 * q + 3]), scale, 3);
-          packed[q] = word;
-        }
-        *reinterpret_cast<uint4*>(p.out_q + (int64_t)m * (act_w / 2) + b * 16) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        p.out_sf[(int64_t)m * (act_w / 32) + b] = (uint8_t)sc;
       }
     }
     __syncthreads();  // LDS is reused by the next work item
