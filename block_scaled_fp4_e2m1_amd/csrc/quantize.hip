@@ -13,7 +13,9 @@
 // Each step is one correctly rounded binary32 operation (the library is built
 // with -ffp-contract=off and correctly rounded division), so the output bytes
 // are a deterministic function of the input: the kernel is bit-exact by
-// construction, not approximately right.
+// construction, not approximately right.  The E2M1 rounding of a pair of
+// values is one v_cvt_scalef32_pk_fp4_* instruction (nearest-even, saturating
+// at 6, sign kept; see e2m1x2_* in quant_device.h).
 //
 // Mapping: one thread quantises one block (16 or 32 elements = 32 or 64
 // bytes of bf16, read with 128-bit loads); consecutive lanes take consecutive
@@ -78,12 +80,24 @@ __global__ void __launch_bounds__(256)
       inv = e8m0_inverse(scode);
     }
     uint32_t packed[BLK / 8];
+    if constexpr (kNV) {
+      // codes of fl32(v * inv)
 #pragma unroll
-    for (int j = 0; j < BLK / 8; j++) {
-      uint32_t word = 0;
+      for (int j = 0; j < BLK / 8; j++) {
+        uint32_t word = 0;
 #pragma unroll
-      for (int t = 0; t < 8; t++) word |= e2m1_rne(v[8 * j + t] * inv) << (4 * t);
-      packed[j] = word;
+        for (int t = 0; t < 4; t++) word = e2m1x2_f32(word, v[8 * j + 2 * t] * inv, v[8 * j + 2 * t + 1] * inv, t);
+        packed[j] = word;
+      }
+    } else {
+      // codes of v * 2^(127 - scode), i.e. of v / 2^(scode - 127) (exact)
+#pragma unroll
+      for (int j = 0; j < BLK / 8; j++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int t = 0; t < 4; t++) word = e2m1x2_bf16_pow2(word, w[4 * j + t], scode, t);
+        packed[j] = word;
+      }
     }
     uint8_t* qdst = q + r * (K / 2) + b * (BLK / 2);
     if constexpr (kNV) {
