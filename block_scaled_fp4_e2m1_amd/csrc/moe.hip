@@ -6,7 +6,7 @@
 // `sm103` branch comparison page, `csrc/ops.h`).  One workgroup per expert
 // reads the whole id list (L2-resident): it counts the ids below its expert
 // (its row offset), then stably compacts the flat indices equal to it with
-// block-wide prefix sums.  No atomics, no workspace, deterministic output.
+// per-wave ballots.  No atomics, no workspace, deterministic output.
 // The combine of the down projection sums each token's top-k FP32 rows, each
 // times its routing weight, in slot order and rounds once to bf16
 // (topk_sum_bf16).
@@ -18,77 +18,113 @@ namespace {
 
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / 64;
+constexpr int kPrepStep = 256;  // ids per wave step: 64 lanes x 4 consecutive ids
+constexpr int kPastEnd = 0x7FFFFFFF;  // id value for positions past a segment (matches no expert)
 
-// Exclusive prefix of v over the workgroup (thread order) and the total.
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  if (lane == 63) sh[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kPrepWaves; w++) {
-    const int sw = sh[w];
-    base += (w < wave) ? sw : 0;
-    total += sw;
-  }
-  __syncthreads();
-  return base + incl - v;
-}
-
-// One workgroup per expert e.  Pass 1 counts ids below e (the row offset of e)
-// and ids equal to e; pass 2 walks the ids in rounds of 4 consecutive ids per
-// thread (coalesced 128-bit loads) and writes the flat index of every id equal
-// to e at offset + (matches before it), which keeps the original order.
+// One workgroup per expert e.  The ids are cut into one contiguous segment per
+// wave (a multiple of kPrepStep long).  Pass 1: each wave counts the ids below
+// e and equal to e in its segment; the per-wave counts give the expert's row
+// offset (all ids below e) and each wave's first output row.  Pass 2: each
+// wave walks its segment in order, 4 consecutive ids per lane, and writes the
+// flat index of every id equal to e at its rank (ballots of the matches), which
+// keeps the original order.  No atomics, no block-wide barrier in the loops.
 __global__ void __launch_bounds__(kPrepThreads)
     moe_prep_kernel(const int32_t* __restrict__ ids, int n, int topk, int E, int32_t* __restrict__ offsets,
                     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_tokens) {
-  __shared__ int sh[kPrepWaves];
+  __shared__ int w_below[kPrepWaves], w_mine[kPrepWaves];
   const int e = blockIdx.x;
-  const int nvec = n / 4;
-  const int4* ids4 = reinterpret_cast<const int4*>(ids);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = (n + kPrepWaves * kPrepStep - 1) / (kPrepWaves * kPrepStep) * kPrepStep;
+  const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
+  const int steps = (s1 - s0 + kPrepStep - 1) / kPrepStep;  // same for every lane of the wave
+  const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15) == 0;
+  auto load4 = [&](int base, int (&v)[4]) {
+    if (vec && base + 3 < s1) {
+      const int4 t = *reinterpret_cast<const int4*>(ids + base);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] = base + j < s1 ? ids[base + j] : kPastEnd;
+    }
+  };
+
+  // ids are read kChunk steps at a time (independent loads in flight
+  // together); segments of at most kChunk steps stay in registers for pass 2
+  constexpr int kChunk = 8;
+  int v[kChunk][4];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < kChunk; u++) {
+      if (k0 + u < steps) {
+        load4(s0 + (k0 + u) * kPrepStep + 4 * lane, v[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++) v[u][j] = kPastEnd;
+      }
+    }
+  };
+
   int below = 0, mine = 0;
-  for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
-    const int4 v = ids4[i];
-    below += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
-    mine += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  for (int k0 = 0; k0 < steps; k0 += kChunk) {
+    load_chunk(k0);
+#pragma unroll
+    for (int u = 0; u < kChunk; u++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        below += v[u][j] < e;
+        mine += v[u][j] == e;
+      }
   }
-  for (int i = nvec * 4 + threadIdx.x; i < n; i += kPrepThreads) {
-    below += ids[i] < e;
-    mine += ids[i] == e;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    below += __shfl_xor(below, o, 64);
+    mine += __shfl_xor(mine, o, 64);
   }
-  int total_below, total_mine;
-  (void)block_excl_scan(below, sh, total_below);
-  (void)block_excl_scan(mine, sh, total_mine);
+  if (lane == 0) {
+    w_below[wave] = below;
+    w_mine[wave] = mine;
+  }
+  __syncthreads();
+  int total_below = 0, total_mine = 0, base = 0;
+#pragma unroll
+  for (int w = 0; w < kPrepWaves; w++) {
+    total_below += w_below[w];
+    total_mine += w_mine[w];
+    base += w < wave ? w_mine[w] : 0;
+  }
   if (threadIdx.x == 0) {
     offsets[e] = total_below;
     if (e == E - 1) offsets[E] = total_below + total_mine;
   }
-  int base = total_below;
-  const int rounds = (n + 4 * kPrepThreads - 1) / (4 * kPrepThreads);
-  for (int r = 0; r < rounds; r++) {
-    const int i0 = (r * kPrepThreads + threadIdx.x) * 4;  // first of this thread's 4 ids
-    int v[4];
+  if (w_mine[wave] == 0) return;
+
+  int pos = total_below + base;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int k0 = 0; k0 < steps; k0 += kChunk) {
+    if (steps > kChunk) load_chunk(k0);  // otherwise v still holds the only chunk
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = (i0 + j < n) ? ids[i0 + j] : -1;
-    const int cnt = (v[0] == e) + (v[1] == e) + (v[2] == e) + (v[3] == e);
-    int round_total;
-    int pos = base + block_excl_scan(cnt, sh, round_total);
+    for (int u = 0; u < kChunk; u++) {
+      if (k0 + u >= steps) break;
+      const int b0 = s0 + (k0 + u) * kPrepStep + 4 * lane;
+      uint64_t bal[4];
+      int before = 0, here = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (v[j] == e) {
-        sorted_ids[pos] = i0 + j;
-        if (sorted_tokens) sorted_tokens[pos] = (i0 + j) / topk;
-        pos++;
+      for (int j = 0; j < 4; j++) {
+        bal[j] = __ballot(v[u][j] == e);
+        before += __popcll(bal[j] & lt);
+        here += __popcll(bal[j]);
       }
+      int r = pos + before;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (v[u][j] == e) {
+          sorted_ids[r] = b0 + j;
+          if (sorted_tokens) sorted_tokens[r] = (b0 + j) / topk;
+          r++;
+        }
+      }
+      pos += here;
     }
-    base += round_total;
   }
 }
 
