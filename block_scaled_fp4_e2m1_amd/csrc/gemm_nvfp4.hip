@@ -528,6 +528,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
   // lane: output row m (its MFMA column), registers 4q..4q+3: columns n..n+3
   // (N % 4 == 0: the 4 columns are all in range or all out)
   const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  if (splits == 1) {
+    // bf16 tile through LDS (the stages are free after the K loop's last
+    // barrier): each lane writes its 4-column runs into a row-major tile,
+    // then every store instruction writes whole 16-byte-per-lane row segments
+    // (BN * 2 contiguous bytes per row) instead of 64 scattered 8-byte pieces
+    constexpr int kOutPitch = BN * 2 + 16;  // bytes per LDS row
+    static_assert(BM * kOutPitch <= 2 * kStage, "output tile fits in the stage buffers");
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+      const int r = wm * WM + i * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int c = wn * WN + j * 32 + 8 * q + 4 * g;
+          *reinterpret_cast<uint2*>(smem + r * kOutPitch + c * 2) =
+              make_uint2(pack_bf16x2(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1]),
+                         pack_bf16x2(alpha * acc[i][j][4 * q + 2], alpha * acc[i][j][4 * q + 3]));
+        }
+    }
+    __syncthreads();
+    constexpr int kChunksPerRow = BN / 8;  // 16-byte chunks (8 columns)
+    for (int idx = tid; idx < BM * kChunksPerRow; idx += NT) {
+      const int r = idx / kChunksPerRow, c = (idx % kChunksPerRow) * 8;
+      const int m = m0 + r, n = n0 + c;
+      if (m < M && n < N)
+        *reinterpret_cast<uint4*>(D + (int64_t)m * N + n) = *reinterpret_cast<const uint4*>(smem + r * kOutPitch + c * 2);
+    }
+    return;
+  }
   float* dst = part + (int64_t)split * M * N;
 #pragma unroll
   for (int i = 0; i < TM; i++) {
@@ -537,14 +567,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
-        const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (splits == 1) {
-          const uint2 o = make_uint2(pack_bf16x2(alpha * v0, alpha * v1), pack_bf16x2(alpha * v2, alpha * v3));
-          if (m < M && n < N) *reinterpret_cast<uint2*>(D + (int64_t)m * N + n) = o;
-        } else {
-          if (m < M && n < N) *reinterpret_cast<float4*>(dst + (int64_t)m * N + n) = make_float4(v0, v1, v2, v3);
-        }
+        if (m < M && n < N)
+          *reinterpret_cast<float4*>(dst + (int64_t)m * N + n) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
     }
   }
