@@ -224,11 +224,17 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   constexpr int kA = BM * kRowBytes, kB = BN * kRowBytes;
   constexpr int kStage = kA + kB + (BM + BN) * kRowScales;
   static_assert(EPI != kEpiSilu || TN % 2 == 0, "SILU needs gate/up column-tile pairs");
-  // SILU takes the B fragment as the MFMA's first operand, so that a lane's
-  // accumulators run along a row (the act block of a row sits in two lanes);
-  // STORE and COMBINE keep A first: a lane holds one column of 16 rows and each
-  // store instruction writes 128 contiguous bytes of two rows.
-  constexpr bool kSwap = EPI == kEpiSilu;
+  // With the B fragment as the MFMA's first operand a lane's accumulators run
+  // along a row (4 consecutive columns per register quad).  SILU needs that
+  // (the act block of a row sits in two lanes), and so does the LDS-staged
+  // output of the ring kernel (8- or 16-byte LDS writes).  The register-staged
+  // kernel stores STORE / COMBINE tiles directly and keeps A first: a lane
+  // holds one column of 16 rows and each store writes 128 contiguous bytes.
+  constexpr bool kSwap = EPI == kEpiSilu || kDMA;
+  // LDS-staged output tile (ring kernel): bf16 or FP32 rows padded by 16 bytes
+  constexpr int kOutElem = EPI == kEpiCombine ? 4 : 2;
+  constexpr int kOutPitch = BN * kOutElem + 16;
+  static_assert(!kDMA || EPI == kEpiSilu || BM * kOutPitch <= kRing * kStage, "output tile fits in the ring");
   constexpr int kSlots = kDMA ? kRing : 2;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
@@ -534,11 +540,52 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   
     }
 
-    // ---- epilogues.  STORE / COMBINE (A first): acc[i][jn][r] = tile row
-    //      wm*WM + 32i + 8(r/4) + 4g + r%4, tile column wn*WN + 32jn + lr.
-    //      SILU (B first): acc[i][jn][r] = tile row wm*WM + 32i + lr, tile
-    //      column wn*WN + 32jn + 8(r/4) + 4g + r%4.
-    if constexpr (EPI == kEpiStore) {
+    // ---- epilogues.  A first: acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) +
+    //      4g + r%4, tile column wn*WN + 32jn + lr.  B first: acc[i][jn][r] =
+    //      tile row wm*WM + 32i + lr, tile column wn*WN + 32jn + 8(r/4) + 4g + r%4.
+    if constexpr (kDMA && EPI != kEpiSilu) {
+      // the tile goes through LDS (the ring is free after the K loop's last
+      // barrier): each lane writes its 4-column runs, then each store writes
+      // 16 contiguous bytes per lane, whole row segments of BN columns
+      if constexpr (EPI == kEpiCombine) {
+        if (tid < BM) row_f[tid] = rf;
+      }
+#pragma unroll
+      for (int i = 0; i < TM; i++) {
+        const int r = wm * WM + i * 32 + lr;
+#pragma unroll
+        for (int jn = 0; jn < TN; jn++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int c = wn * WN + jn * 32 + 8 * q + 4 * g;
+            uint8_t* dst = smem + r * kOutPitch + c * kOutElem;
+            if constexpr (EPI == kEpiCombine)
+              *reinterpret_cast<float4*>(dst) =
+                  make_float4(acc[i][jn][4 * q], acc[i][jn][4 * q + 1], acc[i][jn][4 * q + 2], acc[i][jn][4 * q + 3]);
+            else
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(pack_bf16x2(alpha * acc[i][jn][4 * q], alpha * acc[i][jn][4 * q + 1]),
+                             pack_bf16x2(alpha * acc[i][jn][4 * q + 2], alpha * acc[i][jn][4 * q + 3]));
+          }
+      }
+      __syncthreads();
+      constexpr int kChunksPerRow = BN * kOutElem / 16;
+      for (int idx = tid; idx < BM * kChunksPerRow; idx += NT) {
+        const int r = idx / kChunksPerRow, cb = (idx % kChunksPerRow) * 16;  // byte offset in the row
+        const int n = tn * BN + cb / kOutElem;
+        if (n >= p.N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kOutPitch + cb);
+        if constexpr (EPI == kEpiCombine) {
+          // y[f] = row, f = flat (token, slot) index of the row; the weighted
+          // top-k sum is done afterwards in a fixed order (no atomics)
+          const int f = row_f[r];
+          if (f >= 0) *reinterpret_cast<uint4*>(p.y_f32 + (int64_t)f * p.N + n) = v;
+        } else {
+          const int m = m0 + r;
+          if (m < nvalid_a) *reinterpret_cast<uint4*>(p.out + (int64_t)m * p.N + n) = v;
+        }
+      }
+    } else if constexpr (EPI == kEpiStore) {
 #pragma unroll
       for (int i = 0; i < TM; i++)
 #pragma unroll
