@@ -558,19 +558,37 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1)
     }
     return;
   }
+  // FP32 partial tile of split `split`, through LDS in kPasses row bands of
+  // the same layout (16 bytes per lane per store, whole row segments)
+  constexpr int kPartPitch = BN * 4 + 16;
+  constexpr int kPasses = (BM * kPartPitch + 2 * kStage - 1) / (2 * kStage);
+  constexpr int kBandRows = BM / kPasses;
+  static_assert(kBandRows % 32 == 0 && kBandRows * kPartPitch <= 2 * kStage, "partial band fits in LDS");
   float* dst = part + (int64_t)split * M * N;
 #pragma unroll
-  for (int i = 0; i < TM; i++) {
-    const int m = m0 + wm * WM + i * 32 + lr;
+  for (int h = 0; h < kPasses; h++) {
+    if (h > 0) __syncthreads();  // the previous band has been stored
 #pragma unroll
-    for (int j = 0; j < TN; j++) {
+    for (int i = 0; i < TM; i++) {
+      const int r = wm * WM + i * 32;  // first row of the 32-row block (uniform)
+      if (r / kBandRows != h) continue;
+      const int rl = r - h * kBandRows + lr;
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * g;
-        if (m < M && n < N)
-          *reinterpret_cast<float4*>(dst + (int64_t)m * N + n) =
+      for (int j = 0; j < TN; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int c = wn * WN + j * 32 + 8 * q + 4 * g;
+          *reinterpret_cast<float4*>(smem + rl * kPartPitch + c * 4) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-      }
+        }
+    }
+    __syncthreads();
+    constexpr int kChunksPerRow = BN / 4;  // 16-byte chunks (4 columns)
+    for (int idx = tid; idx < kBandRows * kChunksPerRow; idx += NT) {
+      const int rl = idx / kChunksPerRow, c = (idx % kChunksPerRow) * 4;
+      const int m = m0 + h * kBandRows + rl, n = n0 + c;
+      if (m < M && n < N)
+        *reinterpret_cast<float4*>(dst + (int64_t)m * N + n) = *reinterpret_cast<const float4*>(smem + rl * kPartPitch + c * 4);
     }
   }
 }
