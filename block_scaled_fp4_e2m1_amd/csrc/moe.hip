@@ -18,67 +18,44 @@ namespace {
 
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / 64;
-constexpr int kPrepStep = 256;  // ids per wave step: 64 lanes x 4 consecutive ids
 constexpr int kPastEnd = 0x7FFFFFFF;  // id value for positions past a segment (matches no expert)
 
 // One workgroup per expert e.  The ids are cut into one contiguous segment per
-// wave (a multiple of kPrepStep long).  Pass 1: each wave counts the ids below
-// e and equal to e in its segment; the per-wave counts give the expert's row
-// offset (all ids below e) and each wave's first output row.  Pass 2: each
-// wave walks its segment in order, 4 consecutive ids per lane, and writes the
-// flat index of every id equal to e at its rank (ballots of the matches), which
-// keeps the original order.  No atomics, no block-wide barrier in the loops.
+// wave (a multiple of 64 long); the wave reads it 64 consecutive ids at a time,
+// one per lane.  Pass 1: counts of ids below e and equal to e from ballots
+// (wave-uniform scalars); the per-wave counts give the expert's row offset (all
+// ids below e) and each wave's first output row.  Pass 2: the wave walks its
+// segment in order and writes the flat index of every id equal to e at its
+// rank (ballot + lane prefix count), which keeps the original order.  No
+// atomics, no block-wide barrier in the loops; segments of up to kKeep steps
+// stay in registers between the passes.
 __global__ void __launch_bounds__(kPrepThreads)
     moe_prep_kernel(const int32_t* __restrict__ ids, int n, int topk, int E, int32_t* __restrict__ offsets,
                     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ sorted_tokens) {
+  constexpr int kKeep = 32;
   __shared__ int w_below[kPrepWaves], w_mine[kPrepWaves];
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = (n + kPrepWaves * kPrepStep - 1) / (kPrepWaves * kPrepStep) * kPrepStep;
+  const int seg = (n + kPrepWaves * 64 - 1) / (kPrepWaves * 64) * 64;
   const int s0 = min(n, wave * seg), s1 = min(n, s0 + seg);
-  const int steps = (s1 - s0 + kPrepStep - 1) / kPrepStep;  // same for every lane of the wave
-  const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15) == 0;
-  auto load4 = [&](int base, int (&v)[4]) {
-    if (vec && base + 3 < s1) {
-      const int4 t = *reinterpret_cast<const int4*>(ids + base);
-      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; j++) v[j] = base + j < s1 ? ids[base + j] : kPastEnd;
-    }
-  };
-
-  // ids are read kChunk steps at a time (independent loads in flight
-  // together); segments of at most kChunk steps stay in registers for pass 2
-  constexpr int kChunk = 8;
-  int v[kChunk][4];
+  const int steps = (s1 - s0 + 63) / 64;  // same for every lane of the wave
+  int v[kKeep];
   auto load_chunk = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < kChunk; u++) {
-      if (k0 + u < steps) {
-        load4(s0 + (k0 + u) * kPrepStep + 4 * lane, v[u]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; j++) v[u][j] = kPastEnd;
-      }
+    for (int u = 0; u < kKeep; u++) {
+      const int i = s0 + (k0 + u) * 64 + lane;
+      v[u] = (k0 + u < steps && i < s1) ? ids[i] : kPastEnd;
     }
   };
 
-  int below = 0, mine = 0;
-  for (int k0 = 0; k0 < steps; k0 += kChunk) {
+  int below = 0, mine = 0;  // wave-uniform
+  for (int k0 = 0; k0 < steps; k0 += kKeep) {
     load_chunk(k0);
 #pragma unroll
-    for (int u = 0; u < kChunk; u++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        below += v[u][j] < e;
-        mine += v[u][j] == e;
-      }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    below += __shfl_xor(below, o, 64);
-    mine += __shfl_xor(mine, o, 64);
+    for (int u = 0; u < kKeep; u++) {
+      below += __popcll(__ballot(v[u] < e));
+      mine += __popcll(__ballot(v[u] == e));
+    }
   }
   if (lane == 0) {
     w_below[wave] = below;
@@ -96,34 +73,32 @@ __global__ void __launch_bounds__(kPrepThreads)
     offsets[e] = total_below;
     if (e == E - 1) offsets[E] = total_below + total_mine;
   }
-  if (w_mine[wave] == 0) return;
+  if (mine == 0) return;
 
+  // token = flat / topk without a division: for topk > 1,
+  // q = umulhi(x, ceil(2^32 / topk)) is floor(x / topk) or one more for
+  // x < 2^31, fixed by one compare
+  const uint32_t magic = topk > 1 ? (uint32_t)((0xFFFFFFFFull + (uint64_t)topk) / (uint64_t)topk) : 0u;
+  auto token_of = [&](int x) {
+    if (topk == 1) return x;
+    const int q = (int)__umulhi((uint32_t)x, magic);
+    return q * topk > x ? q - 1 : q;
+  };
   int pos = total_below + base;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int k0 = 0; k0 < steps; k0 += kChunk) {
-    if (steps > kChunk) load_chunk(k0);  // otherwise v still holds the only chunk
+  for (int k0 = 0; k0 < steps; k0 += kKeep) {
+    if (steps > kKeep) load_chunk(k0);  // otherwise v still holds the only chunk
 #pragma unroll
-    for (int u = 0; u < kChunk; u++) {
-      if (k0 + u >= steps) break;
-      const int b0 = s0 + (k0 + u) * kPrepStep + 4 * lane;
-      uint64_t bal[4];
-      int before = 0, here = 0;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        bal[j] = __ballot(v[u][j] == e);
-        before += __popcll(bal[j] & lt);
-        here += __popcll(bal[j]);
+    for (int u = 0; u < kKeep; u++) {
+      const uint64_t bal = __ballot(v[u] == e);
+      if (bal == 0) continue;
+      if (v[u] == e) {
+        const int r = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        const int x = s0 + (k0 + u) * 64 + lane;
+        sorted_ids[r] = x;
+        if (sorted_tokens) sorted_tokens[r] = token_of(x);
       }
-      int r = pos + before;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        if (v[u][j] == e) {
-          sorted_ids[r] = b0 + j;
-          if (sorted_tokens) sorted_tokens[r] = (b0 + j) / topk;
-          r++;
-        }
-      }
-      pos += here;
+      pos += __popcll(bal);
     }
   }
 }
