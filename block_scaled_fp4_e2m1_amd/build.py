@@ -26,6 +26,7 @@ SOURCES = [
     "gemm_nvfp4.hip",
     "gemm_skinny.hip",
     "gemm_mxfp4.hip",
+    "gemm_w4a16.hip",
     "moe.hip",
 ]
 

@@ -34,4 +34,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return float_to_bf16_rne(lo) | (float_to_bf16_rne(hi) << 16);
 }
 
+// E4M3 scale code (magnitude bits) -> its value in binary32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Eight E2M1 values (one 32-bit word, first value in the low nibble) times the
+// binary32 block scale `s` -> eight bf16 values.  The products have at most 6
+// significant bits, so they are exact in binary32 and in bf16.
+__device__ __forceinline__ v8bf dq8_bf16(uint32_t word, float s) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    v2f f;
+    switch (j) {
+      case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+      case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+      case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+      default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+    }
+    // exact products: truncating to the upper 16 bits is the bf16 value
+    o[j] = (__float_as_uint(f.x * s) >> 16) | (__float_as_uint(f.y * s) & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 }  // namespace bsfp4

@@ -75,11 +75,6 @@ __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
   return __builtin_bit_cast(_Float16, bits) * (_Float16)256.0f;
 }
 
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
-}
 
 __device__ __forceinline__ v8h dq8_f16(uint32_t word, _Float16 s) {
   const v2h ss = {s, s};
@@ -93,22 +88,6 @@ __device__ __forceinline__ v8h dq8_f16(uint32_t word, _Float16 s) {
 }
 
 // Eight E2M1 values times an f32 scale -> eight bf16 (exact: <= 6 significant bits).
-__device__ __forceinline__ v8bf dq8_bf16(uint32_t word, float s) {
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    v2f f;
-    switch (j) {
-      case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
-      case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
-      case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
-      default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
-    }
-    // exact products: truncating to the upper 16 bits is the bf16 value
-    o[j] = (__float_as_uint(f.x * s) >> 16) | (__float_as_uint(f.y * s) & 0xFFFF0000u);
-  }
-  return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
-}
 
 // AKIND 0: activations are NVFP4 (codes + E4M3 scales), fp16 MFMA.
 // AKIND 1: activations are bf16, bf16 MFMA.

@@ -1,0 +1,282 @@
+// W4A16 GEMM for larger M on gfx950: D = bf16(alpha * A @ dec(B)^T) with A bf16
+// [M, K], B NVFP4 (E2M1 codes [N, K/2], one E4M3 scale per 16 K-elements
+// [N, K/16]) and alpha the tensor-wide weight scale applied to the FP32
+// accumulator: the dense W4A16 GEMM of the FlashInfer `mm_bf16_fp4` pages
+// ("feat: sm100 cute_dsl w4a16 gemm" and its follow-ups).  Rows up to 64 use
+// the weight-streaming kernels of gemm_skinny.hip.
+//
+// An E2M1 value times an E4M3 scale has at most 6 significant bits, so the
+// dequantised weights are exact in bf16 and v_mfma_f32_32x32x16_bf16 forms the
+// exact products with FP32 accumulation.
+//
+// One workgroup = 8 waves (2 x 4) on a 256 x 256 output tile, 128 x 64 per
+// wave; K in stages of 64 values.  A 3-slot LDS ring is filled by
+// direct-to-LDS buffer loads issued by 4 loader waves: per stage the A rows
+// (128 bytes of bf16, their 16-byte chunks XOR-swizzled by row so that the
+// fragment reads are conflict-free), the B code rows (32 bytes, chunk order
+// swapped on alternate 8-row blocks) and the B scale bytes (4 per row).  Each
+// wave reads its A fragments as bf16 and dequantises its B fragments in
+// registers.  B is the MFMA's first operand, so a lane ends with runs of 4
+// consecutive output columns of one row; the tile leaves through LDS in row
+// bands (bf16 output, or FP32 partials of a K split that splitk_reduce sums in
+// split order).
+#include <cstdlib>
+#include <type_traits>
+
+#include "device_common.h"
+#include "launchers.h"
+#include "lds_dma.h"
+
+namespace bsfp4 {
+namespace {
+
+constexpr int kBM = 256, kBN = 256;
+constexpr int kWGM = 2, kWGN = 4;
+constexpr int kNT = 64 * kWGM * kWGN;
+constexpr int kWM = kBM / kWGM, kWN = kBN / kWGN;
+constexpr int kTM = kWM / 32, kTN = kWN / 32;
+constexpr int kSK = 64;                    // K values per stage
+constexpr int kARow = kSK * 2;             // bytes of one A row per stage (bf16)
+constexpr int kBRow = kSK / 2;             // bytes of one B code row per stage
+constexpr int kSRow = kSK / 16;            // scale bytes of one B row per stage
+constexpr int kA = kBM * kARow;
+constexpr int kBq = kBN * kBRow;
+constexpr int kBs = kBN * kSRow;
+constexpr int kStage = kA + kBq + kBs;
+constexpr int kRing = 3;
+constexpr int kLoad = 4;                   // loader waves
+constexpr int kAI = kA / 1024 / kLoad;     // A loads (1 KB each) per loader wave per stage
+constexpr int kBqI = kBq / 1024 / kLoad;   // B code loads (1 KB each)
+constexpr int kBsI = kBs / 256 / kLoad;    // B scale loads (256 B each)
+constexpr int kL = kAI + kBqI + kBsI;
+static_assert(kAI * kLoad * 1024 == kA && kBqI * kLoad * 1024 == kBq && kBsI * kLoad * 256 == kBs,
+              "loads cover the stage exactly");
+static_assert(kRing * kStage <= 160 * 1024, "ring fits in LDS");
+
+// 16-byte chunk positions: A rows hold 8 chunks, B code rows 2
+__device__ __forceinline__ int swz_a(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+__device__ __forceinline__ int swz_b(int r, int c) { return c ^ ((r >> 3) & 1); }
+
+__global__ void __launch_bounds__(kNT, 1)
+    w4a16_tiled(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
+                const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N, int K, int tiles_m,
+                int tiles_n, int splits, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRing * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWGN, wn = wave % kWGN;
+  const int lr = lane & 31, g = lane >> 5;
+
+  // work item -> (tile, split): consecutive items on one XCD, tiles in bands of
+  // 4 tile rows so that an XCD's items share few A and B panels
+  const int items = tiles_m * tiles_n * splits;
+  int item = blockIdx.x;
+  if (items % 8 == 0) item = (int)(blockIdx.x % 8) * (items / 8) + (int)(blockIdx.x / 8);
+  const int split = item % splits;
+  const int tile = item / splits;
+  const int band_tiles = 4 * tiles_n;
+  const int band = tile / band_tiles, in_band = tile % band_tiles;
+  const int band_rows = min(4, tiles_m - band * 4);
+  const int m0 = (band * 4 + in_band % band_rows) * kBM;
+  const int n0 = (in_band / band_rows) * kBN;
+  const int total = K / kSK;
+  const int sb = (int)((int64_t)total * split / splits);
+  const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
+
+  v16f acc[kTM][kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; i++)
+#pragma unroll
+    for (int j = 0; j < kTN; j++) acc[i][j] = v16f{};
+
+  // ---- per-lane load offsets (the stage's K offset goes in the SGPR offset)
+  const bool loader = wave < kLoad;
+  const int lw = loader ? wave : 0;
+  const v4u32 ra = make_rsrc4(A, (int64_t)M * K * 2);
+  const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
+  const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
+  uint32_t va[kAI], vq[kBqI], vs[kBsI];
+#pragma unroll
+  for (int j = 0; j < kAI; j++) {
+    const int q = lw * kAI + j;
+    const int row = q * 8 + (lane >> 3);
+    const int c = swz_a(row, lane & 7);  // swz_a is its own inverse
+    va[j] = m0 + row < M ? (uint32_t)((m0 + row) * (K * 2) + c * 16) : kBufOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < kBqI; j++) {
+    const int q = lw * kBqI + j;
+    const int row = q * 32 + (lane >> 1);
+    const int c = swz_b(row, lane & 1);
+    vq[j] = n0 + row < N ? (uint32_t)((n0 + row) * (K / 2) + c * 16) : kBufOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < kBsI; j++) {
+    const int row = (lw * kBsI + j) * 64 + lane;
+    vs[j] = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16)) : kBufOOB;
+  }
+  const uint32_t lds0 = lds_offset(smem);
+  auto issue = [&](int st) {
+    const int k0 = (sb + st) * kSK;
+    const uint32_t base = lds0 + (uint32_t)((st % kRing) * kStage);
+#pragma unroll
+    for (int j = 0; j < kAI; j++)
+      buf_lds16(uniform4(ra), va[j], (uint32_t)(k0 * 2),
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + (wave * kAI + j) * 1024)));
+#pragma unroll
+    for (int j = 0; j < kBqI; j++)
+      buf_lds16(uniform4(rq), vq[j], (uint32_t)(k0 / 2),
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + kA + (wave * kBqI + j) * 1024)));
+#pragma unroll
+    for (int j = 0; j < kBsI; j++)
+      buf_lds4(uniform4(rs), vs[j], (uint32_t)(k0 / 16),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + kA + kBq + (wave * kBsI + j) * 256)));
+  };
+
+  if (nst > 0) {
+    if (loader)
+      for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
+    for (int s = 0; s < nst; s++) {
+      if (loader) {
+        if (s + 1 < nst) wait_vmcnt<kL>();  // kRing - 1 = 2 stages were in flight
+        else wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
+      if (loader && s + kRing - 1 < nst) issue(s + kRing - 1);
+      const uint8_t* st = smem + (s % kRing) * kStage;
+      const uint8_t* sa = st;
+      const uint8_t* sq = st + kA;
+      const uint8_t* ss = st + kA + kBq;
+      // this lane's B rows: all 64 code values (two chunks) and 4 scale bytes
+      uint32_t bw[kTN][8], bsc[kTN];
+#pragma unroll
+      for (int jn = 0; jn < kTN; jn++) {
+        const int r = wn * kWN + jn * 32 + lr;
+        const uint4 c0 = *reinterpret_cast<const uint4*>(sq + r * kBRow + swz_b(r, 0) * 16);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(sq + r * kBRow + swz_b(r, 1) * 16);
+        bw[jn][0] = c0.x; bw[jn][1] = c0.y; bw[jn][2] = c0.z; bw[jn][3] = c0.w;
+        bw[jn][4] = c1.x; bw[jn][5] = c1.y; bw[jn][6] = c1.z; bw[jn][7] = c1.w;
+        bsc[jn] = *reinterpret_cast<const uint32_t*>(ss + r * kSRow);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kSK / 16; kk++) {
+        // K values 16kk + 8g .. +7 of the stage: code word 2kk + g, scale byte kk
+        v8bf fb[kTN];
+#pragma unroll
+        for (int jn = 0; jn < kTN; jn++)
+          fb[jn] = dq8_bf16(bw[jn][2 * kk + g], e4m3_to_f32((bsc[jn] >> (8 * kk)) & 0xFFu));
+#pragma unroll
+        for (int i = 0; i < kTM; i++) {
+          const int r = wm * kWM + i * 32 + lr;
+          const v8bf fa = *reinterpret_cast<const v8bf*>(sa + r * kARow + swz_a(r, 2 * kk + g) * 16);
+#pragma unroll
+          for (int jn = 0; jn < kTN; jn++)
+            acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[jn], fa, acc[i][jn], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the ring is free: the tile leaves through it
+
+  // acc[i][jn][4q + t] = row wm*WM + 32i + lr, column wn*WN + 32jn + 8q + 4g + t
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  auto out_bands = [&](auto elem) {
+    constexpr int kE = decltype(elem)::value;  // bytes per output element
+    constexpr int kPitch = kBN * kE + 16;
+    constexpr int kRingBytes = kRing * kStage;
+    constexpr int kPasses = kBM * kPitch <= kRingBytes         ? 1
+                            : (kBM / 2) * kPitch <= kRingBytes ? 2
+                            : (kBM / 4) * kPitch <= kRingBytes ? 4
+                                                               : 8;
+    constexpr int kBand = kBM / kPasses;
+    static_assert(kBand % 32 == 0 && kBand * kPitch <= kRing * kStage, "band fits in the ring");
+    float* dst_part = part + (int64_t)split * M * N;
+#pragma unroll
+    for (int h = 0; h < kPasses; h++) {
+      if (h > 0) __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kTM; i++) {
+        const int r = wm * kWM + i * 32;
+        if (r / kBand != h) continue;
+        uint8_t* row = smem + (r - h * kBand + lr) * kPitch;
+#pragma unroll
+        for (int jn = 0; jn < kTN; jn++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int c = wn * kWN + jn * 32 + 8 * q + 4 * g;
+            if constexpr (kE == 4)
+              *reinterpret_cast<float4*>(row + c * 4) =
+                  make_float4(acc[i][jn][4 * q], acc[i][jn][4 * q + 1], acc[i][jn][4 * q + 2], acc[i][jn][4 * q + 3]);
+            else
+              *reinterpret_cast<uint2*>(row + c * 2) =
+                  make_uint2(pack_bf16x2(alpha * acc[i][jn][4 * q], alpha * acc[i][jn][4 * q + 1]),
+                             pack_bf16x2(alpha * acc[i][jn][4 * q + 2], alpha * acc[i][jn][4 * q + 3]));
+          }
+      }
+      __syncthreads();
+      constexpr int kChunks = kBN * kE / 16;  // 16-byte chunks per row
+      for (int idx = tid; idx < kBand * kChunks; idx += kNT) {
+        const int rl = idx / kChunks, cb = (idx % kChunks) * 16;
+        const int m = m0 + h * kBand + rl, n = n0 + cb / kE;
+        if (m >= M || n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + rl * kPitch + cb);
+        if constexpr (kE == 4)
+          *reinterpret_cast<uint4*>(dst_part + (int64_t)m * N + n) = v;
+        else
+          *reinterpret_cast<uint4*>(D + (int64_t)m * N + n) = v;
+      }
+    }
+  };
+  if (splits == 1)
+    out_bands(std::integral_constant<int, 2>{});
+  else
+    out_bands(std::integral_constant<int, 4>{});
+}
+
+int w4a16_splits(int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int64_t stages = K / kSK;
+  int s = 1;
+  while (s < 8 && tiles * (s + 1) <= cus && stages / (s + 1) >= 8) s++;
+  return s;
+}
+
+int cus_of_device() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    n = (hipGetDevice(&dev) == hipSuccess &&
+         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            ? v
+            : 256;
+  }
+  return n;
+}
+
+}  // namespace
+
+bool w4a16_tiled_ok(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 31;
+  return M > kSkinnyMaxM && K % kSK == 0 && M * K * 2 < lim && N * (K / 2) < lim;
+}
+
+size_t w4a16_tiled_workspace(int64_t M, int64_t N, int64_t K) {
+  const int s = w4a16_splits(M, N, K, cus_of_device());
+  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                              uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
+                              hipStream_t stream) {
+  int splits = w4a16_splits(M, N, K, cus_of_device());
+  if (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))) splits = 1;
+  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
+  const unsigned grid = (unsigned)(tiles_m * tiles_n * splits);
+  w4a16_tiled<<<grid, kNT, 0, stream>>>(A, B, SFB, alpha, D, (int)M, (int)N, (int)K, tiles_m, tiles_n, splits,
+                                        part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(part, splits, alpha, D, M * N, stream);
+}
+
+}  // namespace bsfp4

@@ -38,6 +38,12 @@ size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations);
 
 // D = bf16(alpha * sum_s part[s]) over `splits` FP32 partials of MN elements
 // (MN % 4 == 0), summed in split order.
+// Tiled W4A16 for M > kSkinnyMaxM (K % 64 == 0, operands below 2^31 bytes).
+bool w4a16_tiled_ok(int64_t M, int64_t N, int64_t K);
+size_t w4a16_tiled_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                              uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
+                              hipStream_t stream);
 hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,
                                 hipStream_t stream);
 

@@ -28,10 +28,12 @@ def _problem(M, N, K, seed):
     return a, wq, wsf, alpha
 
 
-def _run_check(a, wq, wsf, alpha):
+def _run_check(a, wq, wsf, alpha, rows=None):
     d = bs.w4a16_gemm(dev_bf16(a), dev_u8(wq), dev_u8(wsf), None if alpha is None else dev_f32([alpha]))
     torch.cuda.synchronize()
     got = host_bf16_bits(d)
+    if rows is not None:
+        got, a = got[rows], a[rows]
     want = OG.w4a16_gemm(a, wq, wsf, 1.0 if alpha is None else alpha)
     ok, worst, nbad = TOL.check_bf16(got, want)
     assert ok, f"{nbad} out of tolerance (worst {worst:.2f})"
@@ -72,3 +74,30 @@ def test_w4a16_rows_33_to_64(monkeypatch, mt4, M, N, K):
 def test_w4a16_split_forms(M, N, K):
     """Split-K form (one or two M tiles) incl. K longer than 16 loads per lane."""
     _run_check(*_problem(M, N, K, 800 + M))
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 64, 64), (200, 288, 640), (256, 256, 2048), (300, 544, 1344),
+                                   (513, 800, 4096), (1000, 96, 512)])
+def test_w4a16_tiled_shapes(M, N, K):
+    """Rows above 64 with K % 64 == 0: the 256 x 256 tiled kernel (ragged M and N,
+    one or several tiles, K splits where tiles are few)."""
+    _run_check(*_problem(M, N, K, 900 + M))
+
+
+@pytest.mark.parametrize("M,N,K", [(96, 160, 1056), (130, 64, 1024 + 32)])
+def test_w4a16_rows_above_64_k_not_multiple_of_64(M, N, K):
+    """K % 64 != 0 keeps the 64-row chunked form."""
+    _run_check(*_problem(M, N, K, 950 + M))
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 7168), (512, 6656, 19968), (2048, 19968, 6656)])
+def test_w4a16_large_sampled(M, N, K):
+    """The workload shape at M = 4096 and the two projection shapes of the
+    W4A16 follow-up page, checked on sampled rows (first/last tile rows included)."""
+    a = synth.bf16_normal(960, (M, K))
+    w = synth.bf16_normal(961, (N, K), 0.02)
+    gw = OQ.global_scale(w)
+    wq, wsf = OQ.nvfp4_quantize(w, gw)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1],
+                                     np.random.default_rng(2).choice(M, 12, replace=False)]))
+    _run_check(a, wq, wsf, np.float32(np.float32(1.0) / gw), rows=rows)
