@@ -34,11 +34,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return float_to_bf16_rne(lo) | (float_to_bf16_rne(hi) << 16);
 }
 
-// E4M3 scale code (magnitude bits) -> its value in binary32, exact.
+// E4M3 scale code (magnitude bits) -> its value in binary32, exact and without
+// a branch: the 7 magnitude bits placed at fp16 bit 7 are the E4M3 value times
+// 2^-8 for normal and subnormal codes alike.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)((c & 0x7Fu) << 7));
+  return (float)h * 256.0f;
 }
 
 // Eight E2M1 values (one 32-bit word, first value in the low nibble) times the
@@ -55,8 +56,8 @@ __device__ __forceinline__ v8bf dq8_bf16(uint32_t word, float s) {
       case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
       default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
     }
-    // exact products: truncating to the upper 16 bits is the bf16 value
-    o[j] = (__float_as_uint(f.x * s) >> 16) | (__float_as_uint(f.y * s) & 0xFFFF0000u);
+    // exact products, so the nearest-even conversion is exact
+    o[j] = __builtin_bit_cast(uint32_t, v2bf{(__bf16)(f.x * s), (__bf16)(f.y * s)});
   }
   return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 }

@@ -147,15 +147,18 @@ __global__ void __launch_bounds__(kNT, 1)
       const uint8_t* sa = st;
       const uint8_t* sq = st + kA;
       const uint8_t* ss = st + kA + kBq;
-      // this lane's B rows: all 64 code values (two chunks) and 4 scale bytes
-      uint32_t bw[kTN][8], bsc[kTN];
+      // this lane's B rows: its 4 code words (K values 16kk + 8g .. +7, word
+      // 2kk + g of the row) and the row's 4 scale bytes
+      uint32_t bw[kTN][4], bsc[kTN];
 #pragma unroll
       for (int jn = 0; jn < kTN; jn++) {
         const int r = wn * kWN + jn * 32 + lr;
         const uint4 c0 = *reinterpret_cast<const uint4*>(sq + r * kBRow + swz_b(r, 0) * 16);
         const uint4 c1 = *reinterpret_cast<const uint4*>(sq + r * kBRow + swz_b(r, 1) * 16);
-        bw[jn][0] = c0.x; bw[jn][1] = c0.y; bw[jn][2] = c0.z; bw[jn][3] = c0.w;
-        bw[jn][4] = c1.x; bw[jn][5] = c1.y; bw[jn][6] = c1.z; bw[jn][7] = c1.w;
+        bw[jn][0] = g ? c0.y : c0.x;
+        bw[jn][1] = g ? c0.w : c0.z;
+        bw[jn][2] = g ? c1.y : c1.x;
+        bw[jn][3] = g ? c1.w : c1.z;
         bsc[jn] = *reinterpret_cast<const uint32_t*>(ss + r * kSRow);
       }
 #pragma unroll
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__(kNT, 1)
         v8bf fb[kTN];
 #pragma unroll
         for (int jn = 0; jn < kTN; jn++)
-          fb[jn] = dq8_bf16(bw[jn][2 * kk + g], e4m3_to_f32((bsc[jn] >> (8 * kk)) & 0xFFu));
+          fb[jn] = dq8_bf16(bw[jn][kk], e4m3_to_f32((bsc[jn] >> (8 * kk)) & 0xFFu));
 #pragma unroll
         for (int i = 0; i < kTM; i++) {
           const int r = wm * kWM + i * 32 + lr;
