@@ -364,6 +364,31 @@ def run_rows(torch, bs, synth, timer, only):
                              "algorithmic_bytes": nbytes}
         rows["w4a16_4096x7168"] = res
 
+    # W4A16 at the projection shapes of the W4A16 follow-up page (down: N=6656,
+    # K=19968; up: N=19968, K=6656), M from weight streaming to compute bound;
+    # "published_B_us" is the page's candidate arm on B300 (other hardware: context)
+    if want("w4a16_projection_shapes"):
+        published = {("down", 1): 54.176, ("down", 32): 54.497, ("down", 128): 55.089, ("down", 512): 117.489,
+                     ("down", 2048): 289.411, ("down", 4096): 586.886, ("up", 1): 39.232, ("up", 32): 39.393,
+                     ("up", 128): 45.792, ("up", 512): 103.473, ("up", 2048): 298.787, ("up", 4096): 599.638}
+        res = {}
+        for proj, N, K in [("down", 6656, 19968), ("up", 19968, 6656)]:
+            w = bf16(synth.bf16_normal(170 if proj == "down" else 171, (N, K), 0.02))
+            gw = bs.global_scale(w)
+            wq, wsf = bs.quantize(w, "nvfp4", gs=gw)
+            del w
+            alpha = torch.tensor([np.float32(1.0) / np.float32(gw.cpu().numpy()[0])], device=dev)
+            for M in (1, 32, 128, 512, 2048, 4096):
+                a = bf16(synth.bf16_normal(172 + M, (M, K)))
+                D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                fn = lambda: bs.w4a16_gemm(a, wq, wsf, alpha, out=D)
+                nbytes = 2 * M * K + N * K // 2 + N * K // 16 + 4 + 2 * M * N
+                r = _rate(timer.run(fn, iters=10, cold=True), 2.0 * M * N * K, nbytes)
+                r["published_B_us"] = published[(proj, M)]
+                res[f"{proj} M={M}"] = r
+            del wq, wsf
+        rows["w4a16_projection_shapes"] = res
+
     # a6: the MXFP4 form at the large workload shape (FP4 MFMA roofline)
     if want("mxfp4_gemm_4096x4096x7168"):
         M, N, K = 4096, 4096, 7168

@@ -129,6 +129,9 @@ BSFP4_API bsfp4_status fp4_quantize(int fmt, const uint16_t* x, int64_t rows_in,
  *             `cutlass_scaled_fp4_mm_sm103a_impl` checks)
  *   ws        device workspace of fp4_gemm_workspace_size(...) bytes (may be
  *             NULL when that size is 0); its contents need no initialisation
+ * NVFP4 block scales are non-negative, as fp4_quantize writes them: the
+ * kernels read an E4M3 scale's 7 magnitude bits only, and the NaN codes
+ * (0x7F, 0xFF) are outside the contract.
  * Results equal the float64 definition up to FP32 summation order.
  * ------------------------------------------------------------------------- */
 BSFP4_API size_t fp4_gemm_workspace_size(int fmt, int64_t M, int64_t N, int64_t K);
@@ -149,6 +152,8 @@ BSFP4_API bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, c
  *   ws        device workspace of w4a16_gemm_workspace_size(...) bytes (may
  *             be NULL when that size is 0); its contents need no
  *             initialisation
+ * Block scales follow fp4_gemm's rule (non-negative, no NaN codes).  Results
+ * equal the float64 definition up to FP32 summation order.
  * ------------------------------------------------------------------------- */
 BSFP4_API size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 BSFP4_API bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
