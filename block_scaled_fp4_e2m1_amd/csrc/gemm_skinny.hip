@@ -30,6 +30,7 @@
 
 #include "device_common.h"
 #include "launchers.h"
+#include "lds_dma.h"
 
 namespace bsfp4 {
 namespace {
@@ -406,6 +407,138 @@ __global__ void __launch_bounds__(512)
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged single-pass form for NVFP4 activations, M <= 16, K <= 8192: one
+// workgroup per 16 output columns, nw <= 8 waves each owning UW units of 128 K
+// values.  Measured on the GPU, the per-lane register loads of the forms above
+// spend most of their time in the vector memory pipeline (each 16-lane quarter
+// of a load touches 16 rows, and 2-byte scale loads cost as much as code
+// loads), so here every operand reaches LDS through direct-to-LDS DMA:
+//   * scales: the workgroup's 16 weight rows of scales are one contiguous
+//     16 x K/16-byte block in memory (row-major [N, K/16]), likewise the 16
+//     activation rows; wave w copies the w-th KB of each, and one barrier makes
+//     them visible to every wave;
+//   * codes: per unit, one instruction moves 16 rows x 64 bytes (four lanes per
+//     row segment) into [unit][row][64 B]; the 16-byte piece p of row r lands at
+//     position p ^ ((r >> 2) & 3), so the MFMA's 128-bit reads (lane = row) hit
+//     distinct banks;
+//   * the activations are issued first (L2-resident) and dequantised into
+//     registers while the weight stream is still in flight; then each weight
+//     unit is consumed as soon as its own DMA has landed (s_waitcnt vmcnt);
+//   * partial 16 x 16 tiles are summed in LDS in wave order (deterministic),
+//     multiplied by alpha and rounded once to bf16.
+// Lanes past the problem (rows >= M, K >= K) read zeros; scale bytes past a
+// row's end only ever multiply zero codes.
+constexpr int kLdsMaxWaves = 8;
+
+template <int UW>
+__global__ void __launch_bounds__(512)
+    skinny_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
+               const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
+               int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(2 + 2 * UW) * kLdsMaxWaves * 1024];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int k_lo = wave * (UW * 128);
+  const int kb16 = K / 16;  // scale bytes per row
+  uint8_t* const lsb = smem;                        // nwaves KB: weight scales, rows n0..n0+15
+  uint8_t* const lsa = smem + nwaves * 1024;        // nwaves KB: activation scales, rows 0..15
+  uint8_t* const lbq = smem + 2 * nwaves * 1024 + wave * (2 * UW * 1024);  // UW KB of weight codes
+  uint8_t* const laq = lbq + UW * 1024;                                    // UW KB of activation codes
+  const v4u32 rbq = make_rsrc4(B, (int64_t)N * (K / 2));
+  const v4u32 rbs = make_rsrc4(SFB, (int64_t)N * kb16);
+  const v4u32 raq = make_rsrc4(A, (int64_t)M * (K / 2));
+  const v4u32 ras = make_rsrc4(SFA, (int64_t)M * kb16);
+  {
+    const int off = wave * 1024 + lane * 16;  // byte of the 16 x K/16 scale block
+    buf_lds16(rbs, off < 16 * kb16 ? (uint32_t)(n0 * kb16 + off) : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsb + wave * 1024)));
+    buf_lds16(ras, off < M * kb16 ? (uint32_t)off : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsa + wave * 1024)));
+  }
+  const int r = lane >> 2;                        // row of the DMA lane
+  const int piece = (lane & 3) ^ ((r >> 2) & 3);  // 16-byte piece it fetches
+  const uint32_t arow = (uint32_t)(r * (K / 2) + k_lo / 2 + 16 * piece);
+  const uint32_t brow = (uint32_t)((n0 + r) * (K / 2) + k_lo / 2 + 16 * piece);
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const bool ok = r < M && k_lo + 128 * i + 32 * piece < K;
+    buf_lds16(raq, ok ? arow + 64 * i : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(laq + 1024 * i)));
+  }
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const bool ok = k_lo + 128 * i + 32 * piece < K;
+    buf_lds16(rbq, ok ? brow + 64 * i : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lbq + 1024 * i)));
+  }
+
+  // MFMA lane (c, g): row c, K values 128i + 32g + 8s (s = word of the piece)
+  const int c = lane & 15, g = lane >> 4;
+  const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
+  wait_vmcnt<UW>();  // scales and activations have landed; only weight units may be in flight
+  __builtin_amdgcn_s_barrier();
+  const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
+  const uint8_t* sarow = lsa + c * kb16 + k_lo / 16 + 2 * g;
+  // two E4M3 scale bytes -> two fp16 values (exact): magnitude bits at fp16 bit 7, times 2^8
+  auto scales2 = [](uint32_t s) {
+    return __builtin_bit_cast(v2h, ((s & 0x7Fu) << 7) | ((s & 0x7F00u) << 15)) *
+           v2h{(_Float16)256.0f, (_Float16)256.0f};
+  };
+  v8h fa[UW][4];
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const uint4 w = *reinterpret_cast<const uint4*>(laq + 1024 * i + rd);
+    const v2h s = scales2(*reinterpret_cast<const uint16_t*>(sarow + 8 * i));
+    fa[i][0] = dq8_f16(w.x, s[0]);
+    fa[i][1] = dq8_f16(w.y, s[0]);
+    fa[i][2] = dq8_f16(w.z, s[1]);
+    fa[i][3] = dq8_f16(w.w, s[1]);
+    // keep this dequantisation ahead of the weight waits
+    asm volatile("" : "+v"(fa[i][0]), "+v"(fa[i][1]), "+v"(fa[i][2]), "+v"(fa[i][3]));
+  }
+  v4f acc = v4f{};
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    switch (UW - 1 - i) {  // weight unit i has landed
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 5: wait_vmcnt<5>(); break;
+      case 6: wait_vmcnt<6>(); break;
+      default: wait_vmcnt<7>(); break;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(lbq + 1024 * i + rd);
+    const v2h s = scales2(*reinterpret_cast<const uint16_t*>(sbrow + 8 * i));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.x, s[0]), fa[i][0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.y, s[0]), fa[i][1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.z, s[1]), fa[i][2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.w, s[1]), fa[i][3], acc, 0, 0, 0);
+    asm volatile("" : "+v"(acc));  // unit i is done before the next unit's wait
+  }
+  // acc[j] = partial D[m = c][n0 + 4g + j]; each wave's tile goes to its own code region
+  float* red = reinterpret_cast<float*>(lbq);
+#pragma unroll
+  for (int j = 0; j < 4; j++) red[(4 * g + j) * 17 + c] = acc[j];
+  __syncthreads();
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  for (int idx = tid; idx < 128; idx += blockDim.x) {  // (row, column pair), waves summed in order
+    const int m = idx >> 3, np = (idx & 7) * 2;
+    if (m >= M) continue;
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int w = 0; w < nwaves; w++) {
+      const float* rw = reinterpret_cast<const float*>(smem + 2 * nwaves * 1024 + w * (2 * UW * 1024));
+      s0 += rw[np * 17 + m];
+      s1 += rw[(np + 1) * 17 + m];
+    }
+    *reinterpret_cast<uint32_t*>(D + (int64_t)m * N + n0 + np) = pack_bf16x2(alpha * s0, alpha * s1);
+  }
+}
+
 // NL for the single-pass form (<= 8 waves of 128*NL values), 0 if K is too long.
 int onepass_nl(int64_t K) {
   const int64_t kb = (K + 127) / 128;
@@ -519,6 +652,48 @@ hipError_t launch_onepass(const uint8_t* A, const uint8_t* SFA, const uint8_t* B
   }
 }
 
+// Units of 128 K values per wave and wave count of the LDS-staged form.
+struct LdsPlan {
+  int uw, nw;
+};
+LdsPlan lds_plan(int64_t K) {
+  const int u = (int)((K + 127) / 128);
+  const int uw = (u + kLdsMaxWaves - 1) / kLdsMaxWaves;
+  return LdsPlan{uw, (u + uw - 1) / uw};
+}
+
+// The LDS-staged NVFP4 form applies for M <= 16, K <= 8192 (at most 8 waves of
+// 8 units), M * K a multiple of 256 and operands whose byte offsets fit 31 bits; BSFP4_SKINNY_LDS=0
+// selects the register-load single-pass form instead, BSFP4_SKINNY_SPLIT=1 the
+// split-K form (measurement overrides).
+bool use_lds(int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_SKINNY_LDS");
+  if (e && e[0] == '0') return false;
+  const char* sp = getenv("BSFP4_SKINNY_SPLIT");  // measurement override: force the split-K form
+  if (sp && sp[0] == '1') return false;
+  if (M > 16 || K > 128 * 8 * kLdsMaxWaves || N * (K / 2) >= ((int64_t)1 << 31)) return false;
+  // the activation scale block (M x K/16 bytes) is copied in whole 16-byte pieces:
+  // its length must be a multiple of 16 so that no piece straddles the buffer's end
+  if ((M * (K / 16)) % 16 != 0) return false;
+  const LdsPlan pl = lds_plan(K);
+  return pl.nw * 1024 >= K;  // one 1 KB scale piece per wave covers the 16 x K/16 block
+}
+
+hipError_t launch_lds(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                      const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const LdsPlan pl = lds_plan(K);
+  const dim3 grid((unsigned)(N / 16)), block((unsigned)(64 * pl.nw));
+  switch (pl.uw) {
+#define BSFP4_LDS_CASE(u) \
+  case u: skinny_lds<u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K); break;
+    BSFP4_LDS_CASE(1) BSFP4_LDS_CASE(2) BSFP4_LDS_CASE(3) BSFP4_LDS_CASE(4)
+    BSFP4_LDS_CASE(5) BSFP4_LDS_CASE(6) BSFP4_LDS_CASE(7) BSFP4_LDS_CASE(8)
+#undef BSFP4_LDS_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // The single-pass NVFP4 form applies for M <= 16 when K fits 8 waves and the
 // buffer offsets fit 31 bits.
 bool use_onepass(int64_t M, int64_t N, int64_t K) {
@@ -540,6 +715,8 @@ template <int AKIND>
 hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                        const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                        hipStream_t stream) {
+  if (AKIND == 0 && use_lds(M, N, K))
+    return launch_lds(static_cast<const uint8_t*>(A), SFA, B, SFB, alpha, D, M, N, K, stream);
   if (AKIND == 0 && use_onepass(M, N, K))
     return launch_onepass(static_cast<const uint8_t*>(A), SFA, B, SFB, alpha, D, M, N, K, stream);
   const bool offsets32 = N * (K / 2) < ((int64_t)1 << 31);  // buffer offsets of the split kernels
@@ -567,7 +744,7 @@ hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_
 
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
   if (M <= 0 || M > 64 || N * (K / 2) >= ((int64_t)1 << 31)) return 0;
-  if (fp4_activations && use_onepass(M, N, K)) return 0;
+  if (fp4_activations && (use_lds(M, N, K) || use_onepass(M, N, K))) return 0;
   if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;
   const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), M <= 16 ? 1 : M <= 32 ? 2 : 4);
   return pl.ksplit > 1 ? (size_t)pl.ksplit * M * N * sizeof(float) : 0;

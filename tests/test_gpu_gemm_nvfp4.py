@@ -54,7 +54,7 @@ def test_nvfp4_gemm_random(M, N, K):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
-@pytest.mark.parametrize("M", [24, 96])
+@pytest.mark.parametrize("M", [16, 24, 96])
 def test_nvfp4_gemm_every_scale_code(M):
     """Random codes with every finite E4M3 scale code (incl. subnormal scales)."""
     N, K = 160, 512
@@ -66,8 +66,9 @@ def test_nvfp4_gemm_every_scale_code(M):
     _check(got, aq, sfa, bq, sfb, np.float32(0.01))
 
 
-def test_nvfp4_gemm_zero_blocks_and_no_alpha():
-    M, N, K = 64, 96, 256
+@pytest.mark.parametrize("M", [64, 16])
+def test_nvfp4_gemm_zero_blocks_and_no_alpha(M):
+    N, K = 96, 256
     aq, sfa, bq, sfb, _ = nvfp4_problem(M, N, K, seed=5)
     aq[:, 32:64] = 0          # zero a whole 64-element K range in A
     sfb[:, 3] = 0             # zero scale block in B
@@ -180,10 +181,17 @@ def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, spli
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (3, 96, 4000 - 4000 % 32), (16, 4096, 7168), (9, 1056, 16384),
-                                   (16, 288, 32), (5, 160, 1088)])
-@pytest.mark.parametrize("form", ["onepass", "split"])
+                                   (16, 288, 32), (5, 160, 1088), (16, 128, 8192), (2, 96, 8224),
+                                   (11, 4096, 4064), (16, 64, 96), (7, 1056, 2304), (1, 32, 256),
+                                   (4, 4096, 4032), (8, 288, 1056)])
+@pytest.mark.parametrize("form", ["lds", "onepass", "split"])
 def test_nvfp4_gemm_small_m_forms(monkeypatch, form, M, N, K):
-    """Both small-M forms (single pass, split-K + reduce) on ragged shapes."""
+    """The small-M forms (LDS-staged and register single pass, split-K + reduce)
+    on ragged shapes: K tails inside a 128-value unit, K up to the LDS form's
+    8192 limit and just past it, several wave counts of the LDS form (shapes
+    with M*K not a multiple of 256 take the register form under "lds")."""
+    if form == "onepass":
+        monkeypatch.setenv("BSFP4_SKINNY_LDS", "0")
     if form == "split":
         monkeypatch.setenv("BSFP4_SKINNY_SPLIT", "1")
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=500 + M + K)
