@@ -539,6 +539,151 @@ __global__ void __launch_bounds__(512)
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged single-pass form for at most four activation rows (decode
+// shapes), NVFP4 (AKIND 0) or bf16 (AKIND 1) activations, K <= 8192.  The
+// weights move exactly as in skinny_lds.  The activation rows, being few, are
+// copied whole into LDS once per workgroup (one contiguous block: rows are
+// contiguous in memory) and, for NVFP4, dequantised there once to fp16 by all
+// threads; the MFMA then reads its activation operand from LDS (lanes of rows
+// >= M feed zeros), so the per-wave VALU work is the weight dequantisation
+// alone instead of weights plus 16 mostly-empty activation rows.
+constexpr int kFewRows = 4;
+
+template <int AKIND, int UW>
+__global__ void __launch_bounds__(512)
+    skinny_lds_few(const void* __restrict__ Aptr, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
+                   const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
+                   int M, int N, int K) {
+  constexpr int kMaxK = 1024 * UW;  // nw <= 8 waves of UW units of 128 values
+  constexpr int kBScale = 8 * 1024;                                   // 16 x K/16 weight scale block
+  constexpr int kBCodes = kLdsMaxWaves * UW * 1024;                   // per-wave [unit][row][64 B]
+  constexpr int kAVals = kFewRows * kMaxK * 2;                        // fp16 / bf16 activation rows
+  constexpr int kACodes = AKIND == 0 ? kFewRows * kMaxK / 2 : 0;      // NVFP4 codes before dequantisation
+  constexpr int kAScales = AKIND == 0 ? ((kFewRows * kMaxK / 16 + 1023) / 1024) * 1024 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kBScale + kBCodes + kAVals + kACodes + kAScales];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int k_lo = wave * (UW * 128);
+  const int kb16 = K / 16;
+  uint8_t* const lsb = smem;
+  uint8_t* const lbq = smem + kBScale + wave * (UW * 1024);
+  uint8_t* const lav = smem + kBScale + kBCodes;  // activation values, row m at m * 2K bytes
+  uint8_t* const laq = lav + kAVals;              // NVFP4 activation codes [M][K/2]
+  uint8_t* const las = laq + kACodes;             // NVFP4 activation scales [M][K/16]
+  const v4u32 rbq = make_rsrc4(B, (int64_t)N * (K / 2));
+  const v4u32 rbs = make_rsrc4(SFB, (int64_t)N * kb16);
+  auto lds_u = [](const uint8_t* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(p)); };
+
+  // ---- weight scales (one 1 KB piece per wave) and the activation block(s),
+  // pieces spread over the waves; all of them are issued before the weight
+  // units, so waiting for "at most UW outstanding" covers them whatever their count
+  {
+    const int off = wave * 1024 + lane * 16;
+    buf_lds16(rbs, off < 16 * kb16 ? (uint32_t)(n0 * kb16 + off) : kBufOOB, 0, lds_u(lsb + wave * 1024));
+  }
+  if constexpr (AKIND == 0) {
+    const v4u32 raq = make_rsrc4(Aptr, (int64_t)M * (K / 2));
+    const v4u32 ras = make_rsrc4(SFA, (int64_t)M * kb16);
+    const int qpieces = (M * (K / 2) + 1023) / 1024, spieces = (M * kb16 + 1023) / 1024;
+    for (int pc = wave; pc < qpieces + spieces; pc += nwaves) {  // codes first, then scales
+      if (pc < qpieces) {
+        const int off = pc * 1024 + lane * 16;
+        buf_lds16(raq, off < M * (K / 2) ? (uint32_t)off : kBufOOB, 0, lds_u(laq + pc * 1024));
+      } else {
+        const int off = (pc - qpieces) * 1024 + lane * 16;
+        buf_lds16(ras, off < M * kb16 ? (uint32_t)off : kBufOOB, 0, lds_u(las + (pc - qpieces) * 1024));
+      }
+    }
+  } else {
+    const v4u32 ra = make_rsrc4(Aptr, (int64_t)M * K * 2);
+    const int apieces = (M * K * 2 + 1023) / 1024;
+    for (int pc = wave; pc < apieces; pc += nwaves) {
+      const int off = pc * 1024 + lane * 16;
+      buf_lds16(ra, off < M * K * 2 ? (uint32_t)off : kBufOOB, 0, lds_u(lav + pc * 1024));
+    }
+  }
+  // ---- weight units
+  const int r = lane >> 2;
+  const int piece = (lane & 3) ^ ((r >> 2) & 3);
+  const uint32_t brow = (uint32_t)((n0 + r) * (K / 2) + k_lo / 2 + 16 * piece);
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    const bool ok = k_lo + 128 * i + 32 * piece < K;
+    buf_lds16(rbq, ok ? brow + 64 * i : kBufOOB, 0, lds_u(lbq + 1024 * i));
+  }
+  wait_vmcnt<UW>();  // activations and scales have landed
+  __builtin_amdgcn_s_barrier();
+  if constexpr (AKIND == 0) {  // dequantise the activation rows once: 8 values per item
+    for (int it = tid; it < M * (K / 8); it += blockDim.x) {
+      const int m = it / (K / 8), w = it - m * (K / 8);
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(laq + m * (K / 2) + 4 * w);
+      const uint32_t sc = las[m * kb16 + (w >> 1)];
+      *reinterpret_cast<v8h*>(lav + m * (2 * K) + 16 * w) = dq8_f16(word, e4m3_to_f16(sc));
+    }
+    __syncthreads();
+  }
+
+  const int c = lane & 15, g = lane >> 4;
+  const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
+  const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
+  const uint8_t* arow = lav + c * (2 * K) + 2 * (k_lo + 32 * g);
+  v4f acc = v4f{};
+#pragma unroll
+  for (int i = 0; i < UW; i++) {
+    switch (UW - 1 - i) {  // weight unit i has landed
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 5: wait_vmcnt<5>(); break;
+      case 6: wait_vmcnt<6>(); break;
+      default: wait_vmcnt<7>(); break;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(lbq + 1024 * i + rd);
+    const uint32_t sb = *reinterpret_cast<const uint16_t*>(sbrow + 8 * i);
+    uint4 av[4] = {};
+    if (c < M && k_lo + 128 * i + 32 * g < K) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) av[q] = *reinterpret_cast<const uint4*>(arow + 256 * i + 16 * q);
+    }
+    if constexpr (AKIND == 0) {
+      const v2h s = __builtin_bit_cast(v2h, ((sb & 0x7Fu) << 7) | ((sb & 0x7F00u) << 15)) *
+                    v2h{(_Float16)256.0f, (_Float16)256.0f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.x, s[0]), __builtin_bit_cast(v8h, av[0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.y, s[0]), __builtin_bit_cast(v8h, av[1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.z, s[1]), __builtin_bit_cast(v8h, av[2]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.w, s[1]), __builtin_bit_cast(v8h, av[3]), acc, 0, 0, 0);
+    } else {
+      const float s0 = e4m3_to_f32(sb & 0xFFu), s1 = e4m3_to_f32(sb >> 8);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(w.x, s0), __builtin_bit_cast(v8bf, av[0]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(w.y, s0), __builtin_bit_cast(v8bf, av[1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(w.z, s1), __builtin_bit_cast(v8bf, av[2]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(w.w, s1), __builtin_bit_cast(v8bf, av[3]), acc, 0, 0, 0);
+    }
+    asm volatile("" : "+v"(acc));  // unit i is done before the next unit's wait
+  }
+  float* red = reinterpret_cast<float*>(lbq);  // 16 x 16 floats: exactly the smallest (1 KB) region
+#pragma unroll
+  for (int j = 0; j < 4; j++) red[(4 * g + j) * 16 + c] = acc[j];
+  __syncthreads();
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  for (int idx = tid; idx < kFewRows * 8; idx += blockDim.x) {
+    const int m = idx >> 3, np = (idx & 7) * 2;
+    if (m >= M) continue;
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int w = 0; w < nwaves; w++) {
+      const float* rw = reinterpret_cast<const float*>(smem + kBScale + w * (UW * 1024));
+      s0 += rw[np * 16 + m];
+      s1 += rw[(np + 1) * 16 + m];
+    }
+    *reinterpret_cast<uint32_t*>(D + (int64_t)m * N + n0 + np) = pack_bf16x2(alpha * s0, alpha * s1);
+  }
+}
+
 // NL for the single-pass form (<= 8 waves of 128*NL values), 0 if K is too long.
 int onepass_nl(int64_t K) {
   const int64_t kb = (K + 127) / 128;
@@ -679,6 +824,36 @@ bool use_lds(int64_t M, int64_t N, int64_t K) {
   return pl.nw * 1024 >= K;  // one 1 KB scale piece per wave covers the 16 x K/16 block
 }
 
+// The few-row form: M <= 4 and otherwise the LDS form's conditions (for bf16
+// activations: K <= 8192 and 32-bit offsets); BSFP4_SKINNY_FEW=0 disables it.
+bool use_few(int akind, int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_SKINNY_FEW");
+  if (e && e[0] == '0') return false;
+  const char* sp = getenv("BSFP4_SKINNY_SPLIT");
+  if (sp && sp[0] == '1') return false;
+  if (M > kFewRows || K > 128 * 8 * kLdsMaxWaves || N * (K / 2) >= ((int64_t)1 << 31)) return false;
+  if (akind == 0 && (M * (K / 16)) % 16 != 0) return false;  // whole 16-byte scale pieces
+  return lds_plan(K).nw * 1024 >= K;
+}
+
+template <int AKIND>
+hipError_t launch_few(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                      uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const LdsPlan pl = lds_plan(K);
+  const dim3 grid((unsigned)(N / 16)), block((unsigned)(64 * pl.nw));
+  switch (pl.uw) {
+#define BSFP4_FEW_CASE(u)                                                                                  \
+  case u:                                                                                                  \
+    skinny_lds_few<AKIND, u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K); \
+    break;
+    BSFP4_FEW_CASE(1) BSFP4_FEW_CASE(2) BSFP4_FEW_CASE(3) BSFP4_FEW_CASE(4)
+    BSFP4_FEW_CASE(5) BSFP4_FEW_CASE(6) BSFP4_FEW_CASE(7) BSFP4_FEW_CASE(8)
+#undef BSFP4_FEW_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lds(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                       const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const LdsPlan pl = lds_plan(K);
@@ -715,6 +890,7 @@ template <int AKIND>
 hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                        const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                        hipStream_t stream) {
+  if (use_few(AKIND, M, N, K)) return launch_few<AKIND>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
   if (AKIND == 0 && use_lds(M, N, K))
     return launch_lds(static_cast<const uint8_t*>(A), SFA, B, SFB, alpha, D, M, N, K, stream);
   if (AKIND == 0 && use_onepass(M, N, K))
@@ -744,6 +920,7 @@ hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_
 
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
   if (M <= 0 || M > 64 || N * (K / 2) >= ((int64_t)1 << 31)) return 0;
+  if (use_few(fp4_activations ? 0 : 1, M, N, K)) return 0;
   if (fp4_activations && (use_lds(M, N, K) || use_onepass(M, N, K))) return 0;
   if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;
   const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), M <= 16 ? 1 : M <= 32 ? 2 : 4);

@@ -184,12 +184,14 @@ def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, spli
                                    (16, 288, 32), (5, 160, 1088), (16, 128, 8192), (2, 96, 8224),
                                    (11, 4096, 4064), (16, 64, 96), (7, 1056, 2304), (1, 32, 256),
                                    (4, 4096, 4032), (8, 288, 1056)])
-@pytest.mark.parametrize("form", ["lds", "onepass", "split"])
+@pytest.mark.parametrize("form", ["few", "lds", "onepass", "split"])
 def test_nvfp4_gemm_small_m_forms(monkeypatch, form, M, N, K):
-    """The small-M forms (LDS-staged and register single pass, split-K + reduce)
-    on ragged shapes: K tails inside a 128-value unit, K up to the LDS form's
-    8192 limit and just past it, several wave counts of the LDS form (shapes
-    with M*K not a multiple of 256 take the register form under "lds")."""
+    """The small-M forms (few-row and 16-row LDS-staged, register single pass,
+    split-K + reduce) on ragged shapes: K tails inside a 128-value unit, K up to
+    the LDS forms' 8192 limit and just past it, several wave counts (shapes
+    outside a form's conditions take the next form)."""
+    if form != "few":
+        monkeypatch.setenv("BSFP4_SKINNY_FEW", "0")
     if form == "onepass":
         monkeypatch.setenv("BSFP4_SKINNY_LDS", "0")
     if form == "split":

@@ -54,8 +54,9 @@ def test_w4a16_workload(M, seed):
     _run_check(a, wq, wsf, np.float32(np.float32(1.0) / gw))
 
 
-def test_w4a16_every_scale_code_no_alpha():
-    M, N, K = 8, 64, 512
+@pytest.mark.parametrize("M", [8, 2])
+def test_w4a16_every_scale_code_no_alpha(M):
+    N, K = 64, 512
     a = synth.bf16_normal(1, (M, K), 4.0)
     wq = synth.random_bytes(2, (N, K // 2))
     wsf = synth.random_e4m3_scales(3, (N, K // 16), 0x00, 0x7F)
@@ -101,3 +102,14 @@ def test_w4a16_large_sampled(M, N, K):
     rows = np.unique(np.concatenate([[0, 255, 256, M - 1],
                                      np.random.default_rng(2).choice(M, 12, replace=False)]))
     _run_check(a, wq, wsf, np.float32(np.float32(1.0) / gw), rows=rows)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (2, 96, 8192), (3, 4096, 7168), (4, 288, 4064),
+                                   (1, 64, 8224), (4, 1056, 96), (2, 160, 1184)])
+@pytest.mark.parametrize("form", ["few", "split"])
+def test_w4a16_few_rows_forms(monkeypatch, form, M, N, K):
+    """At most four rows: the LDS-staged form (activation rows copied whole into
+    LDS; K tails inside a unit, K up to 8192 and just past it) and the split-K form."""
+    if form == "split":
+        monkeypatch.setenv("BSFP4_SKINNY_FEW", "0")
+    _run_check(*_problem(M, N, K, 970 + M + K))
