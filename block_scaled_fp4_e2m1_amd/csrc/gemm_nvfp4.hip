@@ -601,12 +601,21 @@ __global__ void __launch_bounds__(256)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < MN / 4; q += stride) {
     float4 acc = reinterpret_cast<const float4*>(part)[q];
-    for (int s = 1; s < splits; s++) {
-      const float4 v = reinterpret_cast<const float4*>(part + (int64_t)s * MN)[q];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    // up to 8 partials loaded before any is added (independent loads in flight),
+    // then added in split order
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (s0 + j < splits) v[j] = reinterpret_cast<const float4*>(part + (int64_t)(s0 + j) * MN)[q];
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        if (s0 + j < splits) {
+          acc.x += v[j].x;
+          acc.y += v[j].y;
+          acc.z += v[j].z;
+          acc.w += v[j].w;
+        }
     }
     reinterpret_cast<uint2*>(D)[q] = make_uint2(pack_bf16x2(alpha * acc.x, alpha * acc.y),
                                                 pack_bf16x2(alpha * acc.z, alpha * acc.w));

@@ -236,6 +236,168 @@ __global__ void __launch_bounds__(kNT, 1)
     out_bands(std::integral_constant<int, 4>{});
 }
 
+
+// ---------------------------------------------------------------------------
+// W4A16 for 5 <= M <= 64 (rows up to four use the few-row kernel of
+// gemm_skinny.hip): one workgroup = all 64 rows x 128 output columns x one K
+// range, 8 waves = 2 column halves x 4 K quarters of every stage: a wave owns
+// 64 columns x 64 rows (16 v_mfma_f32_16x16x32_bf16 tiles) for 32 of the
+// stage's 128 K values, so every weight value is dequantised exactly once per
+// workgroup and each activation fragment read from LDS feeds four MFMAs; the
+// four K quarters are summed in LDS at the end, in quarter order.  The weight
+// stream is what costs at these shapes; the activations (at most 64 rows) stay
+// L2-resident and are re-read once per 128-column block.
+//   * the weight codes of the workgroup's whole K range (128 rows x K/S/2 bytes,
+//     rows padded by 16 bytes) are copied into LDS first, each row by
+//     consecutive lanes and loads so that HBM sees long row segments (per-stage
+//     64-byte pieces of 128 rows measured several times slower), and so are the
+//     range's weight scales (8 bytes per row and stage);
+//   * the activations follow in stages of 128 K values through a 4-slot ring
+//     (64 rows x 256 bytes of bf16, the 16-byte chunk x of row r at position
+//     x ^ (r & 15), conflict-free fragment reads), two loads per wave and stage;
+//   * K ranges of one column block are summed by splitk_reduce in range order.
+constexpr int kRBM = 64, kRBN = 128, kRNT = 512;
+constexpr int kRSK = 128;                   // K values per stage
+constexpr int kRA = kRBM * kRSK * 2;         // 16 KB of bf16 activations per stage
+constexpr int kRRing = 4;                   // activation stages in LDS: 3 in flight ahead of the one in use
+constexpr int kRMaxStages = 8;              // stages per K range
+constexpr int kRQ = kRBN * (4 * kRMaxStages + 1) * 16;  // weight codes of the range, padded rows
+constexpr int kRScales = kRBN * kRMaxStages * 8;
+constexpr int kRSmem = kRRing * kRA + kRQ + kRScales;
+
+__global__ void __launch_bounds__(kRNT)
+    w4a16_rows64(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
+                 const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N, int K, int splits,
+                 float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x % splits;
+  const int n0 = (blockIdx.x / splits) * kRBN;
+  const int total = K / kRSK;
+  const int sb = (int)((int64_t)total * split / splits);
+  const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
+  const int k_lo = sb * kRSK;
+  uint8_t* const sq = smem + kRRing * kRA;  // [128 rows][(4 nst + 1) 16-byte pieces]
+  uint8_t* const sc = sq + kRQ;             // [128 rows][8 nst bytes]
+  const int qpitch = (4 * nst + 1) * 16, pitch = 8 * nst;
+  const v4u32 ra = make_rsrc4(A, (int64_t)M * K * 2);
+  const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
+  const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
+  auto lds_u = [](const void* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(p)); };
+
+  // ---- weight codes of the range: LDS slot P (16 bytes) = row P / (4 nst + 1), piece P % (4 nst + 1)
+  {
+    const int per_row = 4 * nst + 1, slots = kRBN * per_row;
+    for (int i = wave; i * 64 < slots; i += kRNT / 64) {
+      const int p = 64 * i + lane, row = p / per_row, piece = p - row * per_row;
+      const bool ok = row < kRBN && piece < 4 * nst && n0 + row < N;
+      buf_lds16(rq, ok ? (uint32_t)((n0 + row) * (K / 2) + k_lo / 2 + 16 * piece) : kBufOOB, 0,
+                lds_u(sq + 1024 * i));
+    }
+  }
+  // ---- the range's weight scales: 4 * nst loads of 64 dwords (2 dwords per row and stage)
+  for (int i = wave; i < 4 * nst; i += kRNT / 64) {
+    const int d = 64 * i + lane, row = d / (2 * nst), word = d - row * (2 * nst);
+    const uint32_t off = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
+    buf_lds4(rs, off, 0, lds_u(sc + 256 * i));
+  }
+  // ---- activation ring (the stage's K offset goes in the SGPR offset)
+  uint32_t va[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int r = 4 * (2 * wave + j) + (lane >> 4);
+    const int x = (lane & 15) ^ (r & 15);  // global chunk landing at position lane & 15
+    va[j] = r < M ? (uint32_t)(r * (K * 2) + x * 16) : kBufOOB;
+  }
+  auto issue = [&](int st) {
+    uint8_t* base = smem + (st % kRRing) * kRA;
+    const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((k_lo + st * kRSK) * 2);
+    buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
+    buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
+  };
+  for (int st = 0; st < kRRing - 1 && st < nst; st++) issue(st);
+
+  // wave = (column half h: 64 columns, K quarter q of every stage: 32 values);
+  // lane (c, g) of the 16x16x32 MFMAs: weight row / activation row c, K 8g..8g+7
+  const int c = lane & 15, g = lane >> 4;
+  const int h = wave & 1, q = wave >> 1;
+  v4f acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
+  for (int s = 0; s < nst; s++) {
+    // everything issued before activation stage s (weights, scales) has landed
+    const int ahead = nst - 1 - s < kRRing - 2 ? nst - 1 - s : kRRing - 2;  // later stages in flight
+    static_assert(kRRing - 2 == 2, "wait counts below");
+    if (ahead >= 2) wait_vmcnt<4>();  // two loads per stage
+    else if (ahead == 1) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // stage s visible everywhere; every wave is past stage s-1
+    if (s + kRRing - 1 < nst) issue(s + kRRing - 1);
+    const uint8_t* sa = smem + (s % kRRing) * kRA;
+    v8bf fa[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int r = 16 * t + c;
+      fa[t] = *reinterpret_cast<const v8bf*>(sa + r * 256 + (((4 * q + g) ^ (r & 15)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int col = 64 * h + 16 * j + c;
+      // K values 32q + 8g .. +7 of the stage: code word 4q + g, scale byte 2q + g/2
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(sq + col * qpitch + 64 * s + q * 16 + 4 * g);
+      const uint32_t sb = sc[col * pitch + 8 * s + 2 * q + (g >> 1)];
+      const v8bf fb = dq8_bf16(word, e4m3_to_f32(sb));
+#pragma unroll
+      for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[t], acc[j][t], 0, 0, 0);
+    }
+  }
+  // ---- sum the four K quarters in LDS (in quarter order), then store
+  __syncthreads();  // LDS is free
+  constexpr int kRedPitch = kRBN + 4;  // floats per row of one quarter's 64 x 128 tile
+  static_assert(4 * kRBM * kRedPitch * 4 <= kRSmem, "quarter tiles fit in LDS");
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+      *reinterpret_cast<float4*>(red + (q * kRBM + 16 * t + c) * kRedPitch + 64 * h + 16 * j + 4 * g) =
+          make_float4(acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]);
+  __syncthreads();
+  const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
+  for (int idx = tid; idx < kRBM * kRBN / 4; idx += kRNT) {  // 4 consecutive outputs per item
+    const int m = idx / (kRBN / 4), nl = (idx % (kRBN / 4)) * 4;
+    const int n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    float4 v = *reinterpret_cast<const float4*>(red + m * kRedPitch + nl);
+#pragma unroll
+    for (int qq = 1; qq < 4; qq++) {
+      const float4 u = *reinterpret_cast<const float4*>(red + (qq * kRBM + m) * kRedPitch + nl);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    if (splits == 1)
+      *reinterpret_cast<uint2*>(D + (int64_t)m * N + n) =
+          make_uint2(pack_bf16x2(alpha * v.x, alpha * v.y), pack_bf16x2(alpha * v.z, alpha * v.w));
+    else
+      *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + n) = v;
+  }
+}
+
+// K split of the 64-row kernel: enough work items for the CUs, at least two
+// stages per range, at most kRMaxStages; 0 if no split fits.
+int w4a16_rows64_splits(int64_t N, int64_t K, int cus) {
+  const int64_t tiles = (N + kRBN - 1) / kRBN, total = K / kRSK;
+  int64_t s = 1;
+  while (s < 16 && tiles * (s + 1) <= cus && total / (s + 1) >= 2) s++;
+  while ((total + s - 1) / s > kRMaxStages && s < total) s++;
+  return (total + s - 1) / s <= kRMaxStages ? (int)s : 0;
+}
+
 int w4a16_splits(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int64_t stages = K / kSK;
@@ -277,6 +439,36 @@ hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t
   const unsigned grid = (unsigned)(tiles_m * tiles_n * splits);
   w4a16_tiled<<<grid, kNT, 0, stream>>>(A, B, SFB, alpha, D, (int)M, (int)N, (int)K, tiles_m, tiles_n, splits,
                                         part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(part, splits, alpha, D, M * N, stream);
+}
+
+}  // namespace bsfp4
+
+namespace bsfp4 {
+
+bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_W4A16_ROWS64");  // measurement override: 0 keeps the chunked small-M kernels
+  if (e && e[0] == '0') return false;
+  const int64_t lim = (int64_t)1 << 31;
+  return M > 4 && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
+         w4a16_rows64_splits(N, K, cus_of_device()) > 0;
+}
+
+size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K) {
+  const int s = w4a16_rows64_splits(N, K, cus_of_device());
+  return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
+                               hipStream_t stream) {
+  const int splits = w4a16_rows64_splits(N, K, cus_of_device());
+  if (splits < 1 || (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))))
+    return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)(((N + kRBN - 1) / kRBN) * splits);
+  w4a16_rows64<<<grid, kRNT, 0, stream>>>(A, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, alpha, D, M * N, stream);

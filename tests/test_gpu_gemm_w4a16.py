@@ -66,9 +66,20 @@ def test_w4a16_every_scale_code_no_alpha(M):
 @pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
 @pytest.mark.parametrize("mt4", ["1", "0"])
 def test_w4a16_rows_33_to_64(monkeypatch, mt4, M, N, K):
-    """Rows 33..64 through both kernels (split form with four M tiles, per-wave form)."""
+    """Rows 33..64 through the chunked small-M kernels (split form with four M
+    tiles, per-wave form), the 64-row tiled kernel switched off."""
+    monkeypatch.setenv("BSFP4_W4A16_ROWS64", "0")
     monkeypatch.setenv("BSFP4_SKINNY_MT4", mt4)
     _run_check(*_problem(M, N, K, 700 + M))
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 128, 128), (16, 96, 1024), (33, 4096, 7168), (63, 288, 2048),
+                                   (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160)])
+def test_w4a16_rows64_kernel(M, N, K):
+    """5..64 rows with K % 128 == 0: the 64 x 128 tiled kernel (partial row and
+    column tiles, one or several K ranges, one stage per range); K % 128 != 0
+    takes the chunked small-M kernels."""
+    _run_check(*_problem(M, N, K, 720 + M))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (16, 288, 4160), (29, 1056, 16384)])
@@ -91,7 +102,8 @@ def test_w4a16_rows_above_64_k_not_multiple_of_64(M, N, K):
     _run_check(*_problem(M, N, K, 950 + M))
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 4096, 7168), (512, 6656, 19968), (2048, 19968, 6656)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 7168), (512, 6656, 19968), (2048, 19968, 6656),
+                                   (64, 6656, 19968), (32, 19968, 6656)])
 def test_w4a16_large_sampled(M, N, K):
     """The workload shape at M = 4096 and the two projection shapes of the
     W4A16 follow-up page, checked on sampled rows (first/last tile rows included)."""
@@ -99,7 +111,7 @@ def test_w4a16_large_sampled(M, N, K):
     w = synth.bf16_normal(961, (N, K), 0.02)
     gw = OQ.global_scale(w)
     wq, wsf = OQ.nvfp4_quantize(w, gw)
-    rows = np.unique(np.concatenate([[0, 255, 256, M - 1],
+    rows = np.unique(np.concatenate([[0, 255 % M, 256 % M, M - 1],
                                      np.random.default_rng(2).choice(M, 12, replace=False)]))
     _run_check(a, wq, wsf, np.float32(np.float32(1.0) / gw), rows=rows)
 
