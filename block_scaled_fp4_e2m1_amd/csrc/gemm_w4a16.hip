@@ -238,8 +238,8 @@ __global__ void __launch_bounds__(kNT, 1)
 
 
 // ---------------------------------------------------------------------------
-// W4A16 for 5 <= M <= 64 (rows up to four use the few-row kernel of
-// gemm_skinny.hip): one workgroup = all 64 rows x 128 output columns x one K
+// W4A16 for 33 <= M <= 64 (fewer rows use the kernels of gemm_skinny.hip):
+// one workgroup = all 64 rows x 128 output columns x one K
 // range, 8 waves = 2 column halves x 4 K quarters of every stage: a wave owns
 // 64 columns x 64 rows (16 v_mfma_f32_16x16x32_bf16 tiles) for 32 of the
 // stage's 128 K values, so every weight value is dequantised exactly once per
@@ -249,9 +249,8 @@ __global__ void __launch_bounds__(kNT, 1)
 // L2-resident and are re-read once per 128-column block.
 //   * the weight codes of the workgroup's whole K range (128 rows x K/S/2 bytes,
 //     rows padded by 16 bytes) are copied into LDS first, each row by
-//     consecutive lanes and loads so that HBM sees long row segments (per-stage
-//     64-byte pieces of 128 rows measured several times slower), and so are the
-//     range's weight scales (8 bytes per row and stage);
+//     consecutive lanes and loads so that HBM sees long row segments, and so
+//     are the range's weight scales (8 bytes per row and stage);
 //   * the activations follow in stages of 128 K values through a 4-slot ring
 //     (64 rows x 256 bytes of bf16, the 16-byte chunk x of row r at position
 //     x ^ (r & 15), conflict-free fragment reads), two loads per wave and stage;
@@ -448,11 +447,16 @@ hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t
 
 namespace bsfp4 {
 
+// Used for 33..64 rows: measured with graph replay at N = 4096, K = 7168 it is
+// 4.3 us faster than the chunked small-M kernels at 64 rows, even at 32 rows
+// and slower below.  Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for
+// any 5..64 rows.
 bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
-  const char* e = getenv("BSFP4_W4A16_ROWS64");  // measurement override: 0 keeps the chunked small-M kernels
+  const char* e = getenv("BSFP4_W4A16_ROWS64");
   if (e && e[0] == '0') return false;
+  const int64_t min_rows = (e && e[0] == '1') ? 5 : 33;
   const int64_t lim = (int64_t)1 << 31;
-  return M > 4 && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
+  return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
          w4a16_rows64_splits(N, K, cus_of_device()) > 0;
 }
 

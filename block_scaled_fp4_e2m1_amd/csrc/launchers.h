@@ -44,7 +44,7 @@ size_t w4a16_tiled_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
                               hipStream_t stream);
-// W4A16 for 5 <= M <= 64 (K % 128 == 0): 64 x 128 tiles over K ranges.
+// W4A16 for 33..64 rows (K % 128 == 0): 64 x 128 tiles over K ranges.
 bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K);
 size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,

@@ -75,10 +75,11 @@ def test_w4a16_rows_33_to_64(monkeypatch, mt4, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(5, 128, 128), (16, 96, 1024), (33, 4096, 7168), (63, 288, 2048),
                                    (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160)])
-def test_w4a16_rows64_kernel(M, N, K):
-    """5..64 rows with K % 128 == 0: the 64 x 128 tiled kernel (partial row and
-    column tiles, one or several K ranges, one stage per range); K % 128 != 0
-    takes the chunked small-M kernels."""
+def test_w4a16_rows64_kernel(monkeypatch, M, N, K):
+    """The 64 x 128 tiled kernel forced for any 5..64 rows with K % 128 == 0
+    (partial row and column tiles, one or several K ranges, one stage per
+    range); K % 128 != 0 takes the chunked small-M kernels."""
+    monkeypatch.setenv("BSFP4_W4A16_ROWS64", "1")
     _run_check(*_problem(M, N, K, 720 + M))
 
 
