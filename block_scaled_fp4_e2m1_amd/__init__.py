@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     MOE_WEIGHTED_COMBINE,
     MXFP4,
     NVFP4,
+    SF_LAYOUTS,
     Bsfp4Error,
     global_scale,
     gemm,
@@ -17,6 +18,8 @@ from .binding import (  # noqa: F401
     moe_prep,
     mxfp4_moe_grouped_gemm,
     quantize,
+    scales_swizzle,
+    scales_unswizzle,
     version,
     w4a16_gemm,
 )

@@ -57,6 +57,9 @@ _SIGNATURES = {
     "w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "w4a16_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64,
                                   _c_ptr, _c_size, _c_ptr]),
+    "fp4_scales_swizzled_size": (_c_size, [_c_i64, _c_i64]),
+    "fp4_scales_swizzle": (ctypes.c_int, [ctypes.c_int, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr]),
+    "fp4_scales_unswizzle": (ctypes.c_int, [ctypes.c_int, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr]),
     "fp4_moe_prep_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "fp4_moe_prep": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                     _c_size, _c_ptr]),
@@ -216,6 +219,43 @@ def w4a16_gemm(A, B, SFB, alpha: torch.Tensor | None = None,
     _check(lib.w4a16_gemm(_p(A), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
                           0 if ws is None else ws.numel(), _stream(A.device)), "w4a16_gemm")
     return D
+
+
+SF_LAYOUTS = {"128x4": 0, "128x4_m8": 1}
+
+
+def _sf_layout(layout) -> int:
+    try:
+        return SF_LAYOUTS[layout]
+    except KeyError:
+        raise ValueError(f"unknown scale layout {layout!r}") from None
+
+
+def scales_swizzle(sf: torch.Tensor, layout="128x4", out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major [rows, kblocks] block scales -> padded swizzled [round_up(rows,128), round_up(kblocks,4)]."""
+    _need(sf, torch.uint8, "sf")
+    rows, kblocks = sf.shape
+    R, C = -(-rows // 128) * 128, -(-kblocks // 4) * 4
+    swz = out if out is not None else torch.empty((R, C), dtype=torch.uint8, device=sf.device)
+    _need(swz, torch.uint8, "out")
+    if swz.numel() != R * C:
+        raise ValueError(f"out must hold {R * C} bytes")
+    _check(load().fp4_scales_swizzle(_sf_layout(layout), _p(sf), rows, kblocks, _p(swz), _stream(sf.device)),
+           "fp4_scales_swizzle")
+    return swz
+
+
+def scales_unswizzle(swz: torch.Tensor, rows: int, kblocks: int, layout="128x4",
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Padded swizzled block scales -> row-major [rows, kblocks] (the padding is dropped)."""
+    _need(swz, torch.uint8, "swz")
+    if swz.numel() != load().fp4_scales_swizzled_size(rows, kblocks):
+        raise ValueError("swz does not hold the padded size of (rows, kblocks)")
+    sf = out if out is not None else torch.empty((rows, kblocks), dtype=torch.uint8, device=swz.device)
+    _need(sf, torch.uint8, "out")
+    _check(load().fp4_scales_unswizzle(_sf_layout(layout), _p(swz), rows, kblocks, _p(sf), _stream(swz.device)),
+           "fp4_scales_unswizzle")
+    return sf
 
 
 def moe_prep(topk_ids: torch.Tensor, num_experts: int):

@@ -252,6 +252,46 @@ bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
   return ok();
 }
 
+// ------------------------------------------------------------------ scale layouts
+
+size_t fp4_scales_swizzled_size(int64_t rows, int64_t kblocks) {
+  if (rows < 0 || kblocks <= 0) return 0;
+  return (size_t)((rows + 127) / 128 * 128) * (size_t)((kblocks + 3) / 4 * 4);
+}
+
+static bsfp4_status check_scale_layout(int layout, const void* a, const void* b, int64_t rows, int64_t kblocks,
+                                       const void* swz) {
+  if (layout != BSFP4_SF_128X4 && layout != BSFP4_SF_128X4_M8)
+    return fail(BSFP4_ERR_INVALID_ARG, "unknown scale layout %d", layout);
+  if (rows < 0 || kblocks <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0 and kblocks > 0 (rows=%lld kblocks=%lld)", (long long)rows,
+                (long long)kblocks);
+  if (rows > INT32_MAX || kblocks > INT32_MAX || fp4_scales_swizzled_size(rows, kblocks) >= ((size_t)1 << 31))
+    return fail(BSFP4_ERR_SHAPE, "padded scale buffer must stay below 2^31 bytes");
+  if (rows == 0) return ok();
+  if (a == nullptr || b == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "a scale pointer is NULL");
+  if (!aligned(swz, 4)) return fail(BSFP4_ERR_ALIGNMENT, "the swizzled buffer is not 4-byte aligned");
+  return ok();
+}
+
+bsfp4_status fp4_scales_swizzle(int layout, const uint8_t* sf, int64_t rows, int64_t kblocks, uint8_t* swz,
+                                void* stream) {
+  if (bsfp4_status s = check_scale_layout(layout, sf, swz, rows, kblocks, swz)) return s;
+  if (rows == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_scale_layout(layout, true, sf, swz, rows, kblocks, as_stream(stream)),
+                  "fp4_scales_swizzle launch");
+}
+
+bsfp4_status fp4_scales_unswizzle(int layout, const uint8_t* swz, int64_t rows, int64_t kblocks, uint8_t* sf,
+                                  void* stream) {
+  if (bsfp4_status s = check_scale_layout(layout, swz, sf, rows, kblocks, swz)) return s;
+  if (rows == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_scale_layout(layout, false, swz, sf, rows, kblocks, as_stream(stream)),
+                  "fp4_scales_unswizzle launch");
+}
+
 // ------------------------------------------------------------------ MoE
 
 size_t fp4_moe_prep_workspace_size(int64_t T, int64_t topk, int64_t E) {

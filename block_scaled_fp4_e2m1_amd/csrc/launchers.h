@@ -53,6 +53,11 @@ hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_
 hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,
                                 hipStream_t stream);
 
+// Row-major [rows, kblocks] scales <-> padded 128x4 swizzled layout (0: SM100
+// form, 1: SM103 form); to_swizzled chooses the direction.
+hipError_t launch_scale_layout(int layout, bool to_swizzled, const uint8_t* src, uint8_t* dst, int64_t rows,
+                               int64_t kblocks, hipStream_t stream);
+
 // MXFP4 scaled-MFMA GEMMs (dense and grouped by expert).
 constexpr int kEpiStore = 0;    // bf16 rows
 constexpr int kEpiSilu = 1;     // SiLU(gate) * up, re-quantised to MXFP4

@@ -161,6 +161,40 @@ BSFP4_API bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uin
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * Block-scale layout interchange.  This library keeps block scales row-major,
+ * one byte per block ([rows, K/16] E4M3 or [rows, K/32] E8M0); the pages'
+ * block-scaled GEMMs take them padded to [round_up(rows, 128),
+ * round_up(kblocks, 4)] and swizzled in 512-byte tiles of 128 rows x 4
+ * columns, tile (row tile, column tile) at (row_tile * column_tiles +
+ * column_tile) * 512, the 4 columns of a tile's local row r consecutive at
+ *   BSFP4_SF_128X4     (the SM100 form, also read as the 6-D view
+ *                      (32, 4, rows/128, 4, kblocks/4, 1) of the W4A16 pages):
+ *                      (r % 32) * 16 + (r / 32) * 4
+ *   BSFP4_SF_128X4_M8  (the SM103 form): (r / 16) * 16 + ((r / 4) % 4) * 128
+ *                      + (r % 4) * 4
+ * (vLLM `sm103` branch comparison page, `nvfp4_quant_kernels.cu`: the SM103
+ * scale-offset helper and the SM100 <-> SM103 conversion kernel;
+ * `nvfp4_scaled_mm_entry.cu`: the padded shape checks).  Padding bytes are
+ * written as zeros.  These calls import and export that layout so that scales
+ * prepared for the pages' kernels can be used here and vice versa.
+ *   rows, kblocks  rows >= 0, kblocks > 0, padded size below 2^31 bytes
+ *   sf             device row-major [rows, kblocks] bytes (any alignment)
+ *   swz            device [round_up(rows,128), round_up(kblocks,4)] bytes,
+ *                  4-byte aligned; fp4_scales_swizzled_size() bytes
+ * Byte-exact permutations; nothing is allocated.
+ * ------------------------------------------------------------------------- */
+typedef enum bsfp4_sf_layout {
+  BSFP4_SF_128X4 = 0,
+  BSFP4_SF_128X4_M8 = 1
+} bsfp4_sf_layout;
+
+BSFP4_API size_t fp4_scales_swizzled_size(int64_t rows, int64_t kblocks);
+BSFP4_API bsfp4_status fp4_scales_swizzle(int layout, const uint8_t* sf, int64_t rows, int64_t kblocks,
+                                          uint8_t* swz, void* stream);
+BSFP4_API bsfp4_status fp4_scales_unswizzle(int layout, const uint8_t* swz, int64_t rows, int64_t kblocks,
+                                            uint8_t* sf, void* stream);
+
+/* ----------------------------------------------------------------------------
  * fp4_moe_prep: group routed (token, slot) pairs by expert.  Produces the
  * per-expert row offsets that the pages' experts ops take
  * (`input_offset_by_experts`, vLLM `sm103` branch comparison page,

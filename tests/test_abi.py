@@ -98,3 +98,18 @@ def test_global_scale_validation(lib):
     assert need > 0
     assert f(FAKE, 1 << 20, FAKE, FAKE, need - 4, None) == WORKSPACE
     assert f(FAKE + 1, 1 << 20, FAKE, FAKE, need, None) == ALIGN
+
+
+def test_scale_layout_validation(lib):
+    assert lib.fp4_scales_swizzled_size(200, 13) == 256 * 16
+    assert lib.fp4_scales_swizzled_size(0, 13) == 0
+    f, g = lib.fp4_scales_swizzle, lib.fp4_scales_unswizzle
+    assert f(2, FAKE, 4, 8, FAKE, None) == INVALID and "layout" in _err(lib)
+    assert f(0, FAKE, 4, 0, FAKE, None) == SHAPE
+    assert f(1, FAKE, -1, 8, FAKE, None) == SHAPE
+    assert f(0, None, 4, 8, FAKE, None) == INVALID
+    assert f(0, FAKE, 4, 8, FAKE + 2, None) == ALIGN
+    assert g(0, FAKE + 2, 4, 8, FAKE, None) == ALIGN
+    assert g(1, FAKE, 4, 8, None, None) == INVALID
+    assert f(0, FAKE, 1 << 20, 1 << 12, FAKE, None) == SHAPE and "2^31" in _err(lib)
+    assert f(0, None, 0, 8, None, None) == OK  # empty: a no-op
