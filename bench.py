@@ -18,7 +18,8 @@ The same line carries:
                 committed counter summary matches the current kernel source;
   cpu_baseline  the float64 CPU oracle timed on this host on the same inputs;
   rows          the other hot-path rows (quantiser, small-M GEMM, W4A16,
-                MXFP4 GEMM, MoE layer) with per-launch times, cold and warm.
+                MXFP4 GEMM, MoE layer, the 4-layer quantise+GEMM pipeline)
+                with per-launch times, cold, warm and graph-replayed.
 """
 from __future__ import annotations
 
@@ -344,6 +345,39 @@ def run_rows(torch, bs, synth, timer, only):
             "pipeline_cold": _rate(timer.run(both, cold=True), 2.0 * M * N * K),
             "pipeline_warm": _rate(timer.run(both), 2.0 * M * N * K),
             "pipeline_graph": _rate(timer.graph(both), 2.0 * M * N * K)}
+
+    # The page's 4-layer pipeline (back-to-back activation quantise + NVFP4 GEMM,
+    # N = K = 7168, the same bf16 activation each layer): eager launches against
+    # one HIP graph holding all 8 launches (the launch-gap-free analogue of the
+    # page's PDL arm).  The page's B300 SM103 numbers ride along as context.
+    if want("pipeline_4layer_7168"):
+        N = K = 7168
+        published = {1: (111.65, 107.10), 16: (112.42, 107.07), 64: (120.51, 115.65), 256: (120.83, 115.33),
+                     1024: (151.52, 134.94), 2048: (250.27, 236.35), 4096: (432.38, 416.32)}
+        b = bf16(synth.bf16_normal(180, (N, K), 0.02))
+        gsb = bs.global_scale(b)
+        bq, sfb = bs.quantize(b, "nvfp4", gs=gsb)
+        del b
+        res = {}
+        for M in (1, 16, 64, 256, 1024, 2048, 4096):
+            a = bf16(synth.bf16_normal(181, (M, K)))
+            gsa = torch.tensor([np.float32(0.5)], device=dev)  # a fixed global scale, as on the page
+            aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            asf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+            D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            alpha = torch.tensor([np.float32(1.0)], device=dev)
+
+            def layers():
+                for _ in range(4):
+                    bs.quantize(a, "nvfp4", gs=gsa, q=aq, sf=asf)
+                    bs.gemm(aq, asf, bq, sfb, alpha, out=D)
+            flops = 4 * 2.0 * M * N * K
+            res[f"M={M}"] = {"eager": _rate(timer.run(layers, iters=10), flops),
+                             "graph": _rate(timer.graph(layers, calls=5), flops),
+                             "published_B300_no_pdl_us": published[M][0],
+                             "published_B300_pdl_us": published[M][1]}
+            del a, aq, asf, D
+        rows["pipeline_4layer_7168"] = res
 
     # a5: W4A16 at M=64 and M=1, N=4096, K=7168 (HBM roofline)
     if want("w4a16_4096x7168"):
