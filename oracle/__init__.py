@@ -12,7 +12,8 @@ Layout of the oracle:
   quant.py   -- the NVFP4 and MXFP4 block quantisers and their dequantisers.
   gemm.py    -- NVFP4, MXFP4 and W4A16 GEMMs as the plain definition
                 D = bf16(alpha * dequant(A) @ dequant(B)^T) in float64.
-  moe.py     -- the MXFP4 W4A4 mixture-of-experts layer, stage by stage.
+  moe.py     -- the MXFP4 and NVFP4 W4A4 mixture-of-experts layers, stage by
+                stage.
   layout.py  -- block-scale layout interchange: row-major <-> the pages' padded
                 128x4 swizzled layouts.
   tolerance.py -- the acceptance rule for floating-point outputs.

@@ -1,4 +1,4 @@
-"""MXFP4 W4A4 mixture-of-experts layer, stage by stage (CPU oracle).
+"""MXFP4 and NVFP4 W4A4 mixture-of-experts layers, stage by stage (CPU oracle).
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
@@ -22,13 +22,26 @@ Readings where the pages are silent (listed in the design notes):
   * the combine sums w[t, j] * Y over the token's slots from the unrounded
     down-projection output Y and rounds once to bf16; weights are not
     renormalised.
+
+NVFP4 form (the per-expert NVFP4 ops the vLLM `sm103` branch comparison page
+declares: `scaled_fp4_experts_quant` and `silu_and_mul_scaled_fp4_experts_quant`,
+which take per-expert offsets; their bodies are not printed).  Readings:
+  * each expert e has its own activation global scales gs1[e] (input of
+    gate_up) and gs2[e] (input of down) and its own FP32 GEMM alphas
+    alpha1[e], alpha2[e], the dense NVFP4 conventions applied per expert;
+  * a sorted row of expert e is quantised with the NVFP4 recipe of the dense
+    quantiser using gs of that expert (so the same token routed to two
+    experts may quantise differently and cannot be shared);
+  * h1 = bf16(alpha1[e] * dec(xq) @ dec(W13[e])^T); act = bf16(silu(g) * u)
+    as in the MXFP4 form; act rows are NVFP4-quantised with gs2[e];
+    y = alpha2[e] * dec(aq) @ dec(W2[e])^T unrounded; the same combine.
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .formats import bf16_bits_to_f64, bf16_rne_from_f64
-from .quant import mxfp4_dequantize, mxfp4_quantize
+from .quant import mxfp4_dequantize, mxfp4_quantize, nvfp4_dequantize, nvfp4_quantize
 
 
 def moe_prep(topk_ids, num_experts: int):
@@ -104,6 +117,59 @@ def moe_layer(x_bf16_bits, topk_ids, topk_weights, W13q, W13sf, W2q, W2sf):
     act = silu_mul(h1)
     aq, asf = mxfp4_quantize(act)
     y = grouped_gemm_f64(aq, asf, offsets, W2q, W2sf)
+    out = combine(y, sorted_ids, topk_weights, T)
+    return dict(offsets=offsets, sorted_ids=sorted_ids, xq=xq, xsf=xsf, h1=h1,
+                act=act, aq=aq, asf=asf, y=y, out=out)
+
+
+def _expert_ranges(offsets):
+    offsets = np.asarray(offsets, dtype=np.int64)
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            yield e, lo, hi
+
+
+def nvfp4_rows_quant(x_bf16_bits, offsets, gs_experts):
+    """NVFP4 codes and scales of sorted rows x[r], row r of expert e with gs_experts[e]."""
+    x = np.asarray(x_bf16_bits, dtype=np.uint16)
+    R, K = x.shape
+    gs = np.asarray(gs_experts, dtype=np.float32)
+    q = np.zeros((R, K // 2), dtype=np.uint8)
+    sf = np.zeros((R, K // 16), dtype=np.uint8)
+    for e, lo, hi in _expert_ranges(offsets):
+        q[lo:hi], sf[lo:hi] = nvfp4_quantize(x[lo:hi], gs[e])
+    return q, sf
+
+
+def nvfp4_experts_quant(x_bf16_bits, sorted_ids, topk: int, offsets, gs_experts):
+    """Sorted row r = x[token of r] quantised with the global scale of r's expert."""
+    x = np.asarray(x_bf16_bits, dtype=np.uint16)
+    tokens = np.asarray(sorted_ids, dtype=np.int64) // topk
+    return nvfp4_rows_quant(x[tokens], offsets, gs_experts)
+
+
+def nvfp4_grouped_gemm_f64(Aq, Asf, offsets, Wq, Wsf, alphas) -> np.ndarray:
+    """Per expert e: alpha[e] * dec(A rows of e) @ dec(W[e])^T, unrounded."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    al = np.asarray(alphas, dtype=np.float32).astype(np.float64)
+    out = np.zeros((int(offsets[-1]), Wq.shape[1]), dtype=np.float64)
+    for e, lo, hi in _expert_ranges(offsets):
+        out[lo:hi] = al[e] * (nvfp4_dequantize(Aq[lo:hi], Asf[lo:hi]) @ nvfp4_dequantize(Wq[e], Wsf[e]).T)
+    return out
+
+
+def nvfp4_moe_layer(x_bf16_bits, topk_ids, topk_weights, W13q, W13sf, W2q, W2sf, gs1, alpha1, gs2,
+                    alpha2):
+    """The NVFP4 layer from scratch; the same stage names as moe_layer."""
+    T, topk = np.asarray(topk_ids).shape
+    E = W13q.shape[0]
+    offsets, sorted_ids = moe_prep(topk_ids, E)
+    xq, xsf = nvfp4_experts_quant(x_bf16_bits, sorted_ids, topk, offsets, gs1)
+    h1 = bf16_rne_from_f64(nvfp4_grouped_gemm_f64(xq, xsf, offsets, W13q, W13sf, alpha1))
+    act = silu_mul(h1)
+    aq, asf = nvfp4_rows_quant(act, offsets, gs2)
+    y = nvfp4_grouped_gemm_f64(aq, asf, offsets, W2q, W2sf, alpha2)
     out = combine(y, sorted_ids, topk_weights, T)
     return dict(offsets=offsets, sorted_ids=sorted_ids, xq=xq, xsf=xsf, h1=h1,
                 act=act, aq=aq, asf=asf, y=y, out=out)
