@@ -17,6 +17,9 @@ from .binding import (  # noqa: F401
     moe_layer,
     moe_prep,
     mxfp4_moe_grouped_gemm,
+    nvfp4_experts_quantize,
+    nvfp4_moe_grouped_gemm,
+    nvfp4_moe_layer,
     quantize,
     scales_swizzle,
     scales_unswizzle,

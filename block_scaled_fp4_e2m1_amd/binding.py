@@ -39,6 +39,7 @@ class MoeEpilogueArgs(ctypes.Structure):
         ("topk_weights", _c_ptr),
         ("num_tokens", _c_i64),
         ("topk", _c_i64),
+        ("out_gs", _c_ptr),
     ]
 
 
@@ -69,6 +70,13 @@ _SIGNATURES = {
                                               _c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_int,
                                               ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size,
                                               _c_ptr]),
+    "nvfp4_experts_quantize": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr,
+                                              _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "nvfp4_moe_grouped_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                                        _c_i64]),
+    "nvfp4_moe_grouped_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr,
+                                              _c_ptr, _c_i64, _c_i64, ctypes.c_int,
+                                              ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size, _c_ptr]),
 }
 
 _lib = None
@@ -335,5 +343,85 @@ def moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf):
     aq, asf = mxfp4_moe_grouped_gemm(xq, xsf, offsets, W13, W13sf, MOE_SILU_MUL_QUANT,
                                      a_row_index=sorted_tokens)
     return mxfp4_moe_grouped_gemm(aq, asf, offsets, W2, W2sf, MOE_WEIGHTED_COMBINE,
+                                  sorted_ids=sorted_ids, topk_weights=topk_weights,
+                                  num_tokens=T, topk=topk)
+
+
+def nvfp4_experts_quantize(x, expert_offsets, gs_experts, row_map=None, q=None, sf=None):
+    """NVFP4 rows grouped by expert: row r quantises x[row_map[r]] with the
+    global scale gs_experts[e] of the expert that owns row r."""
+    _need(x, torch.bfloat16, "x")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(gs_experts, torch.float32, "gs_experts")
+    R, K = x.shape
+    rows_out = R
+    if row_map is not None:
+        _need(row_map, torch.int32, "row_map")
+        rows_out = row_map.numel()
+    E = expert_offsets.numel() - 1
+    if q is None:
+        q = torch.empty((rows_out, K // 2), dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty((rows_out, K // 16), dtype=torch.uint8, device=x.device)
+    _check(load().nvfp4_experts_quantize(_p(x), R, K, _p(row_map), _p(expert_offsets), E, _p(gs_experts),
+                                         rows_out, _p(q), _p(sf), _stream(x.device)), "nvfp4_experts_quantize")
+    return q, sf
+
+
+def nvfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, alpha_experts=None, epilogue=MOE_STORE_BF16, *,
+                           out=None, out_q=None, out_sf=None, out_gs=None, sorted_ids=None,
+                           topk_weights=None, num_tokens=0, topk=0):
+    """Grouped NVFP4 GEMM over expert-sorted rows with per-expert alphas; see the C header."""
+    for t, n in ((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf")):
+        _need(t, torch.uint8, n)
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    if alpha_experts is not None:
+        _need(alpha_experts, torch.float32, "alpha_experts")
+    rows, K = Aq.shape[0], Aq.shape[1] * 2
+    E, N = W.shape[0], W.shape[1]
+    dev = Aq.device
+    if epilogue == MOE_STORE_BF16 and out is None:
+        out = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    if epilogue == MOE_SILU_MUL_QUANT:
+        _need(out_gs, torch.float32, "out_gs")
+        if out_q is None:
+            out_q = torch.empty((rows, N // 4), dtype=torch.uint8, device=dev)
+        if out_sf is None:
+            out_sf = torch.empty((rows, N // 32), dtype=torch.uint8, device=dev)
+    if epilogue == MOE_WEIGHTED_COMBINE:
+        _need(sorted_ids, torch.int32, "sorted_ids")
+        _need(topk_weights, torch.float32, "topk_weights")
+        if out is None:
+            out = torch.empty((num_tokens, N), dtype=torch.bfloat16, device=dev)
+    args = MoeEpilogueArgs(
+        out=None if out is None else out.data_ptr(),
+        out_q=None if out_q is None else out_q.data_ptr(),
+        out_sf=None if out_sf is None else out_sf.data_ptr(),
+        sorted_ids=None if sorted_ids is None else sorted_ids.data_ptr(),
+        topk_weights=None if topk_weights is None else topk_weights.data_ptr(),
+        num_tokens=num_tokens, topk=topk,
+        out_gs=None if out_gs is None else out_gs.data_ptr())
+    lib = load()
+    ws = _workspace(lib.nvfp4_moe_grouped_gemm_workspace_size(rows, E, N, K, epilogue, num_tokens), dev)
+    _check(lib.nvfp4_moe_grouped_gemm(_p(Aq), _p(Asf), _p(expert_offsets), E, rows, _p(W), _p(Wsf),
+                                      _p(alpha_experts), N, K, epilogue, ctypes.byref(args), _p(ws),
+                                      0 if ws is None else ws.numel(), _stream(dev)),
+           "nvfp4_moe_grouped_gemm")
+    if epilogue == MOE_SILU_MUL_QUANT:
+        return out_q, out_sf
+    return out
+
+
+def nvfp4_moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf, gs1, alpha1, gs2, alpha2):
+    """The NVFP4 W4A4 MoE layer: routing prep -> per-expert NVFP4 quantisation
+    of each routed row (gs1[e]) -> gate_up grouped GEMM (alpha1[e]) with the
+    fused SiLU-gate + NVFP4 re-quant epilogue (gs2[e]) -> down grouped GEMM
+    (alpha2[e]) with the top-k weighted combine."""
+    T, topk = topk_ids.shape
+    E = W13.shape[0]
+    offsets, sorted_ids, sorted_tokens = moe_prep(topk_ids, E)
+    xq, xsf = nvfp4_experts_quantize(x, offsets, gs1, row_map=sorted_tokens)
+    aq, asf = nvfp4_moe_grouped_gemm(xq, xsf, offsets, W13, W13sf, alpha1, MOE_SILU_MUL_QUANT, out_gs=gs2)
+    return nvfp4_moe_grouped_gemm(aq, asf, offsets, W2, W2sf, alpha2, MOE_WEIGHTED_COMBINE,
                                   sorted_ids=sorted_ids, topk_weights=topk_weights,
                                   num_tokens=T, topk=topk)

@@ -405,4 +405,111 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, int64
                   "mxfp4_moe_grouped_gemm launch");
 }
 
+// ------------------------------------------------------------------ NVFP4 MoE
+
+bsfp4_status nvfp4_experts_quantize(const uint16_t* x, int64_t rows_in, int64_t K, const int32_t* row_map,
+                                    const int32_t* expert_offsets, int64_t E, const float* gs_experts,
+                                    int64_t rows_out, uint8_t* q, uint8_t* sf, void* stream) {
+  if (rows_in < 0 || rows_out < 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0 and K > 0 (rows_in=%lld rows_out=%lld K=%lld)",
+                (long long)rows_in, (long long)rows_out, (long long)K);
+  if (K % 16) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (E <= 0 || E > bsfp4::kMaxExperts)
+    return fail(BSFP4_ERR_SHAPE, "need 0 < E <= %lld (E=%lld)", (long long)bsfp4::kMaxExperts, (long long)E);
+  if (row_map == nullptr && rows_out != rows_in)
+    return fail(BSFP4_ERR_SHAPE, "without row_map rows_out (%lld) must equal rows_in (%lld)",
+                (long long)rows_out, (long long)rows_in);
+  REQUIRE_PTR(expert_offsets);
+  REQUIRE_PTR(gs_experts);
+  if (!aligned(expert_offsets, 4) || !aligned(gs_experts, 4))
+    return fail(BSFP4_ERR_ALIGNMENT, "expert_offsets / gs_experts are not 4-byte aligned");
+  if (rows_out == 0) return ok();
+  if (rows_in > 0) REQUIRE_PTR(x);
+  if (row_map != nullptr && !aligned(row_map, 4)) return fail(BSFP4_ERR_ALIGNMENT, "row_map is not 4-byte aligned");
+  REQUIRE_PTR(q);
+  if (sf == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "sf is NULL");
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_nvfp4_experts_quant(x, rows_in, K, row_map, expert_offsets, E, gs_experts, rows_out,
+                                                    q, sf, as_stream(stream)),
+                  "nvfp4_experts_quantize launch");
+}
+
+size_t nvfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K, int epilogue,
+                                             int64_t num_tokens) {
+  (void)E;
+  (void)K;
+  (void)num_tokens;
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE && rows > 0 && N > 0)
+    return (size_t)rows * (size_t)N * sizeof(float);
+  return 0;
+}
+
+bsfp4_status nvfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, const int32_t* expert_offsets,
+                                    int64_t E, int64_t rows, const uint8_t* W, const uint8_t* Wsf,
+                                    const float* alpha_experts, int64_t N, int64_t K, int epilogue,
+                                    const bsfp4_moe_epilogue_args* ep, void* ws, size_t ws_bytes, void* stream) {
+  if (epilogue != BSFP4_MOE_STORE_BF16 && epilogue != BSFP4_MOE_SILU_MUL_QUANT &&
+      epilogue != BSFP4_MOE_WEIGHTED_COMBINE)
+    return fail(BSFP4_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+  if (ep == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep is NULL");
+  if (rows < 0 || E <= 0 || E > bsfp4::kMaxExperts || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need rows >= 0, 0 < E <= %lld, N > 0, K > 0", (long long)bsfp4::kMaxExperts);
+  if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+  if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
+  if (epilogue == BSFP4_MOE_SILU_MUL_QUANT && N % 64)
+    return fail(BSFP4_ERR_SHAPE, "SILU_MUL_QUANT needs N %% 64 == 0 (got N=%lld)", (long long)N);
+  if (rows > INT32_MAX || N * (K / 2) >= ((int64_t)1 << 31))
+    return fail(BSFP4_ERR_SHAPE, "rows must fit in 31 bits and one expert's N*K/2 bytes below 2^31");
+  REQUIRE_PTR(W);
+  REQUIRE_PTR(Wsf);
+  REQUIRE_PTR(expert_offsets);
+  if (!aligned(expert_offsets, 4)) return fail(BSFP4_ERR_ALIGNMENT, "expert_offsets is not 4-byte aligned");
+  if (alpha_experts != nullptr && !aligned(alpha_experts, 4))
+    return fail(BSFP4_ERR_ALIGNMENT, "alpha_experts is not 4-byte aligned");
+  if (rows > 0) {
+    REQUIRE_PTR(Aq);
+    REQUIRE_PTR(Asf);
+    if (epilogue == BSFP4_MOE_STORE_BF16) {
+      if (ep->out == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "ep.out is NULL");
+      if (!aligned(ep->out, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out is not 16-byte aligned");
+    } else if (epilogue == BSFP4_MOE_SILU_MUL_QUANT) {
+      if (ep->out_q == nullptr || ep->out_sf == nullptr || ep->out_gs == nullptr)
+        return fail(BSFP4_ERR_INVALID_ARG, "ep.out_q / out_sf / out_gs is NULL");
+      if (!aligned(ep->out_q, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out_q is not 16-byte aligned");
+      if (!aligned(ep->out_sf, 2)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out_sf is not 2-byte aligned");
+      if (!aligned(ep->out_gs, 4)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out_gs is not 4-byte aligned");
+    }
+  }
+  const int64_t T = ep->num_tokens;
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
+    if (T <= 0 || ep->topk <= 0 || T * ep->topk != rows)
+      return fail(BSFP4_ERR_SHAPE, "WEIGHTED_COMBINE needs num_tokens*topk == rows (T=%lld topk=%lld rows=%lld)",
+                  (long long)T, (long long)ep->topk, (long long)rows);
+    if (ep->out == nullptr || ep->sorted_ids == nullptr || ep->topk_weights == nullptr)
+      return fail(BSFP4_ERR_INVALID_ARG, "ep.out / sorted_ids / topk_weights is NULL");
+    if (!aligned(ep->out, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ep.out is not 16-byte aligned");
+    const size_t need = nvfp4_moe_grouped_gemm_workspace_size(rows, E, N, K, epilogue, T);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+  }
+  if (rows == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  const hipStream_t st = as_stream(stream);
+  if (epilogue == BSFP4_MOE_WEIGHTED_COMBINE) {
+    float* y = static_cast<float*>(ws);
+    hipError_t e = bsfp4::launch_nvfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, alpha_experts, N, K,
+                                               bsfp4::kEpiCombine, nullptr, nullptr, nullptr, nullptr,
+                                               ep->sorted_ids, y, st);
+    if (e == hipSuccess)
+      e = bsfp4::launch_topk_sum(y, ep->topk_weights, static_cast<uint16_t*>(ep->out), T, ep->topk, N, st);
+    return launched(e, "nvfp4_moe_grouped_gemm launch");
+  }
+  return launched(bsfp4::launch_nvfp4_grouped(Aq, Asf, expert_offsets, E, rows, W, Wsf, alpha_experts, N, K,
+                                              epilogue == BSFP4_MOE_STORE_BF16 ? bsfp4::kEpiStore : bsfp4::kEpiSilu,
+                                              static_cast<uint16_t*>(ep->out), ep->out_q, ep->out_sf, ep->out_gs,
+                                              nullptr, nullptr, st),
+                  "nvfp4_moe_grouped_gemm launch");
+}
+
 }  // extern "C"

@@ -15,6 +15,10 @@ constexpr int64_t kAmaxMaxParts = 1024;
 hipError_t launch_quantize(int fmt, const uint16_t* x, int64_t rows_in, int64_t K, const float* gs,
                            const int32_t* row_map, int64_t rows_out, uint8_t* q, uint8_t* sf,
                            hipStream_t stream);
+// NVFP4 rows grouped by expert, row r of expert e quantised with gs[e].
+hipError_t launch_nvfp4_experts_quant(const uint16_t* x, int64_t rows_in, int64_t K, const int32_t* row_map,
+                                      const int32_t* offsets, int64_t E, const float* gs, int64_t rows_out,
+                                      uint8_t* q, uint8_t* sf, hipStream_t stream);
 
 int global_scale_parts(int64_t numel);
 hipError_t launch_global_scale(const uint16_t* x, int64_t numel, float* gs, float* partial,
@@ -71,6 +75,13 @@ hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int
                                 const uint8_t* Wsf, int64_t N, int64_t K, int epilogue, uint16_t* out,
                                 uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids,
                                 float* y_f32, hipStream_t stream);
+
+// NVFP4 grouped GEMM over per-expert weights, fp16-dequant core (epilogues as
+// above; SILU re-quantises to NVFP4 with the per-expert global scale out_gs).
+hipError_t launch_nvfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* offsets, int64_t E,
+                                int64_t rows, const uint8_t* W, const uint8_t* Wsf, const float* alpha,
+                                int64_t N, int64_t K, int epilogue, uint16_t* out, uint8_t* out_q, uint8_t* out_sf,
+                                const float* out_gs, const int32_t* sorted_ids, float* y, hipStream_t stream);
 
 // MoE routing prep and the combine's helpers.
 hipError_t launch_moe_prep(const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E, int32_t* offsets,

@@ -30,21 +30,37 @@
 namespace bsfp4 {
 namespace {
 
-template <int BLK>
+// kExperts (NVFP4 only): output row r belongs to the expert e with
+// offsets[e] <= r < offsets[e+1] and is quantised with gs_ptr[e]; rows outside
+// [offsets[0], offsets[E]) are written as zeros.
+template <int BLK, bool kExperts = false>
 __global__ void __launch_bounds__(256)
     quantize_blocks(const uint16_t* __restrict__ x, int64_t rows_in, int64_t K,
                     const float* __restrict__ gs_ptr, const int32_t* __restrict__ row_map,
-                    int64_t rows_out, uint8_t* __restrict__ q, uint8_t* __restrict__ sf) {
+                    int64_t rows_out, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                    const int32_t* __restrict__ offsets = nullptr, int num_experts = 0) {
   constexpr bool kNV = (BLK == 16);
+  static_assert(kNV || !kExperts, "per-expert global scales are an NVFP4 form");
   constexpr int kWords = BLK / 2;  // bf16 pairs per block
   const int64_t bpr = K / BLK;
   const int64_t total = rows_out * bpr;
-  const float gs = kNV ? gs_ptr[0] : 1.0f;
+  float gs = kNV && !kExperts ? gs_ptr[0] : 1.0f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t r = i / bpr;
     const int64_t b = i - r * bpr;
-    const int64_t src = row_map ? (int64_t)row_map[r] : r;
+    int64_t src = row_map ? (int64_t)row_map[r] : r;
+    if constexpr (kExperts) {
+      // largest e with offsets[e] <= r (experts without rows share an offset
+      // with the next one, so the search lands on the expert that owns r)
+      int lo = 0, hi = num_experts;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= r) lo = mid; else hi = mid;
+      }
+      if (r < offsets[0] || r >= offsets[num_experts]) src = -1;  // no expert: zero row
+      gs = gs_ptr[lo];
+    }
     uint32_t w[kWords];
     if (src >= 0 && src < rows_in) {
       const uint4* p = reinterpret_cast<const uint4*>(x + src * K + b * BLK);
@@ -165,6 +181,17 @@ hipError_t launch_quantize(int fmt, const uint16_t* x, int64_t rows_in, int64_t 
   } else {
     quantize_blocks<32><<<grid, 256, 0, stream>>>(x, rows_in, K, nullptr, row_map, rows_out, q, sf);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_experts_quant(const uint16_t* x, int64_t rows_in, int64_t K, const int32_t* row_map,
+                                      const int32_t* offsets, int64_t E, const float* gs, int64_t rows_out,
+                                      uint8_t* q, uint8_t* sf, hipStream_t stream) {
+  if (rows_out == 0) return hipSuccess;
+  const int64_t items = rows_out * (K / 16);
+  const int64_t want = (items + 255) / 256;
+  const int grid = (int)(want < kQuantMaxGrid ? want : kQuantMaxGrid);
+  quantize_blocks<16, true><<<grid, 256, 0, stream>>>(x, rows_in, K, gs, row_map, rows_out, q, sf, offsets, (int)E);
   return hipGetLastError();
 }
 

@@ -261,6 +261,9 @@ typedef struct bsfp4_moe_epilogue_args {
   const float* topk_weights;   /* WEIGHTED_COMBINE, [num_tokens * topk] */
   int64_t num_tokens;          /* WEIGHTED_COMBINE */
   int64_t topk;                /* WEIGHTED_COMBINE */
+  const float* out_gs;         /* nvfp4_moe_grouped_gemm SILU_MUL_QUANT: device
+                                  float[E], global scale of act per expert;
+                                  unused by mxfp4_moe_grouped_gemm */
 } bsfp4_moe_epilogue_args;
 
 BSFP4_API size_t mxfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K,
@@ -269,6 +272,61 @@ BSFP4_API bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* 
                                               int64_t a_rows_total, const int32_t* a_row_index,
                                               const int32_t* expert_offsets, int64_t E, int64_t rows,
                                               const uint8_t* W, const uint8_t* Wsf, int64_t N, int64_t K,
+                                              int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
+                                              size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * NVFP4 mixture-of-experts layer: the per-expert NVFP4 ops the vLLM `sm103`
+ * branch comparison page declares (`csrc/ops.h`, `torch_bindings.cpp`:
+ * `scaled_fp4_experts_quant` and `silu_and_mul_scaled_fp4_experts_quant`,
+ * both addressed through per-expert row offsets).  Every expert e carries its
+ * own activation global scale and GEMM alpha (the dense NVFP4 conventions
+ * applied per expert; the op bodies are not printed).
+ *
+ * nvfp4_experts_quantize: output row r (rows grouped by expert, as from
+ * fp4_moe_prep) quantises input row row_map[r] (row r if row_map is NULL)
+ * with the NVFP4 recipe of fp4_quantize, using gs_experts[e] for the expert e
+ * with expert_offsets[e] <= r < expert_offsets[e+1].
+ *   x            device bf16 [rows_in, K], K % 16 == 0
+ *   row_map      device int32 [rows_out] or NULL (then rows_out == rows_in);
+ *                entries outside [0, rows_in) give all-zero rows
+ *   expert_offsets device int32 [E+1], 1 <= E <= 1024, non-decreasing; rows
+ *                outside [offsets[0], offsets[E]) are written as zeros
+ *   gs_experts   device float [E]
+ *   q, sf        device uint8 [rows_out, K/2], [rows_out, K/16]
+ * ------------------------------------------------------------------------- */
+BSFP4_API bsfp4_status nvfp4_experts_quantize(const uint16_t* x, int64_t rows_in, int64_t K,
+                                              const int32_t* row_map, const int32_t* expert_offsets,
+                                              int64_t E, const float* gs_experts, int64_t rows_out,
+                                              uint8_t* q, uint8_t* sf, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * nvfp4_moe_grouped_gemm: for every expert e, rows [off[e], off[e+1]) of the
+ * NVFP4 activations times expert e's NVFP4 weights, alpha_experts[e] applied
+ * to the FP32 accumulator (`cutlass_fp4_group_mm` in the page's op list).
+ * The products are exact (fp16 MFMA on the dequantised values) and accumulate
+ * in FP32, as in fp4_gemm.
+ *   Aq, Asf        device [rows, K/2] codes, [rows, K/16] E4M3 scales,
+ *                  expert-sorted (e.g. from nvfp4_experts_quantize)
+ *   expert_offsets device int32 [E+1], 1 <= E <= 1024
+ *   W, Wsf         device [E, N, K/2], [E, N, K/16]; N*K/2 < 2^31
+ *   alpha_experts  device float [E] or NULL (all 1.0)
+ *   N % 32 == 0 (N % 64 == 0 for SILU_MUL_QUANT), K % 32 == 0
+ *   epilogue       as for mxfp4_moe_grouped_gemm, except that
+ *                  SILU_MUL_QUANT writes NVFP4: ep.out_q [rows, N/4] codes,
+ *                  ep.out_sf [rows, N/32] E4M3 scales, act row of expert e
+ *                  quantised with ep.out_gs[e] (the fused
+ *                  `silu_and_mul_scaled_fp4_experts_quant`, NVFP4 form)
+ *   ws             device workspace of
+ *                  nvfp4_moe_grouped_gemm_workspace_size(...) bytes
+ * Scales as for fp4_gemm: non-negative E4M3 codes.
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t nvfp4_moe_grouped_gemm_workspace_size(int64_t rows, int64_t E, int64_t N, int64_t K,
+                                                       int epilogue, int64_t num_tokens);
+BSFP4_API bsfp4_status nvfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf,
+                                              const int32_t* expert_offsets, int64_t E, int64_t rows,
+                                              const uint8_t* W, const uint8_t* Wsf,
+                                              const float* alpha_experts, int64_t N, int64_t K,
                                               int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
                                               size_t ws_bytes, void* stream);
 

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_hot_path():
     names = declared()
     for fn in ["fp4_quantize", "fp4_gemm", "w4a16_gemm", "mxfp4_moe_grouped_gemm", "fp4_moe_prep",
-               "fp4_global_scale", "bsfp4_last_error"]:
+               "fp4_global_scale", "bsfp4_last_error", "nvfp4_experts_quantize", "nvfp4_moe_grouped_gemm"]:
         assert fn in names
 
 
@@ -42,7 +42,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert not missing, f"declared but not exported: {missing}"
     # nothing else leaks out of the library
     extra = [n for n in exported if not (n.startswith("fp4_") or n.startswith("bsfp4_")
-                                         or n.startswith("w4a16_") or n.startswith("mxfp4_"))]
+                                         or n.startswith("w4a16_") or n.startswith("mxfp4_")
+                                         or n.startswith("nvfp4_"))]
     assert not extra, extra
 
 
@@ -113,3 +114,45 @@ def test_scale_layout_validation(lib):
     assert g(1, FAKE, 4, 8, None, None) == INVALID
     assert f(0, FAKE, 1 << 20, 1 << 12, FAKE, None) == SHAPE and "2^31" in _err(lib)
     assert f(0, None, 0, 8, None, None) == OK  # empty: a no-op
+
+
+def test_nvfp4_moe_validation(lib):
+    import ctypes
+
+    from block_scaled_fp4_e2m1_amd.binding import MoeEpilogueArgs
+    q = lib.nvfp4_experts_quantize
+    #        x     rows K   row_map offs  E  gs    rows_out q     sf
+    assert q(FAKE, 8, 40, None, FAKE, 4, FAKE, 8, FAKE, FAKE, None) == SHAPE and "multiple of 16" in _err(lib)
+    assert q(FAKE, 8, 64, None, FAKE, 0, FAKE, 8, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 8, 64, None, FAKE, 1025, FAKE, 8, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 8, 64, None, FAKE, 4, FAKE, 9, FAKE, FAKE, None) == SHAPE  # rows_out != rows_in
+    assert q(FAKE, 8, 64, None, None, 4, FAKE, 8, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, 8, 64, None, FAKE, 4, None, 8, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, 8, 64, None, FAKE, 4, FAKE + 2, 8, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 8, 64, FAKE + 1, FAKE, 4, FAKE, 8, FAKE, FAKE, None) == ALIGN
+    assert q(None, 0, 64, None, FAKE, 4, FAKE, 0, None, None, None) == OK  # empty: a no-op
+
+    g = lib.nvfp4_moe_grouped_gemm
+    ep = MoeEpilogueArgs(out=FAKE, out_q=FAKE, out_sf=FAKE, out_gs=FAKE)
+
+    def call(epi=0, E=4, rows=64, N=128, K=64, alpha=FAKE, args=ep, ws=None, ws_bytes=0, Aq=FAKE):
+        return g(Aq, FAKE, FAKE, E, rows, FAKE, FAKE, alpha, N, K, epi, ctypes.byref(args) if args else None,
+                 ws, ws_bytes, None)
+
+    assert call(epi=3) == INVALID
+    assert call(args=None) == INVALID
+    assert call(E=0) == SHAPE and call(E=1025) == SHAPE
+    assert call(K=48) == SHAPE and call(N=48) == SHAPE
+    assert call(epi=1, N=96) == SHAPE and "N % 64" in _err(lib)
+    assert call(N=1 << 16, K=1 << 16) == SHAPE and "2^31" in _err(lib)
+    assert call(alpha=FAKE + 2) == ALIGN
+    assert call(Aq=None) == INVALID
+    assert call(epi=1, args=MoeEpilogueArgs(out_q=FAKE, out_sf=FAKE)) == INVALID and "out_gs" in _err(lib)
+    assert call(epi=1, args=MoeEpilogueArgs(out_q=FAKE, out_sf=FAKE + 1, out_gs=FAKE)) == ALIGN
+    comb = MoeEpilogueArgs(out=FAKE, sorted_ids=FAKE, topk_weights=FAKE, num_tokens=8, topk=8)
+    assert call(epi=2, args=comb) == WORKSPACE
+    assert call(epi=2, args=MoeEpilogueArgs(out=FAKE, sorted_ids=FAKE, topk_weights=FAKE, num_tokens=8,
+                                            topk=4)) == SHAPE
+    assert lib.nvfp4_moe_grouped_gemm_workspace_size(64, 4, 128, 64, 2, 8) == 64 * 128 * 4
+    assert lib.nvfp4_moe_grouped_gemm_workspace_size(64, 4, 128, 64, 1, 8) == 0
+    assert call(rows=0, Aq=None) == OK  # no rows: nothing to do
