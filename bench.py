@@ -508,6 +508,86 @@ def run_rows(torch, bs, synth, timer, only):
                                "down_combine": timer.run(gemm2, cold=True)["median_us"]},
             "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
             "bound": "hbm (weights are 83% of the bytes)"}
+
+    # f2: the NVFP4 MoE layer at the same shape (per-expert global scales and
+    # alphas; every routed row quantised with its expert's scale)
+    if want("moe_nvfp4_4096x2048_e128_top8"):
+        T, H, I, E, topk = 4096, 2048, 768, 128, 8
+        R = T * topk
+        x = bf16(synth.bf16_normal(240, (T, H)))
+        ids_np, w_np = synth.routing(241, T, E, topk)
+        ids = torch.from_numpy(ids_np).to(dev)
+        tw = torch.from_numpy(w_np.reshape(-1)).to(dev)
+        w13 = bf16(synth.bf16_normal(242, (E * 2 * I, H), 0.02))
+        g13 = bs.global_scale(w13)
+        W13, W13sf = bs.quantize(w13, "nvfp4", gs=g13)
+        del w13
+        w2 = bf16(synth.bf16_normal(243, (E * H, I), 0.02))
+        g2 = bs.global_scale(w2)
+        W2, W2sf = bs.quantize(w2, "nvfp4", gs=g2)
+        del w2
+        W13, W13sf = W13.view(E, 2 * I, H // 2), W13sf.view(E, 2 * I, H // 16)
+        W2, W2sf = W2.view(E, H, I // 2), W2sf.view(E, H, I // 16)
+        offs, sids, stok = bs.moe_prep(ids, E)
+        gs1 = bs.global_scale(x).expand(E).contiguous()
+        alpha1 = 1.0 / (gs1 * g13)
+        xq, xsf = bs.nvfp4_experts_quantize(x, offs, gs1, row_map=stok)
+        # act scale calibration (setup): the gate_up rows' SiLU-gated amax
+        h1 = bs.nvfp4_moe_grouped_gemm(xq, xsf, offs, W13, W13sf, alpha1, bs.MOE_STORE_BF16).float()
+        act = (torch.nn.functional.silu(h1[:, :I]) * h1[:, I:]).to(torch.bfloat16)
+        gs2 = bs.global_scale(act).expand(E).contiguous()
+        del h1, act
+        alpha2 = 1.0 / (gs2 * g2)
+        aq = torch.empty((R, I // 2), dtype=torch.uint8, device=dev)
+        asf = torch.empty((R, I // 16), dtype=torch.uint8, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        lib = bs.load()
+        import ctypes
+        from block_scaled_fp4_e2m1_amd import binding as B
+        ws_bytes = lib.nvfp4_moe_grouped_gemm_workspace_size(R, E, H, I, bs.MOE_WEIGHTED_COMBINE, T)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def prep():
+            B._check(lib.fp4_moe_prep(B._p(ids), T, topk, E, B._p(offs), B._p(sids), B._p(stok), None, 0,
+                                      B._stream(dev)), "prep")
+
+        def equant():
+            B._check(lib.nvfp4_experts_quantize(B._p(x), T, H, B._p(stok), B._p(offs), E, B._p(gs1), R,
+                                                B._p(xq), B._p(xsf), B._stream(dev)), "equant")
+
+        a1 = B.MoeEpilogueArgs(out_q=aq.data_ptr(), out_sf=asf.data_ptr(), out_gs=gs2.data_ptr())
+        a2 = B.MoeEpilogueArgs(out=out.data_ptr(), sorted_ids=sids.data_ptr(), topk_weights=tw.data_ptr(),
+                               num_tokens=T, topk=topk)
+
+        def gemm1():
+            B._check(lib.nvfp4_moe_grouped_gemm(B._p(xq), B._p(xsf), B._p(offs), E, R, B._p(W13), B._p(W13sf),
+                                                B._p(alpha1), 2 * I, H, bs.MOE_SILU_MUL_QUANT, ctypes.byref(a1),
+                                                None, 0, B._stream(dev)), "gemm1")
+
+        def gemm2():
+            B._check(lib.nvfp4_moe_grouped_gemm(B._p(aq), B._p(asf), B._p(offs), E, R, B._p(W2), B._p(W2sf),
+                                                B._p(alpha2), H, I, bs.MOE_WEIGHTED_COMBINE, ctypes.byref(a2),
+                                                B._p(ws), ws_bytes, B._stream(dev)), "gemm2")
+
+        def layer():
+            prep()
+            equant()
+            gemm1()
+            gemm2()
+        wbytes = W13.numel() + W13sf.numel() + W2.numel() + W2sf.numel()
+        # weights + x read + out written + quantised rows written/read + act codes written/read
+        nbytes = wbytes + 2 * T * H * 2 + 2 * (xq.numel() + xsf.numel()) + 2 * (aq.numel() + asf.numel())
+        flops = 2.0 * R * (2 * I) * H + 2.0 * R * H * I
+        layer()
+        rows["moe_nvfp4_4096x2048_e128_top8"] = {
+            "layer_cold": _rate(timer.run(layer, iters=10, cold=True), flops, nbytes),
+            "layer_warm": _rate(timer.run(layer, iters=10), flops, nbytes),
+            "stages_cold_us": {"prep": timer.run(prep, cold=True)["median_us"],
+                               "experts_quant": timer.run(equant, cold=True)["median_us"],
+                               "gate_up_silu_quant": timer.run(gemm1, cold=True)["median_us"],
+                               "down_combine": timer.run(gemm2, cold=True)["median_us"]},
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "bound": "mfma (fp16 on the exact dequantised values)", "peak_tflops": PEAK["f16"]}
     return rows
 
 

@@ -28,6 +28,7 @@ SOURCES = [
     "gemm_mxfp4.hip",
     "gemm_w4a16.hip",
     "moe.hip",
+    "moe_nvfp4.hip",
     "layout.hip",
 ]
 

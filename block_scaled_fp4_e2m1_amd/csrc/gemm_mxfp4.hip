@@ -626,18 +626,6 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
 
 // Loader waves of the DMA ring (BSFP4_MXFP4_LOADERS, measurement override):
 // 0 = every wave issues its share.
@@ -649,7 +637,7 @@ int loaders() {
 template <int BM, int BN, int WGN, int SK, int EPI>
 hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
   constexpr int NT = 128 * WGN;
-  int64_t grid = (int64_t)cu_count() * wg_per_cu<BM, BN>();
+  int64_t grid = (int64_t)device_cu_count() * wg_per_cu<BM, BN>();
   if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
   if (a.K % 128 == 0) {
     const int l = loaders();

@@ -720,17 +720,6 @@ SkinnyPlan skinny_plan(int64_t N, int64_t K, int cus, int mt) {
   return SkinnyPlan{pick, (int)ksplit};
 }
 
-int skinny_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    n = (hipGetDevice(&dev) == hipSuccess &&
-         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            ? v
-            : 256;
-  }
-  return n;
-}
 
 template <int AKIND, int MT, int NL>
 hipError_t launch_split_nl(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
@@ -748,7 +737,7 @@ template <int AKIND, int MT>
 hipError_t launch_split(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                         const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                         hipStream_t stream) {
-  const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), MT);
+  const SkinnyPlan pl = skinny_plan(N, K, device_cu_count(), MT);
   switch (pl.nl) {
     case 2: return launch_split_nl<AKIND, MT, 2>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
     case 4: return launch_split_nl<AKIND, MT, 4>(A, SFA, B, SFB, alpha, D, M, N, K, pl.ksplit, part, stream);
@@ -923,7 +912,7 @@ size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
   if (use_few(fp4_activations ? 0 : 1, M, N, K)) return 0;
   if (fp4_activations && (use_lds(M, N, K) || use_onepass(M, N, K))) return 0;
   if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;
-  const SkinnyPlan pl = skinny_plan(N, K, skinny_cus(), M <= 16 ? 1 : M <= 32 ? 2 : 4);
+  const SkinnyPlan pl = skinny_plan(N, K, device_cu_count(), M <= 16 ? 1 : M <= 32 ? 2 : 4);
   return pl.ksplit > 1 ? (size_t)pl.ksplit * M * N * sizeof(float) : 0;
 }
 

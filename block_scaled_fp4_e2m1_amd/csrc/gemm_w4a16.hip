@@ -405,17 +405,6 @@ int w4a16_splits(int64_t M, int64_t N, int64_t K, int cus) {
   return s;
 }
 
-int cus_of_device() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    n = (hipGetDevice(&dev) == hipSuccess &&
-         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            ? v
-            : 256;
-  }
-  return n;
-}
 
 }  // namespace
 
@@ -425,14 +414,14 @@ bool w4a16_tiled_ok(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t w4a16_tiled_workspace(int64_t M, int64_t N, int64_t K) {
-  const int s = w4a16_splits(M, N, K, cus_of_device());
+  const int s = w4a16_splits(M, N, K, device_cu_count());
   return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
 hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
                               hipStream_t stream) {
-  int splits = w4a16_splits(M, N, K, cus_of_device());
+  int splits = w4a16_splits(M, N, K, device_cu_count());
   if (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))) splits = 1;
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)((N + kBN - 1) / kBN);
   const unsigned grid = (unsigned)(tiles_m * tiles_n * splits);
@@ -457,18 +446,18 @@ bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const int64_t min_rows = (e && e[0] == '1') ? 5 : 33;
   const int64_t lim = (int64_t)1 << 31;
   return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
-         w4a16_rows64_splits(N, K, cus_of_device()) > 0;
+         w4a16_rows64_splits(N, K, device_cu_count()) > 0;
 }
 
 size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K) {
-  const int s = w4a16_rows64_splits(N, K, cus_of_device());
+  const int s = w4a16_rows64_splits(N, K, device_cu_count());
   return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
 hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                                uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
                                hipStream_t stream) {
-  const int splits = w4a16_rows64_splits(N, K, cus_of_device());
+  const int splits = w4a16_rows64_splits(N, K, device_cu_count());
   if (splits < 1 || (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))))
     return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(((N + kRBN - 1) / kRBN) * splits);

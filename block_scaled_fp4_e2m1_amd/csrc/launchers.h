@@ -9,6 +9,9 @@
 
 namespace bsfp4 {
 
+// Compute units of the current device (cached on first use; 256 if the query fails).
+int device_cu_count();
+
 constexpr int64_t kQuantMaxGrid = 4096;
 constexpr int64_t kAmaxMaxParts = 1024;
 
