@@ -55,9 +55,18 @@ def parse():
     return p.parse_args()
 
 
-def src_sha(name: str) -> str:
-    with open(os.path.join(ROOT, "block_scaled_fp4_e2m1_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_sha(names: str) -> str:
+    """First 16 hex digits of the SHA-256 of the named csrc files (a '+'-joined
+    list), concatenated in that order."""
+    h = hashlib.sha256()
+    for name in names.split("+"):
+        with open(os.path.join(ROOT, "block_scaled_fp4_e2m1_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# the headline kernel's source files: its body and the shared dequantise-once core
+TRAFFIC_SOURCES = "gemm_nvfp4.hip+nvfp4_f16core.h"
 
 
 def stored_traffic(kernel_key: str, source: str):
@@ -216,7 +225,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     alg_bytes = M * K // 2 + M * K // 16 + N * K // 2 + N * K // 16 + 4 + 2 * M * N
 
-    traffic = stored_traffic("nvfp4_gemm_4096x4096x7168", "gemm_nvfp4.hip")
+    traffic = stored_traffic("nvfp4_gemm_4096x4096x7168", TRAFFIC_SOURCES)
     roofline = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK["f16"], "unit": "TFLOP/s",
                 "frac": round(tflops / PEAK["f16"], 4), "traffic": traffic,
                 "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4),
