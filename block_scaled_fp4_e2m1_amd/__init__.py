@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     nvfp4_moe_grouped_gemm,
     nvfp4_moe_layer,
     quantize,
+    quantize_gemm,
     scales_swizzle,
     scales_unswizzle,
     version,

@@ -70,6 +70,9 @@ _SIGNATURES = {
                                               _c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_int,
                                               ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size,
                                               _c_ptr]),
+    "nvfp4_quantize_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_quantize_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64,
+                                           _c_i64, _c_ptr, _c_size, _c_ptr]),
     "nvfp4_experts_quantize": (ctypes.c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr,
                                               _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "nvfp4_moe_grouped_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int,
@@ -207,6 +210,27 @@ def gemm(A, SFA, B, SFB, alpha: torch.Tensor | None = None, fmt="nvfp4",
     ws = _workspace(lib.fp4_gemm_workspace_size(f, M, N, K), A.device)
     _check(lib.fp4_gemm(f, _p(A), _p(SFA), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
                         0 if ws is None else ws.numel(), _stream(A.device)), "fp4_gemm")
+    return D
+
+
+def quantize_gemm(x, gs, B, SFB, alpha: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """D = gemm(quantize(x, "nvfp4", gs), B, SFB, alpha) in one call (one fused
+    kernel for up to four rows)."""
+    _need(x, torch.bfloat16, "x")
+    _need(gs, torch.float32, "gs")
+    _need(B, torch.uint8, "B")
+    _need(SFB, torch.uint8, "SFB")
+    M, K = x.shape
+    N = B.shape[0]
+    if alpha is not None:
+        _need(alpha, torch.float32, "alpha")
+    D = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(D, torch.bfloat16, "out")
+    lib = load()
+    ws = _workspace(lib.nvfp4_quantize_gemm_workspace_size(M, N, K), x.device)
+    _check(lib.nvfp4_quantize_gemm(_p(x), _p(gs), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
+                                   0 if ws is None else ws.numel(), _stream(x.device)), "nvfp4_quantize_gemm")
     return D
 
 

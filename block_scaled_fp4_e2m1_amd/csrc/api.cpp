@@ -405,6 +405,56 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, int64
                   "mxfp4_moe_grouped_gemm launch");
 }
 
+// ------------------------------------------------------------------ quantise + GEMM
+
+namespace {
+int64_t round16(int64_t b) { return (b + 15) / 16 * 16; }
+}  // namespace
+
+size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 || N % 32) return 0;
+  if (bsfp4::nvfp4_fused_quant_gemm_ok(M, N, K)) return 0;
+  return (size_t)(round16(M * (K / 2)) + round16(M * (K / 16))) + bsfp4::nvfp4_gemm_workspace(M, N, K);
+}
+
+bsfp4_status nvfp4_quantize_gemm(const uint16_t* x, const float* gs, const uint8_t* B, const uint8_t* SFB,
+                                 const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(BSFP4_ERR_SHAPE, "need M >= 0, N > 0, K > 0 (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+                (long long)K);
+  if (K % 32) return fail(BSFP4_ERR_SHAPE, "K=%lld is not a multiple of 32", (long long)K);
+  if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
+  REQUIRE_SCALAR_PTR(gs);
+  REQUIRE_PTR(B);
+  REQUIRE_PTR(SFB);
+  if (alpha != nullptr && !aligned(alpha, 4)) return fail(BSFP4_ERR_ALIGNMENT, "alpha is not 4-byte aligned");
+  if (M > 0) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(D);
+  }
+  const size_t need = nvfp4_quantize_gemm_workspace_size(M, N, K);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need)
+      return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
+  }
+  if (M == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  const hipStream_t st = as_stream(stream);
+  if (need == 0)
+    return launched(bsfp4::launch_nvfp4_fused_quant_gemm(x, gs, B, SFB, alpha, D, M, N, K, st),
+                    "nvfp4_quantize_gemm launch");
+  uint8_t* q = static_cast<uint8_t*>(ws);
+  uint8_t* sf = q + round16(M * (K / 2));
+  uint8_t* gws = sf + round16(M * (K / 16));
+  const size_t gws_bytes = ws_bytes - (size_t)(gws - q);
+  hipError_t e = bsfp4::launch_quantize(0, x, M, K, gs, nullptr, M, q, sf, st);
+  if (e == hipSuccess) e = bsfp4::launch_nvfp4_gemm(q, sf, B, SFB, alpha, D, M, N, K, gws, gws_bytes, st);
+  return launched(e, "nvfp4_quantize_gemm launch");
+}
+
 // ------------------------------------------------------------------ NVFP4 MoE
 
 bsfp4_status nvfp4_experts_quantize(const uint16_t* x, int64_t rows_in, int64_t K, const int32_t* row_map,

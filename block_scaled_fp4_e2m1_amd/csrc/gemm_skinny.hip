@@ -31,6 +31,7 @@
 #include "device_common.h"
 #include "launchers.h"
 #include "lds_dma.h"
+#include "quant_device.h"
 
 namespace bsfp4 {
 namespace {
@@ -541,7 +542,9 @@ __global__ void __launch_bounds__(512)
 
 // ---------------------------------------------------------------------------
 // LDS-staged single-pass form for at most four activation rows (decode
-// shapes), NVFP4 (AKIND 0) or bf16 (AKIND 1) activations, K <= 8192.  The
+// shapes), NVFP4 (AKIND 0) or bf16 (AKIND 1) activations, K <= 8192; AKIND 2
+// is the fused quantise + GEMM: bf16 rows quantised to NVFP4 with the global
+// scale gs inside the workgroup (see below).  The
 // weights move exactly as in skinny_lds.  The activation rows, being few, are
 // copied whole into LDS once per workgroup (one contiguous block: rows are
 // contiguous in memory) and, for NVFP4, dequantised there once to fp16 by all
@@ -554,7 +557,7 @@ template <int AKIND, int UW>
 __global__ void __launch_bounds__(512)
     skinny_lds_few(const void* __restrict__ Aptr, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
                    const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
-                   int M, int N, int K) {
+                   int M, int N, int K, const float* __restrict__ gs_ptr = nullptr) {
   constexpr int kMaxK = 1024 * UW;  // nw <= 8 waves of UW units of 128 values
   constexpr int kBScale = 8 * 1024;                                   // 16 x K/16 weight scale block
   constexpr int kBCodes = kLdsMaxWaves * UW * 1024;                   // per-wave [unit][row][64 B]
@@ -625,6 +628,41 @@ __global__ void __launch_bounds__(512)
     }
     __syncthreads();
   }
+  if constexpr (AKIND == 2) {
+    // Fused quantiser: each 16-value block of the bf16 rows (32 contiguous LDS
+    // bytes; the rows are contiguous) goes through the NVFP4 quantiser's
+    // binary32 steps with gs -- s = fl32(fl32(amax/6)*gs) to E4M3 (RNE,
+    // saturating), inv = fl32(gs/dec(s)), codes = E2M1 RNE of fl32(v*inv) --
+    // and is replaced in place by the exact fp16 values code * dec(s), i.e.
+    // what the AKIND 0 path computes from fp4_quantize's output.
+    const float gs = gs_ptr[0];
+    for (int it = tid; it < M * kb16; it += blockDim.x) {
+      uint8_t* blk = lav + 32 * it;
+      const uint4 lo = *reinterpret_cast<const uint4*>(blk), hi = *reinterpret_cast<const uint4*>(blk + 16);
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float v[16];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        v[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+      }
+      const uint32_t scode = e4m3_rne_satfinite((amax / 6.0f) * gs);
+      const float sdec = e4m3_decode(scode);
+      const float inv = (sdec == 0.0f) ? 0.0f : gs / sdec;
+      uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        q0 = e2m1x2_f32(q0, v[2 * t] * inv, v[2 * t + 1] * inv, t);
+        q1 = e2m1x2_f32(q1, v[8 + 2 * t] * inv, v[8 + 2 * t + 1] * inv, t);
+      }
+      const _Float16 sh = e4m3_to_f16(scode);
+      *reinterpret_cast<v8h*>(blk) = dq8_f16(q0, sh);
+      *reinterpret_cast<v8h*>(blk + 16) = dq8_f16(q1, sh);
+    }
+    __syncthreads();
+  }
 
   const int c = lane & 15, g = lane >> 4;
   const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
@@ -650,7 +688,7 @@ __global__ void __launch_bounds__(512)
 #pragma unroll
       for (int q = 0; q < 4; q++) av[q] = *reinterpret_cast<const uint4*>(arow + 256 * i + 16 * q);
     }
-    if constexpr (AKIND == 0) {
+    if constexpr (AKIND != 1) {  // fp16 activations (NVFP4 or fused-quantised)
       const v2h s = __builtin_bit_cast(v2h, ((sb & 0x7Fu) << 7) | ((sb & 0x7F00u) << 15)) *
                     v2h{(_Float16)256.0f, (_Float16)256.0f};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.x, s[0]), __builtin_bit_cast(v8h, av[0]), acc, 0, 0, 0);
@@ -827,13 +865,13 @@ bool use_few(int akind, int64_t M, int64_t N, int64_t K) {
 
 template <int AKIND>
 hipError_t launch_few(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB, const float* alpha,
-                      uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                      uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream, const float* gs = nullptr) {
   const LdsPlan pl = lds_plan(K);
   const dim3 grid((unsigned)(N / 16)), block((unsigned)(64 * pl.nw));
   switch (pl.uw) {
 #define BSFP4_FEW_CASE(u)                                                                                  \
   case u:                                                                                                  \
-    skinny_lds_few<AKIND, u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K); \
+    skinny_lds_few<AKIND, u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, gs); \
     break;
     BSFP4_FEW_CASE(1) BSFP4_FEW_CASE(2) BSFP4_FEW_CASE(3) BSFP4_FEW_CASE(4)
     BSFP4_FEW_CASE(5) BSFP4_FEW_CASE(6) BSFP4_FEW_CASE(7) BSFP4_FEW_CASE(8)
@@ -905,6 +943,16 @@ hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8
 hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                                uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, hipStream_t stream) {
   return launch_kind<1>(A, nullptr, B, SFB, alpha, D, M, N, K, part, stream);
+}
+
+bool nvfp4_fused_quant_gemm_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && K % 32 == 0 && N % 16 == 0 && use_few(1, M, N, K);
+}
+
+hipError_t launch_nvfp4_fused_quant_gemm(const uint16_t* x, const float* gs, const uint8_t* B, const uint8_t* SFB,
+                                         const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                                         hipStream_t stream) {
+  return launch_few<2>(x, nullptr, B, SFB, alpha, D, M, N, K, stream, gs);
 }
 
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {

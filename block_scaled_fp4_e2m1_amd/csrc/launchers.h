@@ -79,6 +79,13 @@ hipError_t launch_mxfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int
                                 uint8_t* out_q, uint8_t* out_sf, const int32_t* sorted_ids,
                                 float* y_f32, hipStream_t stream);
 
+// Fused NVFP4 quantise + GEMM for at most four rows (the bf16 rows quantised
+// with gs inside every workgroup; the same D as fp4_quantize then the GEMM).
+bool nvfp4_fused_quant_gemm_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nvfp4_fused_quant_gemm(const uint16_t* x, const float* gs, const uint8_t* B, const uint8_t* SFB,
+                                         const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
+                                         hipStream_t stream);
+
 // NVFP4 grouped GEMM over per-expert weights, fp16-dequant core (epilogues as
 // above; SILU re-quantises to NVFP4 with the per-expert global scale out_gs).
 hipError_t launch_nvfp4_grouped(const uint8_t* Aq, const uint8_t* Asf, const int32_t* offsets, int64_t E,

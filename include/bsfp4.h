@@ -276,6 +276,29 @@ BSFP4_API bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* 
                                               size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * nvfp4_quantize_gemm: the producer and consumer of a layer in one call,
+ * D = fp4_gemm(NVFP4, fp4_quantize(NVFP4, x, gs), B, SFB, alpha), bit for bit
+ * the output of the two-call sequence.  The HIP counterpart of the pages'
+ * programmatic-dependent-launch overlap of `scaled_fp4_quant_sm103_pdl` and
+ * `cutlass_scaled_fp4_mm_sm103a_pdl` (vLLM `sm103` branch comparison page,
+ * "PDL" benchmarks of the quant + GEMM pair and the 4-layer pipeline): for up
+ * to four rows (decode shapes, K <= 8192) every workgroup quantises the bf16
+ * rows itself while its weight stream is in flight, so there is one kernel
+ * and no intermediate buffer; otherwise the quantiser writes the codes and
+ * scales into the workspace and the GEMM reads them.
+ *   x       device bf16 [M, K]
+ *   gs      device float[1], the activation global scale (e.g. from
+ *           fp4_global_scale)
+ *   B, SFB, alpha, D, M, N, K as for fp4_gemm with BSFP4_NVFP4
+ *   ws      device workspace of nvfp4_quantize_gemm_workspace_size(M, N, K)
+ *           bytes, 16-byte aligned (0 bytes on the fused path)
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t nvfp4_quantize_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+BSFP4_API bsfp4_status nvfp4_quantize_gemm(const uint16_t* x, const float* gs, const uint8_t* B,
+                                           const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M,
+                                           int64_t N, int64_t K, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
  * NVFP4 mixture-of-experts layer: the per-expert NVFP4 ops the vLLM `sm103`
  * branch comparison page declares (`csrc/ops.h`, `torch_bindings.cpp`:
  * `scaled_fp4_experts_quant` and `silu_and_mul_scaled_fp4_experts_quant`,

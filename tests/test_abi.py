@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_hot_path():
     names = declared()
     for fn in ["fp4_quantize", "fp4_gemm", "w4a16_gemm", "mxfp4_moe_grouped_gemm", "fp4_moe_prep",
-               "fp4_global_scale", "bsfp4_last_error", "nvfp4_experts_quantize", "nvfp4_moe_grouped_gemm"]:
+               "fp4_global_scale", "bsfp4_last_error", "nvfp4_experts_quantize", "nvfp4_moe_grouped_gemm",
+               "nvfp4_quantize_gemm"]:
         assert fn in names
 
 
@@ -156,3 +157,21 @@ def test_nvfp4_moe_validation(lib):
     assert lib.nvfp4_moe_grouped_gemm_workspace_size(64, 4, 128, 64, 2, 8) == 64 * 128 * 4
     assert lib.nvfp4_moe_grouped_gemm_workspace_size(64, 4, 128, 64, 1, 8) == 0
     assert call(rows=0, Aq=None) == OK  # no rows: nothing to do
+
+
+def test_quantize_gemm_validation(lib):
+    f = lib.nvfp4_quantize_gemm
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("gs", FAKE), kw.get("B", FAKE), kw.get("SFB", FAKE),
+                         kw.get("alpha", None), kw.get("D", FAKE), kw.get("M", 300), kw.get("N", 64),
+                         kw.get("K", 64), kw.get("ws", None), kw.get("ws_bytes", 0), None]
+    assert f(*args(K=48)) == SHAPE and f(*args(N=48)) == SHAPE and f(*args(M=-1)) == SHAPE
+    assert f(*args(gs=None)) == INVALID and "gs" in _err(lib)
+    assert f(*args(gs=FAKE + 2)) == ALIGN
+    assert f(*args(x=None)) == INVALID
+    assert f(*args(alpha=FAKE + 1)) == ALIGN
+    need = lib.nvfp4_quantize_gemm_workspace_size(300, 64, 64)
+    assert need >= 300 * 32 + 300 * 4
+    assert f(*args()) == WORKSPACE
+    assert f(*args(ws=FAKE + 8, ws_bytes=need)) == ALIGN
+    assert f(*args(M=0, x=None, D=None)) == OK
+    assert lib.nvfp4_quantize_gemm_workspace_size(0, 64, 64) == 0
