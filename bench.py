@@ -358,17 +358,19 @@ def run_rows(torch, bs, synth, timer, only):
     # The page's 4-layer pipeline (back-to-back activation quantise + NVFP4 GEMM,
     # N = K = 7168, the same bf16 activation each layer): eager launches against
     # one HIP graph holding all 8 launches (the launch-gap-free analogue of the
-    # page's PDL arm).  The page's B300 SM103 numbers ride along as context.
+    # page's PDL arm), and for up to four rows the fused quantise + GEMM (one
+    # kernel per layer) in a graph.  The page's B300 SM103 numbers ride along as
+    # context (none is printed for M = 4).
     if want("pipeline_4layer_7168"):
         N = K = 7168
-        published = {1: (111.65, 107.10), 16: (112.42, 107.07), 64: (120.51, 115.65), 256: (120.83, 115.33),
+        published = {1: (111.65, 107.10), 4: (None, None), 16: (112.42, 107.07), 64: (120.51, 115.65), 256: (120.83, 115.33),
                      1024: (151.52, 134.94), 2048: (250.27, 236.35), 4096: (432.38, 416.32)}
         b = bf16(synth.bf16_normal(180, (N, K), 0.02))
         gsb = bs.global_scale(b)
         bq, sfb = bs.quantize(b, "nvfp4", gs=gsb)
         del b
         res = {}
-        for M in (1, 16, 64, 256, 1024, 2048, 4096):
+        for M in (1, 4, 16, 64, 256, 1024, 2048, 4096):
             a = bf16(synth.bf16_normal(181, (M, K)))
             gsa = torch.tensor([np.float32(0.5)], device=dev)  # a fixed global scale, as on the page
             aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
@@ -385,6 +387,16 @@ def run_rows(torch, bs, synth, timer, only):
                              "graph": _rate(timer.graph(layers, calls=5), flops),
                              "published_B300_no_pdl_us": published[M][0],
                              "published_B300_pdl_us": published[M][1]}
+            if M <= 4:
+                # the fused quantise + GEMM: one kernel per layer
+                def fused_layers():
+                    for _ in range(4):
+                        bs.quantize_gemm(a, gsa, bq, sfb, alpha, out=D)
+                fused_layers()
+                ref = D.clone()
+                layers()
+                res[f"M={M}"]["fused_graph"] = _rate(timer.graph(fused_layers, calls=5), flops)
+                res[f"M={M}"]["fused_matches_two_kernels"] = bool(torch.equal(D, ref))
             del a, aq, asf, D
         rows["pipeline_4layer_7168"] = res
 
