@@ -45,6 +45,12 @@ __global__ void __launch_bounds__(256)
   const int64_t bpr = K / BLK;
   const int64_t total = rows_out * bpr;
   float gs = kNV && !kExperts ? gs_ptr[0] : 1.0f;
+  // expert offsets cached in LDS for the per-row search
+  __shared__ int32_t s_off[kExperts ? kMaxExperts + 1 : 1];
+  if constexpr (kExperts) {
+    for (int i = threadIdx.x; i <= num_experts; i += blockDim.x) s_off[i] = offsets[i];
+    __syncthreads();
+  }
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t r = i / bpr;
@@ -56,9 +62,9 @@ __global__ void __launch_bounds__(256)
       int lo = 0, hi = num_experts;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (offsets[mid] <= r) lo = mid; else hi = mid;
+        if (s_off[mid] <= r) lo = mid; else hi = mid;
       }
-      if (r < offsets[0] || r >= offsets[num_experts]) src = -1;  // no expert: zero row
+      if (r < s_off[0] || r >= s_off[num_experts]) src = -1;  // no expert: zero row
       gs = gs_ptr[lo];
     }
     uint32_t w[kWords];

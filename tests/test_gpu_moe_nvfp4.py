@@ -67,6 +67,7 @@ CASES = [
     (200, 256, 192, 6, 3, 30),    # act width 192: three 64-column act tiles
     (150, 96, 96, 5, 2, 40),      # K = 96 (half a load group), act width 96 (1.5 act tiles)
     (300, 512, 256, 16, 4, 50),
+    (48, 64, 64, 1024, 4, 80),    # the largest expert count: mostly empty experts
 ]
 
 
