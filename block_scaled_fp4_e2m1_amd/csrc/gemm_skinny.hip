@@ -544,7 +544,9 @@ __global__ void __launch_bounds__(512)
 // LDS-staged single-pass form for at most four activation rows (decode
 // shapes), NVFP4 (AKIND 0) or bf16 (AKIND 1) activations, K <= 8192; AKIND 2
 // is the fused quantise + GEMM: bf16 rows quantised to NVFP4 with the global
-// scale gs inside the workgroup (see below).  The
+// scale gs inside the workgroup; AKIND 3 (NVFP4, one or two rows) runs the
+// raw E2M1 codes on the scaled FP4 MFMA and applies the E4M3 block scales to
+// the exact per-block dot products (see the main loop).  The
 // weights move exactly as in skinny_lds.  The activation rows, being few, are
 // copied whole into LDS once per workgroup (one contiguous block: rows are
 // contiguous in memory) and, for NVFP4, dequantised there once to fp16 by all
@@ -562,8 +564,10 @@ __global__ void __launch_bounds__(512)
   constexpr int kBScale = 8 * 1024;                                   // 16 x K/16 weight scale block
   constexpr int kBCodes = kLdsMaxWaves * UW * 1024;                   // per-wave [unit][row][64 B]
   constexpr int kAVals = kFewRows * kMaxK * 2;                        // fp16 / bf16 activation rows
-  constexpr int kACodes = AKIND == 0 ? kFewRows * kMaxK / 2 : 0;      // NVFP4 codes before dequantisation
-  constexpr int kAScales = AKIND == 0 ? ((kFewRows * kMaxK / 16 + 1023) / 1024) * 1024 : 0;
+  constexpr bool kFp4A = AKIND == 0 || AKIND == 3;                   // NVFP4 activations
+  constexpr int kACodes = kFp4A ? kFewRows * kMaxK / 2 : 0;           // NVFP4 codes before dequantisation
+  constexpr int kAScales = kFp4A ? ((kFewRows * kMaxK / 16 + 1023) / 1024) * 1024 : 0;
+  static_assert(AKIND != 3 || (kMaxK / 16) * 64 + kFewRows * (kMaxK / 16) * 4 <= kAVals, "scale tables fit");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBScale + kBCodes + kAVals + kACodes + kAScales];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -587,7 +591,7 @@ __global__ void __launch_bounds__(512)
     const int off = wave * 1024 + lane * 16;
     buf_lds16(rbs, off < 16 * kb16 ? (uint32_t)(n0 * kb16 + off) : kBufOOB, 0, lds_u(lsb + wave * 1024));
   }
-  if constexpr (AKIND == 0) {
+  if constexpr (kFp4A) {
     const v4u32 raq = make_rsrc4(Aptr, (int64_t)M * (K / 2));
     const v4u32 ras = make_rsrc4(SFA, (int64_t)M * kb16);
     const int qpieces = (M * (K / 2) + 1023) / 1024, spieces = (M * kb16 + 1023) / 1024;
@@ -664,6 +668,22 @@ __global__ void __launch_bounds__(512)
     __syncthreads();
   }
 
+  // AKIND 3: scale tables in binary32 (E4M3 decoded exactly): weights as
+  // [block][16 columns], activations as [row][block]
+  float* const tsb = reinterpret_cast<float*>(lav);
+  float* const tsa = tsb + (kMaxK / 16) * 16;
+  if constexpr (AKIND == 3) {
+    for (int it = tid; it < 16 * kb16; it += blockDim.x) {
+      const int b = it >> 4, n = it & 15;
+      tsb[it] = e4m3_to_f32(lsb[n * kb16 + b]);
+    }
+    for (int it = tid; it < M * kb16; it += blockDim.x) {
+      const int m = it / kb16, b = it - m * kb16;
+      tsa[m * (kMaxK / 16) + b] = e4m3_to_f32(las[m * kb16 + b]);
+    }
+    __syncthreads();
+  }
+
   const int c = lane & 15, g = lane >> 4;
   const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
   const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
@@ -682,6 +702,37 @@ __global__ void __launch_bounds__(512)
       default: wait_vmcnt<7>(); break;
     }
     const uint4 w = *reinterpret_cast<const uint4*>(lbq + 1024 * i + rd);
+    if constexpr (AKIND == 3) {
+      // Re-blocked onto the scaled FP4 MFMA with unit scales: the second
+      // operand is block-diagonal -- its row c holds activation row c/8's
+      // codes of block c%8 of this 128-value unit and zeros elsewhere -- so
+      // the MFMA yields the per-block dot products of raw E2M1 codes (exact),
+      // and each is scaled by dec(sA)*dec(sB) (exact) before the FP32 sum.
+      const int m = c >> 3, jb = c & 7;
+      const int k_unit = k_lo + 128 * i;
+      const bool live = m < M && (jb >> 1) == g && k_unit + 32 * g < K;
+      uint2 ac = make_uint2(0, 0);
+      if (live) ac = *reinterpret_cast<const uint2*>(laq + m * (K / 2) + k_unit / 2 + 8 * jb);
+      const v8i fy = (jb & 1) ? v8i{0, 0, (int)ac.x, (int)ac.y, 0, 0, 0, 0}
+                              : v8i{(int)ac.x, (int)ac.y, 0, 0, 0, 0, 0, 0};
+      const v8i fx = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fx, fy, v4f{0, 0, 0, 0}, 4, 4, 0, 127, 0, 127);
+      // The MFMA reads every lane's operands, so it must run with all lanes
+      // active: the pin keeps the compiler from sinking it into the
+      // lane-dependent code below, which is branch-free (selects) for the same
+      // reason.  Table reads stay inside the tables (m <= 1, b < kMaxK/16).
+      asm volatile("" : "+v"(d));
+      const int b = k_unit / 16 + jb;  // this lane's block (its output column c)
+      const bool use = m < M && b < kb16;
+      const float sa = tsa[m * (kMaxK / 16) + b];
+      const float4 sb4 = *reinterpret_cast<const float4*>(tsb + b * 16 + 4 * g);
+      acc[0] += (use ? sa * sb4.x : 0.0f) * d[0];
+      acc[1] += (use ? sa * sb4.y : 0.0f) * d[1];
+      acc[2] += (use ? sa * sb4.z : 0.0f) * d[2];
+      acc[3] += (use ? sa * sb4.w : 0.0f) * d[3];
+      asm volatile("" : "+v"(acc));
+      continue;
+    }
     const uint32_t sb = *reinterpret_cast<const uint16_t*>(sbrow + 8 * i);
     uint4 av[4] = {};
     if (c < M && k_lo + 128 * i + 32 * g < K) {
@@ -704,9 +755,23 @@ __global__ void __launch_bounds__(512)
     }
     asm volatile("" : "+v"(acc));  // unit i is done before the next unit's wait
   }
+  if constexpr (AKIND == 3) {
+    // sum the 8 blocks (lanes c = 8m .. 8m+7) into lane 8m, which then holds
+    // column m of rows 4g .. 4g+3, like the other forms' lane (g, c = m)
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[j] += __shfl_xor(acc[j], o, 64);
+  }
   float* red = reinterpret_cast<float*>(lbq);  // 16 x 16 floats: exactly the smallest (1 KB) region
 #pragma unroll
-  for (int j = 0; j < 4; j++) red[(4 * g + j) * 16 + c] = acc[j];
+  for (int j = 0; j < 4; j++) {
+    if constexpr (AKIND == 3) {
+      if ((c & 7) == 0) red[(4 * g + j) * 16 + (c >> 3)] = acc[j];
+    } else {
+      red[(4 * g + j) * 16 + c] = acc[j];
+    }
+  }
   __syncthreads();
   const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
   for (int idx = tid; idx < kFewRows * 8; idx += blockDim.x) {
@@ -917,7 +982,15 @@ template <int AKIND>
 hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                        const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                        hipStream_t stream) {
-  if (use_few(AKIND, M, N, K)) return launch_few<AKIND>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+  if (use_few(AKIND, M, N, K)) {
+    if constexpr (AKIND == 0) {
+      // one or two rows: the re-blocked FP4-MFMA form (BSFP4_FEW_FP4MFMA=0
+      // selects the dequantising form, for measurements and tests)
+      const char* e = getenv("BSFP4_FEW_FP4MFMA");
+      if (M <= 2 && !(e && e[0] == '0')) return launch_few<3>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+    }
+    return launch_few<AKIND>(A, SFA, B, SFB, alpha, D, M, N, K, stream);
+  }
   if (AKIND == 0 && use_lds(M, N, K))
     return launch_lds(static_cast<const uint8_t*>(A), SFA, B, SFB, alpha, D, M, N, K, stream);
   if (AKIND == 0 && use_onepass(M, N, K))

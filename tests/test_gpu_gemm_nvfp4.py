@@ -201,6 +201,19 @@ def test_nvfp4_gemm_small_m_forms(monkeypatch, form, M, N, K):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (2, 96, 4064), (1, 4096, 7168), (2, 4096, 7168),
+                                   (1, 32, 32), (2, 288, 8192), (1, 1056, 96), (2, 160, 1056)])
+@pytest.mark.parametrize("form", ["1", "0"])
+def test_nvfp4_gemm_few_rows_fp4_mfma(monkeypatch, form, M, N, K):
+    """One or two rows on the scaled FP4 MFMA (block-diagonal activation operand,
+    per-block E4M3 scales applied to the exact block dot products; the default)
+    and on the dequantising form."""
+    monkeypatch.setenv("BSFP4_FEW_FP4MFMA", form)
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=600 + M + K)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
 @pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
 @pytest.mark.parametrize("mt4", ["1", "0"])
 def test_nvfp4_gemm_rows_33_to_64(monkeypatch, mt4, M, N, K):
