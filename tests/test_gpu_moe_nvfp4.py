@@ -155,3 +155,30 @@ def test_nvfp4_moe_workload_stagewise():
     rel = TOL.rms(err) / TOL.rms(F.bf16_bits_to_f64(full))
     print(f"end-to-end from scratch: rms rel err {rel:.2e}")
     assert rel <= 0.02
+
+
+def test_nvfp4_moe_single_expert():
+    """E = 1, top-1: every row belongs to the one expert."""
+    d = _inputs(40, 128, 64, 1, 1, 90)
+    _check(d, _run(d))
+
+
+def test_nvfp4_experts_quantize_edges():
+    """Rows whose row_map entry is out of range, and rows outside the expert
+    offsets, are written as zeros; the other rows match the oracle."""
+    T, K, E = 12, 64, 3
+    x = synth.bf16_normal(91, (T, K))
+    offs = np.array([2, 5, 5, 9], np.int32)            # rows 0-1 and 9-10 belong to no expert
+    row_map = np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 9, -1, 30], np.int32)
+    gs = np.array([50.0, 20.0, 400.0], np.float32)
+    q, sf = bs.nvfp4_experts_quantize(dev_bf16(x), dev_i32(offs), dev_f32(gs), row_map=dev_i32(row_map))
+    torch.cuda.synchronize()
+    q, sf = q.cpu().numpy(), sf.cpu().numpy()
+    for r in range(len(row_map)):
+        e = int(np.searchsorted(offs, r, side="right")) - 1
+        src = row_map[r]
+        if not (0 <= e < E and offs[e] <= r < offs[e + 1]) or not (0 <= src < T):
+            assert not q[r].any() and not sf[r].any(), r
+        else:
+            wq, wsf = OQ.nvfp4_quantize(x[src:src + 1], gs[e])
+            assert np.array_equal(q[r], wq[0]) and np.array_equal(sf[r], wsf[0]), r
