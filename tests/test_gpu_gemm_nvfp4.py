@@ -152,7 +152,7 @@ FORCED = [
 ]
 
 
-@pytest.mark.parametrize("variant", ["", "lds4", "reg8", "reg4"])
+@pytest.mark.parametrize("variant", ["", "w8", "lds4", "reg8", "reg4"])
 @pytest.mark.parametrize("M,N,K,splits", FORCED)
 def test_nvfp4_gemm_forced_256_tiles(monkeypatch, variant, M, N, K, splits):
     monkeypatch.setenv("BSFP4_NVFP4_TILE", "256")
@@ -165,11 +165,11 @@ def test_nvfp4_gemm_forced_256_tiles(monkeypatch, variant, M, N, K, splits):
 
 
 @pytest.mark.parametrize("tile", ["128", "256x128"])
-@pytest.mark.parametrize("variant", ["", "reg8"])
+@pytest.mark.parametrize("variant", ["", "w8", "reg8"])
 @pytest.mark.parametrize("M,N,K,splits", [(300, 544, 1056, 1), (513, 768, 2048, 3), (97, 1056, 4160, 5),
                                           (257, 288, 96, 1), (129, 160, 3072, 2)])
 def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, splits):
-    if variant and tile == "256x128":
+    if variant.startswith("reg") and tile == "256x128":
         pytest.skip("the register-dequant kernels have no 256x128 tile")
     monkeypatch.setenv("BSFP4_NVFP4_TILE", tile)
     if variant:
