@@ -13,8 +13,9 @@ What the pages fix:
     epilogue bug": alpha multiplies the FP32 accumulator, followed by one
     conversion to the output type.
   * "feat: sm100 cute_dsl w4a16 gemm" (follow-up PR body, "Description"):
-    W4A16 takes bf16 activations and NVFP4 weights; the tensor-wide FP32
-    weight scale is applied to the FP32 accumulator in the epilogue.
+    W4A16 multiplies bf16 activations by NVFP4 weights, and the one FP32
+    scale of the whole weight tensor multiplies the FP32 sums before the
+    output conversion.
   * "[Kernel] Enable CUTLASS MXFP4 W4A4 MoE on SM12x": MXFP4 x MXFP4 GEMM
     with E8M0 scales per 32 elements.
 
