@@ -1,9 +1,12 @@
 """Thin Python binding of libbsfp4 (ctypes).
 
-Argument marshalling only: each function checks dtypes/contiguity so that
-it can hand raw device pointers to the C ABI, allocates outputs and
-workspace with torch (device memory and streams are all torch is used for),
-and calls the library on the current HIP stream.  Every step of the
+Argument marshalling only: each function checks dtypes, contiguity and the
+exact extents of every tensor it hands over (the C ABI sees raw pointers and
+cannot check how large a buffer is, so an undersized scale or output tensor
+must be refused here), then that all tensors sit on one GPU, allocates
+outputs and workspace with torch (device memory and streams are all torch
+is used for), and calls the library on the current HIP stream.  Shape errors
+raise ValueError before anything reaches the library.  Every step of the
 computation runs in the library's gfx950 kernels; if the library is not
 built, every call raises.
 """
@@ -126,12 +129,42 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
+
+
+def _dims(t, nd, name):
+    if t.dim() != nd:
+        raise ValueError(f"{name} must be {nd}-D, got shape {tuple(t.shape)}")
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t, n, name):
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()} (shape {tuple(t.shape)})")
+
+
+def _device(*named):
+    """Every given tensor must be a GPU tensor, all on the same device."""
+    dev = None
+    for t, name in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    return dev
 
 
 def _workspace(nbytes: int, device):
@@ -156,6 +189,12 @@ def version() -> int:
 def global_scale(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Device float32[1] holding 2688 / max|x| for a bf16 tensor."""
     _need(x, torch.bfloat16, "x")
+    if x.numel() == 0:
+        raise ValueError("x must not be empty")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _numel(out, 1, "out")
+    _device((x, "x"), (out, "out"))
     lib = load()
     gs = out if out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
     ws = _workspace(lib.fp4_global_scale_workspace_size(x.numel()), x.device)
@@ -173,21 +212,35 @@ def quantize(x: torch.Tensor, fmt="nvfp4", gs: torch.Tensor | None = None,
     """
     f = _fmt(fmt)
     _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
+    _dims(x, 2, "x")
     R, K = x.shape
+    blk = 16 if f == NVFP4 else 32
+    if K % blk:
+        raise ValueError(f"K={K} is not a multiple of {blk}")
     if row_map is not None:
         _need(row_map, torch.int32, "row_map")
+        _dims(row_map, 1, "row_map")
         rows_out = row_map.numel()
     else:
         rows_out = R
-    blk = 16 if f == NVFP4 else 32
+    if f == NVFP4:
+        if gs is None:
+            raise ValueError("NVFP4 quantisation needs the global scale gs")
+        _need(gs, torch.float32, "gs")
+        _numel(gs, 1, "gs")
+    elif gs is not None:
+        raise ValueError("MXFP4 quantisation takes no global scale")
+    if q is not None:
+        _need(q, torch.uint8, "q")
+        _shape(q, (rows_out, K // 2), "q")
+    if sf is not None:
+        _need(sf, torch.uint8, "sf")
+        _numel(sf, rows_out * (K // blk), "sf")
+    _device((x, "x"), (row_map, "row_map"), (gs, "gs"), (q, "q"), (sf, "sf"))
     if q is None:
         q = torch.empty((rows_out, K // 2), dtype=torch.uint8, device=x.device)
     if sf is None:
         sf = torch.empty((rows_out, K // blk), dtype=torch.uint8, device=x.device)
-    if gs is not None:
-        _need(gs, torch.float32, "gs")
     lib = load()
     _check(lib.fp4_quantize(f, _p(x), R, K, _p(gs), _p(row_map), rows_out, _p(q), _p(sf),
                             _stream(x.device)), "fp4_quantize")
@@ -200,12 +253,25 @@ def gemm(A, SFA, B, SFB, alpha: torch.Tensor | None = None, fmt="nvfp4",
     f = _fmt(fmt)
     for t, n in ((A, "A"), (SFA, "SFA"), (B, "B"), (SFB, "SFB")):
         _need(t, torch.uint8, n)
+    _dims(A, 2, "A")
+    _dims(B, 2, "B")
     M, K = A.shape[0], A.shape[1] * 2
     N = B.shape[0]
+    if B.shape[1] * 2 != K:
+        raise ValueError(f"A has K={K} but B has K={B.shape[1] * 2}")
+    blk = 16 if f == NVFP4 else 32
+    if K % blk:
+        raise ValueError(f"K={K} is not a multiple of {blk}")
+    _numel(SFA, M * (K // blk), "SFA")
+    _numel(SFB, N * (K // blk), "SFB")
     if alpha is not None:
         _need(alpha, torch.float32, "alpha")
+        _numel(alpha, 1, "alpha")
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        _shape(out, (M, N), "out")
+    _device((A, "A"), (SFA, "SFA"), (B, "B"), (SFB, "SFB"), (alpha, "alpha"), (out, "out"))
     D = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    _need(D, torch.bfloat16, "out")
     lib = load()
     ws = _workspace(lib.fp4_gemm_workspace_size(f, M, N, K), A.device)
     _check(lib.fp4_gemm(f, _p(A), _p(SFA), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
@@ -221,12 +287,24 @@ def quantize_gemm(x, gs, B, SFB, alpha: torch.Tensor | None = None,
     _need(gs, torch.float32, "gs")
     _need(B, torch.uint8, "B")
     _need(SFB, torch.uint8, "SFB")
+    _dims(x, 2, "x")
+    _dims(B, 2, "B")
     M, K = x.shape
     N = B.shape[0]
+    if B.shape[1] * 2 != K:
+        raise ValueError(f"x has K={K} but B has K={B.shape[1] * 2}")
+    if K % 16:
+        raise ValueError(f"K={K} is not a multiple of 16")
+    _numel(gs, 1, "gs")
+    _numel(SFB, N * (K // 16), "SFB")
     if alpha is not None:
         _need(alpha, torch.float32, "alpha")
+        _numel(alpha, 1, "alpha")
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        _shape(out, (M, N), "out")
+    _device((x, "x"), (gs, "gs"), (B, "B"), (SFB, "SFB"), (alpha, "alpha"), (out, "out"))
     D = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    _need(D, torch.bfloat16, "out")
     lib = load()
     ws = _workspace(lib.nvfp4_quantize_gemm_workspace_size(M, N, K), x.device)
     _check(lib.nvfp4_quantize_gemm(_p(x), _p(gs), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
@@ -240,12 +318,23 @@ def w4a16_gemm(A, B, SFB, alpha: torch.Tensor | None = None,
     _need(A, torch.bfloat16, "A")
     _need(B, torch.uint8, "B")
     _need(SFB, torch.uint8, "SFB")
+    _dims(A, 2, "A")
+    _dims(B, 2, "B")
     M, K = A.shape
     N = B.shape[0]
+    if B.shape[1] * 2 != K:
+        raise ValueError(f"A has K={K} but B has K={B.shape[1] * 2}")
+    if K % 16:
+        raise ValueError(f"K={K} is not a multiple of 16")
+    _numel(SFB, N * (K // 16), "SFB")
     if alpha is not None:
         _need(alpha, torch.float32, "alpha")
+        _numel(alpha, 1, "alpha")
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        _shape(out, (M, N), "out")
+    _device((A, "A"), (B, "B"), (SFB, "SFB"), (alpha, "alpha"), (out, "out"))
     D = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    _need(D, torch.bfloat16, "out")
     lib = load()
     ws = _workspace(lib.w4a16_gemm_workspace_size(M, N, K), A.device)
     _check(lib.w4a16_gemm(_p(A), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
@@ -266,12 +355,14 @@ def _sf_layout(layout) -> int:
 def scales_swizzle(sf: torch.Tensor, layout="128x4", out: torch.Tensor | None = None) -> torch.Tensor:
     """Row-major [rows, kblocks] block scales -> padded swizzled [round_up(rows,128), round_up(kblocks,4)]."""
     _need(sf, torch.uint8, "sf")
+    _dims(sf, 2, "sf")
     rows, kblocks = sf.shape
     R, C = -(-rows // 128) * 128, -(-kblocks // 4) * 4
+    if out is not None:
+        _need(out, torch.uint8, "out")
+        _numel(out, R * C, "out")
+    _device((sf, "sf"), (out, "out"))
     swz = out if out is not None else torch.empty((R, C), dtype=torch.uint8, device=sf.device)
-    _need(swz, torch.uint8, "out")
-    if swz.numel() != R * C:
-        raise ValueError(f"out must hold {R * C} bytes")
     _check(load().fp4_scales_swizzle(_sf_layout(layout), _p(sf), rows, kblocks, _p(swz), _stream(sf.device)),
            "fp4_scales_swizzle")
     return swz
@@ -281,10 +372,14 @@ def scales_unswizzle(swz: torch.Tensor, rows: int, kblocks: int, layout="128x4",
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """Padded swizzled block scales -> row-major [rows, kblocks] (the padding is dropped)."""
     _need(swz, torch.uint8, "swz")
-    if swz.numel() != load().fp4_scales_swizzled_size(rows, kblocks):
-        raise ValueError("swz does not hold the padded size of (rows, kblocks)")
+    if rows < 0 or kblocks <= 0:
+        raise ValueError(f"need rows >= 0 and kblocks > 0 (rows={rows}, kblocks={kblocks})")
+    _numel(swz, (-(-rows // 128) * 128) * (-(-kblocks // 4) * 4), "swz")
+    if out is not None:
+        _need(out, torch.uint8, "out")
+        _numel(out, rows * kblocks, "out")
+    _device((swz, "swz"), (out, "out"))
     sf = out if out is not None else torch.empty((rows, kblocks), dtype=torch.uint8, device=swz.device)
-    _need(sf, torch.uint8, "out")
     _check(load().fp4_scales_unswizzle(_sf_layout(layout), _p(swz), rows, kblocks, _p(sf), _stream(swz.device)),
            "fp4_scales_unswizzle")
     return sf
@@ -293,8 +388,11 @@ def scales_unswizzle(swz: torch.Tensor, rows: int, kblocks: int, layout="128x4",
 def moe_prep(topk_ids: torch.Tensor, num_experts: int):
     """(expert_offsets int32 [E+1], sorted_ids int32 [T*topk], sorted_tokens int32 [T*topk])."""
     _need(topk_ids, torch.int32, "topk_ids")
+    _dims(topk_ids, 2, "topk_ids")
+    if num_experts <= 0:
+        raise ValueError(f"num_experts must be > 0, got {num_experts}")
     T, topk = topk_ids.shape
-    dev = topk_ids.device
+    dev = _device((topk_ids, "topk_ids"))
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
     sorted_ids = torch.empty(T * topk, dtype=torch.int32, device=dev)
     sorted_tokens = torch.empty(T * topk, dtype=torch.int32, device=dev)
@@ -304,6 +402,72 @@ def moe_prep(topk_ids: torch.Tensor, num_experts: int):
                             _p(sorted_tokens), _p(ws), 0 if ws is None else ws.numel(), _stream(dev)),
            "fp4_moe_prep")
     return offsets, sorted_ids, sorted_tokens
+
+
+def _moe_common(K, blk, E, N, W, Asf, a_rows, Wsf, expert_offsets):
+    """Extents shared by the grouped GEMMs: W [E, N, K/2] codes, its scales,
+    the activation scales and the expert offsets."""
+    if K % blk:
+        raise ValueError(f"K={K} is not a multiple of {blk}")
+    if W.shape[2] * 2 != K:
+        raise ValueError(f"Aq has K={K} but W has K={W.shape[2] * 2}")
+    _numel(Asf, a_rows * (K // blk), "Asf")
+    _numel(Wsf, E * N * (K // blk), "Wsf")
+    _numel(expert_offsets, E + 1, "expert_offsets")
+
+
+def _moe_outputs(epilogue, rows, N, act_blk, out, out_q, out_sf, sorted_ids, topk_weights, num_tokens, topk):
+    """Output extents of each epilogue (act_blk: 64 values of N per MXFP4
+    act scale byte, i.e. 32 act values; 32 of N per NVFP4 act scale byte)."""
+    if epilogue == MOE_STORE_BF16:
+        if out is not None:
+            _need(out, torch.bfloat16, "out")
+            _shape(out, (rows, N), "out")
+    elif epilogue == MOE_SILU_MUL_QUANT:
+        if N % 64:
+            raise ValueError(f"SILU_MUL_QUANT needs N % 64 == 0 (got N={N})")
+        if out_q is not None:
+            _need(out_q, torch.uint8, "out_q")
+            _shape(out_q, (rows, N // 4), "out_q")
+        if out_sf is not None:
+            _need(out_sf, torch.uint8, "out_sf")
+            _numel(out_sf, rows * (N // act_blk), "out_sf")
+    elif epilogue == MOE_WEIGHTED_COMBINE:
+        if sorted_ids is None or topk_weights is None:
+            raise ValueError("WEIGHTED_COMBINE needs sorted_ids and topk_weights")
+        if num_tokens <= 0 or topk <= 0 or num_tokens * topk != rows:
+            raise ValueError(f"WEIGHTED_COMBINE needs num_tokens * topk == rows "
+                             f"(num_tokens={num_tokens}, topk={topk}, rows={rows})")
+        _need(sorted_ids, torch.int32, "sorted_ids")
+        _numel(sorted_ids, rows, "sorted_ids")
+        _need(topk_weights, torch.float32, "topk_weights")
+        _numel(topk_weights, rows, "topk_weights")
+        if out is not None:
+            _need(out, torch.bfloat16, "out")
+            _shape(out, (num_tokens, N), "out")
+    else:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+
+
+def _moe_layer_shapes(x, topk_ids, topk_weights, W13, W2):
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_weights, torch.float32, "topk_weights")
+    _dims(x, 2, "x")
+    _dims(topk_ids, 2, "topk_ids")
+    _dims(W13, 3, "W13")
+    _dims(W2, 3, "W2")
+    T, H = x.shape
+    _shape(topk_weights, topk_ids.shape, "topk_weights")
+    if topk_ids.shape[0] != T:
+        raise ValueError(f"x has {T} tokens but topk_ids has {topk_ids.shape[0]}")
+    E, two_i, h2 = W13.shape
+    if h2 * 2 != H:
+        raise ValueError(f"W13 has K={h2 * 2} but x has hidden size {H}")
+    if two_i % 2:
+        raise ValueError("W13 must hold gate and up rows (an even row count)")
+    if tuple(W2.shape) != (E, H, two_i // 4):
+        raise ValueError(f"W2 must have shape {(E, H, two_i // 4)}, got {tuple(W2.shape)}")
 
 
 def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_BF16, *,
@@ -316,15 +480,26 @@ def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_B
     for t, n in ((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf")):
         _need(t, torch.uint8, n)
     _need(expert_offsets, torch.int32, "expert_offsets")
+    _dims(Aq, 2, "Aq")
+    _dims(W, 3, "W")
     a_total, K = Aq.shape[0], Aq.shape[1] * 2
     if a_row_index is not None:
         _need(a_row_index, torch.int32, "a_row_index")
+        _dims(a_row_index, 1, "a_row_index")
         if rows is None:
             rows = a_row_index.numel()
+        elif rows > a_row_index.numel():
+            raise ValueError(f"rows={rows} exceeds len(a_row_index)={a_row_index.numel()}")
     elif rows is None:
         rows = a_total
+    elif rows != a_total:
+        raise ValueError(f"without a_row_index rows ({rows}) must equal Aq.shape[0] ({a_total})")
     E, N = W.shape[0], W.shape[1]
-    dev = Aq.device
+    _moe_common(K, 32, E, N, W, Asf, a_total, Wsf, expert_offsets)
+    _moe_outputs(epilogue, rows, N, 64, out, out_q, out_sf, sorted_ids, topk_weights, num_tokens, topk)
+    dev = _device((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf"), (expert_offsets, "expert_offsets"),
+                  (a_row_index, "a_row_index"), (out, "out"), (out_q, "out_q"), (out_sf, "out_sf"),
+                  (sorted_ids, "sorted_ids"), (topk_weights, "topk_weights"))
     if epilogue == MOE_STORE_BF16 and out is None:
         out = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
     if epilogue == MOE_SILU_MUL_QUANT:
@@ -332,11 +507,8 @@ def mxfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, epilogue=MOE_STORE_B
             out_q = torch.empty((rows, N // 4), dtype=torch.uint8, device=dev)
         if out_sf is None:
             out_sf = torch.empty((rows, N // 64), dtype=torch.uint8, device=dev)
-    if epilogue == MOE_WEIGHTED_COMBINE:
-        _need(sorted_ids, torch.int32, "sorted_ids")
-        _need(topk_weights, torch.float32, "topk_weights")
-        if out is None:
-            out = torch.empty((num_tokens, N), dtype=torch.bfloat16, device=dev)
+    if epilogue == MOE_WEIGHTED_COMBINE and out is None:
+        out = torch.empty((num_tokens, N), dtype=torch.bfloat16, device=dev)
     args = MoeEpilogueArgs(
         out=None if out is None else out.data_ptr(),
         out_q=None if out_q is None else out_q.data_ptr(),
@@ -360,6 +532,7 @@ def moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf):
     token once -> gate_up grouped GEMM reading the activations by token, with
     the fused SiLU-gate + MXFP4 re-quant epilogue -> down grouped GEMM with the
     top-k weighted combine."""
+    _moe_layer_shapes(x, topk_ids, topk_weights, W13, W2)
     T, topk = topk_ids.shape
     E = W13.shape[0]
     offsets, sorted_ids, sorted_tokens = moe_prep(topk_ids, E)
@@ -377,12 +550,27 @@ def nvfp4_experts_quantize(x, expert_offsets, gs_experts, row_map=None, q=None, 
     _need(x, torch.bfloat16, "x")
     _need(expert_offsets, torch.int32, "expert_offsets")
     _need(gs_experts, torch.float32, "gs_experts")
+    _dims(x, 2, "x")
     R, K = x.shape
+    if K % 16:
+        raise ValueError(f"K={K} is not a multiple of 16")
     rows_out = R
     if row_map is not None:
         _need(row_map, torch.int32, "row_map")
+        _dims(row_map, 1, "row_map")
         rows_out = row_map.numel()
     E = expert_offsets.numel() - 1
+    if E <= 0:
+        raise ValueError("expert_offsets must hold E + 1 >= 2 entries")
+    _numel(gs_experts, E, "gs_experts")
+    if q is not None:
+        _need(q, torch.uint8, "q")
+        _shape(q, (rows_out, K // 2), "q")
+    if sf is not None:
+        _need(sf, torch.uint8, "sf")
+        _numel(sf, rows_out * (K // 16), "sf")
+    _device((x, "x"), (expert_offsets, "expert_offsets"), (gs_experts, "gs_experts"), (row_map, "row_map"),
+            (q, "q"), (sf, "sf"))
     if q is None:
         q = torch.empty((rows_out, K // 2), dtype=torch.uint8, device=x.device)
     if sf is None:
@@ -399,24 +587,32 @@ def nvfp4_moe_grouped_gemm(Aq, Asf, expert_offsets, W, Wsf, alpha_experts=None, 
     for t, n in ((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf")):
         _need(t, torch.uint8, n)
     _need(expert_offsets, torch.int32, "expert_offsets")
-    if alpha_experts is not None:
-        _need(alpha_experts, torch.float32, "alpha_experts")
+    _dims(Aq, 2, "Aq")
+    _dims(W, 3, "W")
     rows, K = Aq.shape[0], Aq.shape[1] * 2
     E, N = W.shape[0], W.shape[1]
-    dev = Aq.device
+    _moe_common(K, 16, E, N, W, Asf, rows, Wsf, expert_offsets)
+    if alpha_experts is not None:
+        _need(alpha_experts, torch.float32, "alpha_experts")
+        _numel(alpha_experts, E, "alpha_experts")
+    if epilogue == MOE_SILU_MUL_QUANT:
+        if out_gs is None:
+            raise ValueError("SILU_MUL_QUANT needs out_gs (one global scale per expert)")
+        _need(out_gs, torch.float32, "out_gs")
+        _numel(out_gs, E, "out_gs")
+    _moe_outputs(epilogue, rows, N, 32, out, out_q, out_sf, sorted_ids, topk_weights, num_tokens, topk)
+    dev = _device((Aq, "Aq"), (Asf, "Asf"), (W, "W"), (Wsf, "Wsf"), (expert_offsets, "expert_offsets"),
+                  (alpha_experts, "alpha_experts"), (out, "out"), (out_q, "out_q"), (out_sf, "out_sf"),
+                  (out_gs, "out_gs"), (sorted_ids, "sorted_ids"), (topk_weights, "topk_weights"))
     if epilogue == MOE_STORE_BF16 and out is None:
         out = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
     if epilogue == MOE_SILU_MUL_QUANT:
-        _need(out_gs, torch.float32, "out_gs")
         if out_q is None:
             out_q = torch.empty((rows, N // 4), dtype=torch.uint8, device=dev)
         if out_sf is None:
             out_sf = torch.empty((rows, N // 32), dtype=torch.uint8, device=dev)
-    if epilogue == MOE_WEIGHTED_COMBINE:
-        _need(sorted_ids, torch.int32, "sorted_ids")
-        _need(topk_weights, torch.float32, "topk_weights")
-        if out is None:
-            out = torch.empty((num_tokens, N), dtype=torch.bfloat16, device=dev)
+    if epilogue == MOE_WEIGHTED_COMBINE and out is None:
+        out = torch.empty((num_tokens, N), dtype=torch.bfloat16, device=dev)
     args = MoeEpilogueArgs(
         out=None if out is None else out.data_ptr(),
         out_q=None if out_q is None else out_q.data_ptr(),
@@ -441,6 +637,7 @@ def nvfp4_moe_layer(x, topk_ids, topk_weights, W13, W13sf, W2, W2sf, gs1, alpha1
     of each routed row (gs1[e]) -> gate_up grouped GEMM (alpha1[e]) with the
     fused SiLU-gate + NVFP4 re-quant epilogue (gs2[e]) -> down grouped GEMM
     (alpha2[e]) with the top-k weighted combine."""
+    _moe_layer_shapes(x, topk_ids, topk_weights, W13, W2)
     T, topk = topk_ids.shape
     E = W13.shape[0]
     offsets, sorted_ids, sorted_tokens = moe_prep(topk_ids, E)

@@ -47,8 +47,6 @@ CFLAGS = [
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
-    # hardware float atomics (fine on ordinary device memory)
-    "-munsafe-fp-atomics",
     # no packed-FP32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",

@@ -38,6 +38,11 @@ bsfp4_status ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The MXFP4 kernels address an operand with 32-bit buffer offsets from its
+// base (one expert's weights in the grouped form), so each must stay below
+// 2^31 bytes.
+constexpr int64_t kLim31 = (int64_t)1 << 31;
+
 #define REQUIRE_PTR(p)                                                             \
   do {                                                                             \
     if ((p) == nullptr) return fail(BSFP4_ERR_INVALID_ARG, "%s is NULL", #p);      \
@@ -182,6 +187,9 @@ bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8
       return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
     if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
   }
+  if (fmt == BSFP4_MXFP4 && (M * (K / 2) >= kLim31 || N * (K / 2) >= kLim31))
+    return fail(BSFP4_ERR_SHAPE, "MXFP4 operands must stay below 2^31 bytes (M*K/2=%lld, N*K/2=%lld)",
+                (long long)(M * (K / 2)), (long long)(N * (K / 2)));
   if (M == 0) return ok();
   if (bsfp4_status s = check_device()) return s;
   if (fmt == BSFP4_NVFP4)
@@ -356,6 +364,9 @@ bsfp4_status mxfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* Asf, int64
     return fail(BSFP4_ERR_SHAPE, "SILU_MUL_QUANT needs N %% 64 == 0 (got N=%lld)", (long long)N);
   if (rows > INT32_MAX || a_rows_total > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
+  if (a_rows_total * (K / 2) >= kLim31 || N * (K / 2) >= kLim31)
+    return fail(BSFP4_ERR_SHAPE, "Aq (a_rows_total*K/2=%lld) and one expert's W (N*K/2=%lld) must stay below 2^31 bytes",
+                (long long)(a_rows_total * (K / 2)), (long long)(N * (K / 2)));
   REQUIRE_PTR(W);
   REQUIRE_PTR(Wsf);
   REQUIRE_PTR(expert_offsets);

@@ -33,6 +33,7 @@
 // by A and B, which leaves the sum unchanged; each lane's eight values always
 // lie inside one 16-element scale block.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -559,17 +560,20 @@ hipError_t launch_splitk_reduce(const float* part, int splits, const float* alph
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached on first use; 256 if the query fails).
+// Compute units of the current device, cached per device id (a fixed property
+// of the device; 256 if the query fails or the id is out of the cache's range).
 int device_cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    n = (hipGetDevice(&dev) == hipSuccess &&
-         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            ? v
-            : 256;
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {

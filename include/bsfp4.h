@@ -28,8 +28,18 @@
  * status; on error nothing is launched and bsfp4_last_error() returns a
  * message for the calling thread.  Pointers must be 16-byte aligned
  * (128-bit vector loads and stores), except the scalar `gs`/`alpha`
- * pointers (4-byte aligned).  All entry points are thread-safe: the library
- * keeps no state besides the per-thread error message.
+ * pointers (4-byte aligned).  The extent of a buffer cannot be checked
+ * through a pointer: the caller must pass buffers of exactly the documented
+ * sizes (the Python binding checks them).
+ *
+ * State and thread safety: all entry points are thread-safe.  Besides the
+ * per-thread error message, the library caches two fixed properties per
+ * device id (whether it is a gfx950, and its compute-unit count), each filled
+ * on first use without a data race.  The kernel planners also read BSFP4_*
+ * environment variables on every call; these are measurement and test
+ * overrides that force a particular kernel, tile or K split (results stay
+ * within the documented tolerance whichever is chosen) and are unset in
+ * normal use.
  */
 #ifndef BSFP4_H_
 #define BSFP4_H_
@@ -126,7 +136,9 @@ BSFP4_API bsfp4_status fp4_quantize(int fmt, const uint16_t* x, int64_t rows_in,
  *   alpha     device float[1]; NULL means 1.0
  *   D         device bf16 [M, N]
  *   sizes     M >= 0, N % 32 == 0, K % 32 == 0, N > 0, K > 0 (the pages'
- *             `cutlass_scaled_fp4_mm_sm103a_impl` checks)
+ *             `cutlass_scaled_fp4_mm_sm103a_impl` checks); for MXFP4 also
+ *             M*K/2 < 2^31 and N*K/2 < 2^31 (32-bit buffer offsets),
+ *             otherwise BSFP4_ERR_SHAPE
  *   ws        device workspace of fp4_gemm_workspace_size(...) bytes (may be
  *             NULL when that size is 0); its contents need no initialisation
  * NVFP4 block scales are non-negative, as fp4_quantize writes them: the
@@ -230,7 +242,9 @@ BSFP4_API bsfp4_status fp4_moe_prep(const int32_t* topk_ids, int64_t T, int64_t 
  *   expert_offsets   device int32 [E+1] (from fp4_moe_prep), 1 <= E <= 1024
  *   rows             problem rows (T*topk for a routed layer)
  *   W, Wsf           device [E, N, K/2], [E, N, K/32]
- *   N % 32 == 0 (N % 64 == 0 for SILU_MUL_QUANT), K % 32 == 0
+ *   N % 32 == 0 (N % 64 == 0 for SILU_MUL_QUANT), K % 32 == 0;
+ *   a_rows_total*K/2 < 2^31 and N*K/2 < 2^31 (32-bit buffer offsets),
+ *   otherwise BSFP4_ERR_SHAPE
  *   epilogue         one of bsfp4_moe_epilogue; its fields in `ep`:
  *     BSFP4_MOE_STORE_BF16:  ep.out = bf16 [rows, N]
  *     BSFP4_MOE_SILU_MUL_QUANT: act = bf16(silu(h[:, :N/2]) * h[:, N/2:])

@@ -91,6 +91,28 @@ def test_gemm_validation(lib):
     assert f(*args(B=FAKE + 4)) == ALIGN
     assert f(*args(alpha=FAKE + 2)) == ALIGN
     assert f(*args(M=0, A=None, SFA=None, D=None)) == OK  # empty output: nothing to do
+    # MXFP4 operands address with 32-bit offsets: 2^31 bytes or more are refused
+    # before any device query or launch
+    assert f(*args(fmt=1, M=1 << 16, K=1 << 16)) == SHAPE and "2^31" in _err(lib)
+    assert f(*args(fmt=1, N=1 << 16, K=1 << 16)) == SHAPE and "2^31" in _err(lib)
+
+
+def test_mxfp4_grouped_validation(lib):
+    from block_scaled_fp4_e2m1_amd.binding import MoeEpilogueArgs
+    g = lib.mxfp4_moe_grouped_gemm
+    ep = MoeEpilogueArgs(out=FAKE)
+
+    def call(a_total=64, rows=64, N=128, K=64, E=4, epi=0, idx=None):
+        return g(FAKE, FAKE, a_total, idx, FAKE, E, rows, FAKE, FAKE, N, K, epi, ctypes.byref(ep), None, 0, None)
+
+    assert call(epi=7) == INVALID
+    assert call(K=48) == SHAPE
+    assert call(N=96, epi=1) == SHAPE and "N % 64" in _err(lib)
+    assert call(a_total=32) == SHAPE               # without an index, a_rows_total must equal rows
+    # 32-bit offsets: Aq and one expert's W must stay below 2^31 bytes
+    assert call(a_total=1 << 16, rows=1 << 16, K=1 << 16) == SHAPE and "2^31" in _err(lib)
+    assert call(a_total=64, rows=64, N=1 << 16, K=1 << 16) == SHAPE and "2^31" in _err(lib)
+    assert call(a_total=1 << 16, rows=64, K=1 << 16, idx=FAKE) == SHAPE and "2^31" in _err(lib)
 
 
 def test_global_scale_validation(lib):
