@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     NVFP4,
     SF_LAYOUTS,
     Bsfp4Error,
+    e2m1_convert,
     global_scale,
     gemm,
     load,

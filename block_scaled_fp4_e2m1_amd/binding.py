@@ -83,7 +83,12 @@ _SIGNATURES = {
     "nvfp4_moe_grouped_gemm": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr,
                                               _c_ptr, _c_i64, _c_i64, ctypes.c_int,
                                               ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size, _c_ptr]),
+    "bsfp4_e2m1_convert": (ctypes.c_int, [ctypes.c_int, _c_ptr, _c_ptr, _c_i64, _c_ptr, _c_ptr]),
 }
+
+CVT_F32 = 0
+CVT_BF16_E8M0 = 1
+CVT_F32_E8M0 = 2
 
 _lib = None
 
@@ -340,6 +345,35 @@ def w4a16_gemm(A, B, SFB, alpha: torch.Tensor | None = None,
     _check(lib.w4a16_gemm(_p(A), _p(B), _p(SFB), _p(alpha), _p(D), M, N, K, _p(ws),
                           0 if ws is None else ws.numel(), _stream(A.device)), "w4a16_gemm")
     return D
+
+
+def e2m1_convert(values: torch.Tensor, scale_codes: torch.Tensor | None = None) -> torch.Tensor:
+    """E2M1 codes of value pairs by the kernels' own converters (diagnostic).
+
+    values: float32 [2n] (scale 1 without scale_codes, else pair i divided by
+    2^(scale_codes[i] - 127)) or bf16 [2n] (scale_codes required); n % 4 == 0.
+    Returns uint8 [n]: code of value 2i in the low nibble of byte i."""
+    if not isinstance(values, torch.Tensor) or values.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("values must be a float32 or bfloat16 tensor")
+    _need(values, values.dtype, "values")
+    _dims(values, 1, "values")
+    if values.numel() % 8:
+        raise ValueError("values must hold a multiple of 8 elements (4 pairs)")
+    pairs = values.numel() // 2
+    if values.dtype == torch.bfloat16:
+        if scale_codes is None:
+            raise ValueError("bf16 values need scale_codes")
+        mode = CVT_BF16_E8M0
+    else:
+        mode = CVT_F32 if scale_codes is None else CVT_F32_E8M0
+    if scale_codes is not None:
+        _need(scale_codes, torch.uint8, "scale_codes")
+        _numel(scale_codes, pairs, "scale_codes")
+    dev = _device((values, "values"), (scale_codes, "scale_codes"))
+    codes = torch.empty(pairs, dtype=torch.uint8, device=dev)
+    _check(load().bsfp4_e2m1_convert(mode, _p(values), _p(scale_codes), pairs, _p(codes), _stream(dev)),
+           "bsfp4_e2m1_convert")
+    return codes
 
 
 SF_LAYOUTS = {"128x4": 0, "128x4_m8": 1}

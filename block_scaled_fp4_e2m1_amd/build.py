@@ -30,6 +30,7 @@ SOURCES = [
     "moe.hip",
     "moe_nvfp4.hip",
     "layout.hip",
+    "e2m1_convert.hip",
 ]
 
 ARCH = "gfx950"

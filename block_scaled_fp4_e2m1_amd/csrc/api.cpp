@@ -260,6 +260,26 @@ bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
   return ok();
 }
 
+// ------------------------------------------------------------------ E2M1 conversion
+
+bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
+                                uint8_t* codes, void* stream) {
+  if (mode != BSFP4_CVT_F32 && mode != BSFP4_CVT_BF16_E8M0 && mode != BSFP4_CVT_F32_E8M0)
+    return fail(BSFP4_ERR_INVALID_ARG, "unknown conversion mode %d", mode);
+  if (pairs < 0 || pairs % 4)
+    return fail(BSFP4_ERR_SHAPE, "pairs must be >= 0 and a multiple of 4 (got %lld)", (long long)pairs);
+  if (mode == BSFP4_CVT_F32) {
+    if (scale_codes != nullptr) return fail(BSFP4_ERR_INVALID_ARG, "BSFP4_CVT_F32 takes no scale codes");
+  }
+  if (pairs == 0) return ok();
+  REQUIRE_PTR(in);
+  REQUIRE_PTR(codes);
+  if (mode != BSFP4_CVT_F32) REQUIRE_PTR(scale_codes);
+  if (bsfp4_status s = check_device()) return s;
+  return launched(bsfp4::launch_e2m1_convert(mode, in, scale_codes, pairs, codes, as_stream(stream)),
+                  "bsfp4_e2m1_convert launch");
+}
+
 // ------------------------------------------------------------------ scale layouts
 
 size_t fp4_scales_swizzled_size(int64_t rows, int64_t kblocks) {

@@ -601,14 +601,13 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
           }
           amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
           const uint32_t sc = e8m0_ceil(amax / 6.0f);
-          const float scale = __uint_as_float(sc == 0 ? 0x00400000u : sc << 23);  // 2^(sc - 127)
           // piece q: codes of columns 8q + 4g .. +3 (two bytes, first column in the low nibble)
           uint32_t piece[4];
 #pragma unroll
           for (int q = 0; q < 4; q++) {
             uint32_t w2 = 0;
-            w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, a[4 * q], a[4 * q + 1], scale, 0);
-            w2 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w2, a[4 * q + 2], a[4 * q + 3], scale, 1);
+            w2 = e2m1x2_f32_pow2(w2, a[4 * q], a[4 * q + 1], sc, 0);
+            w2 = e2m1x2_f32_pow2(w2, a[4 * q + 2], a[4 * q + 3], sc, 1);
             piece[q] = w2 & 0xFFFFu;
           }
           // block dword q = piece q of lane g = 0 | piece q of lane g = 1 << 16;

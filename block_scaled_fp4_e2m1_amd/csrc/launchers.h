@@ -23,6 +23,10 @@ hipError_t launch_nvfp4_experts_quant(const uint16_t* x, int64_t rows_in, int64_
                                       const int32_t* offsets, int64_t E, const float* gs, int64_t rows_out,
                                       uint8_t* q, uint8_t* sf, hipStream_t stream);
 
+// E2M1 codes of caller-given value pairs (see bsfp4_e2m1_convert); pairs % 4 == 0.
+hipError_t launch_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
+                               uint8_t* codes, hipStream_t stream);
+
 int global_scale_parts(int64_t numel);
 hipError_t launch_global_scale(const uint16_t* x, int64_t numel, float* gs, float* partial,
                                hipStream_t stream);

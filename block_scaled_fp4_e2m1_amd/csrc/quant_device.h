@@ -53,10 +53,12 @@ __device__ __forceinline__ float e8m0_inverse(uint32_t c) {
 // even code, saturating at 6, the sign bit kept (so -0 and negatives that
 // round to zero give code 8).  These are the encoder's rules: E2M1 magnitudes
 // {0, 0.5, 1, 1.5, 2, 3, 4, 6} with midpoints 0.25, 0.75, 1.25, 1.75, 2.5,
-// 3.5, 5 rounding to the code with mantissa bit 0.  Checked on the GPU against
-// a counting-midpoint encoder for 2^20 random pairs incl. every midpoint, both
-// signs, zeros, subnormals and +-inf (NaN inputs are outside the contract: the
-// instruction gives code 7).
+// 3.5, 5 rounding to the code with mantissa bit 0.  The three helpers below
+// are exported unchanged through bsfp4_e2m1_convert, and the GPU test
+// tests/test_gpu_e2m1_converters.py holds them bit for bit to the oracle's
+// encoder: every non-NaN bf16 pattern at several E8M0 scales, every E2M1
+// midpoint and grid point +-1..3 ulp, subnormals, +-0, +-inf and dense random
+// binary32 sweeps (NaN inputs are outside the contract).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // codes of (a, b), scale 1
@@ -80,6 +82,18 @@ __device__ __forceinline__ uint32_t e2m1x2_bf16_pow2(uint32_t word, uint32_t pai
     case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, v, scale, 1);
     case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, v, scale, 2);
     default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, v, scale, 3);
+  }
+}
+
+// codes of the binary32 values (a, b) divided by 2^(scode - 127), an E8M0
+// scale (the MXFP4 re-quantisation of the fused SiLU-mul epilogue)
+__device__ __forceinline__ uint32_t e2m1x2_f32_pow2(uint32_t word, float a, float b, uint32_t scode, int sel) {
+  const float scale = __uint_as_float(scode == 0 ? 0x00400000u : scode << 23);
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, scale, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, scale, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, scale, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, a, b, scale, 3);
   }
 }
 

@@ -367,6 +367,40 @@ BSFP4_API bsfp4_status nvfp4_moe_grouped_gemm(const uint8_t* Aq, const uint8_t* 
                                               int epilogue, const bsfp4_moe_epilogue_args* ep, void* ws,
                                               size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------------------------------------
+ * Diagnostics.
+ *
+ * bsfp4_e2m1_convert: E2M1 codes of caller-given value pairs, computed by the
+ * very device routines the quantiser kernels and the fused SiLU-mul + MXFP4
+ * epilogue use (gfx950's v_cvt_scalef32_pk_fp4_* instructions), so that the
+ * hardware rounding can be held to a reference encoder.  The pages name the
+ * per-block routine (`cvt_warp_fp16_to_fp4`, `cvt_fp16_to_fp4_sm103`, vLLM
+ * `sm103` branch comparison page, `nvfp4_quant_kernels.cu`) without printing
+ * it; the rule implemented is nearest E2M1 value, ties to the even code,
+ * saturation at 6, sign bit kept.
+ *   mode         BSFP4_CVT_F32: `in` holds 2*pairs binary32 values (the
+ *                NVFP4 quantiser's fl32(v * inv)), scale 1;
+ *                BSFP4_CVT_BF16_E8M0: `in` holds 2*pairs bf16 values, pair i
+ *                divided by 2^(scale_codes[i] - 127) (the MXFP4 quantiser);
+ *                BSFP4_CVT_F32_E8M0: 2*pairs binary32 values, pair i divided
+ *                by 2^(scale_codes[i] - 127) (the fused SiLU-mul epilogue)
+ *   in           device, 16-byte aligned
+ *   scale_codes  device uint8 [pairs] E8M0 codes 0..254 (NULL for
+ *                BSFP4_CVT_F32), 16-byte aligned
+ *   pairs        >= 0, a multiple of 4
+ *   codes        device uint8 [pairs]: byte i = code of value 2i (low nibble)
+ *                | code of value 2i+1 << 4
+ * NaN inputs are outside the contract.
+ * ------------------------------------------------------------------------- */
+typedef enum bsfp4_cvt_mode {
+  BSFP4_CVT_F32 = 0,
+  BSFP4_CVT_BF16_E8M0 = 1,
+  BSFP4_CVT_F32_E8M0 = 2
+} bsfp4_cvt_mode;
+
+BSFP4_API bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
+                                          uint8_t* codes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

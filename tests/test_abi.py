@@ -115,6 +115,17 @@ def test_mxfp4_grouped_validation(lib):
     assert call(a_total=1 << 16, rows=64, K=1 << 16, idx=FAKE) == SHAPE and "2^31" in _err(lib)
 
 
+def test_e2m1_convert_validation(lib):
+    f = lib.bsfp4_e2m1_convert
+    assert f(3, FAKE, None, 8, FAKE, None) == INVALID
+    assert f(0, FAKE, None, 6, FAKE, None) == SHAPE          # pairs % 4
+    assert f(0, FAKE, None, -4, FAKE, None) == SHAPE
+    assert f(0, FAKE, FAKE, 8, FAKE, None) == INVALID        # the unit-scale form takes no scales
+    assert f(1, FAKE, None, 8, FAKE, None) == INVALID        # the E8M0 forms need them
+    assert f(2, FAKE + 4, FAKE, 8, FAKE, None) == ALIGN
+    assert f(0, None, None, 0, None, None) == OK             # empty: a no-op
+
+
 def test_global_scale_validation(lib):
     f = lib.fp4_global_scale
     assert f(FAKE, 0, FAKE, FAKE, 1024, None) == SHAPE
