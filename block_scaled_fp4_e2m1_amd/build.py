@@ -31,6 +31,7 @@ SOURCES = [
     "moe_nvfp4.hip",
     "layout.hip",
     "e2m1_convert.hip",
+    "scratch.hip",
 ]
 
 ARCH = "gfx950"

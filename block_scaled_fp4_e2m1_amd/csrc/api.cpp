@@ -162,9 +162,11 @@ size_t fp4_gemm_workspace_size(int fmt, int64_t M, int64_t N, int64_t K) {
   return 0;
 }
 
-bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
-                      const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M, int64_t N,
-                      int64_t K, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks shared by fp4_gemm and fp4_gemm_noalloc (everything but the
+// workspace).
+static bsfp4_status check_gemm_args(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                                    const uint8_t* SFB, const float* alpha, const uint16_t* D, int64_t M, int64_t N,
+                                    int64_t K) {
   if (fmt != BSFP4_NVFP4 && fmt != BSFP4_MXFP4) return fail(BSFP4_ERR_INVALID_ARG, "unknown format %d", fmt);
   if (M < 0 || N <= 0 || K <= 0)
     return fail(BSFP4_ERR_SHAPE, "need M >= 0, N > 0, K > 0 (M=%lld N=%lld K=%lld)", (long long)M,
@@ -173,6 +175,9 @@ bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8
   if (N % 32) return fail(BSFP4_ERR_SHAPE, "N=%lld is not a multiple of 32", (long long)N);
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return fail(BSFP4_ERR_SHAPE, "dimensions must fit in 31 bits");
+  if (fmt == BSFP4_MXFP4 && (M * (K / 2) >= kLim31 || N * (K / 2) >= kLim31))
+    return fail(BSFP4_ERR_SHAPE, "MXFP4 operands must stay below 2^31 bytes (M*K/2=%lld, N*K/2=%lld)",
+                (long long)(M * (K / 2)), (long long)(N * (K / 2)));
   if (M > 0) {
     REQUIRE_PTR(A);
     REQUIRE_PTR(SFA);
@@ -181,22 +186,52 @@ bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8
   REQUIRE_PTR(B);
   REQUIRE_PTR(SFB);
   if (alpha != nullptr && !aligned(alpha, 4)) return fail(BSFP4_ERR_ALIGNMENT, "alpha is not 4-byte aligned");
+  return BSFP4_OK;
+}
+
+static bsfp4_status launch_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                                const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, void* ws,
+                                size_t ws_bytes, hipStream_t st) {
+  if (fmt == BSFP4_NVFP4)
+    return launched(bsfp4::launch_nvfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, ws, ws_bytes, st), "fp4_gemm launch");
+  return launched(bsfp4::launch_mxfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, st), "fp4_gemm launch");
+}
+
+bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                      const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M, int64_t N,
+                      int64_t K, void* ws, size_t ws_bytes, void* stream) {
+  if (bsfp4_status s = check_gemm_args(fmt, A, SFA, B, SFB, alpha, D, M, N, K)) return s;
   const size_t need = fp4_gemm_workspace_size(fmt, M, N, K);
   if (need > 0) {
     if (ws == nullptr || ws_bytes < need)
       return fail(BSFP4_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
     if (!aligned(ws, 16)) return fail(BSFP4_ERR_ALIGNMENT, "ws is not 16-byte aligned");
   }
-  if (fmt == BSFP4_MXFP4 && (M * (K / 2) >= kLim31 || N * (K / 2) >= kLim31))
-    return fail(BSFP4_ERR_SHAPE, "MXFP4 operands must stay below 2^31 bytes (M*K/2=%lld, N*K/2=%lld)",
-                (long long)(M * (K / 2)), (long long)(N * (K / 2)));
   if (M == 0) return ok();
   if (bsfp4_status s = check_device()) return s;
-  if (fmt == BSFP4_NVFP4)
-    return launched(bsfp4::launch_nvfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, ws, ws_bytes, as_stream(stream)),
-                    "fp4_gemm launch");
-  return launched(bsfp4::launch_mxfp4_gemm(A, SFA, B, SFB, alpha, D, M, N, K, as_stream(stream)),
-                  "fp4_gemm launch");
+  return launch_gemm(fmt, A, SFA, B, SFB, alpha, D, M, N, K, ws, ws_bytes, as_stream(stream));
+}
+
+size_t fp4_gemm_noalloc_max_workspace(void) { return bsfp4::kScratchBytes; }
+
+bsfp4_status fp4_gemm_noalloc(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                              const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (bsfp4_status s = check_gemm_args(fmt, A, SFA, B, SFB, alpha, D, M, N, K)) return s;
+  const size_t need = fp4_gemm_workspace_size(fmt, M, N, K);
+  if (need > bsfp4::kScratchBytes)
+    return fail(BSFP4_ERR_WORKSPACE,
+                "this shape needs %zu bytes of split-K partials, above the %zu-byte static scratch of "
+                "fp4_gemm_noalloc (use fp4_gemm with a caller workspace)",
+                need, bsfp4::kScratchBytes);
+  if (M == 0) return ok();
+  if (bsfp4_status s = check_device()) return s;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = bsfp4::scratch_device_ptr(&ws);
+    if (e != hipSuccess) return fail(BSFP4_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  }
+  return launch_gemm(fmt, A, SFA, B, SFB, alpha, D, M, N, K, ws, need > 0 ? bsfp4::kScratchBytes : 0,
+                     as_stream(stream));
 }
 
 // ------------------------------------------------------------------ W4A16

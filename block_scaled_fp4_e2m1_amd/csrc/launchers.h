@@ -23,6 +23,11 @@ hipError_t launch_nvfp4_experts_quant(const uint16_t* x, int64_t rows_in, int64_
                                       const int32_t* offsets, int64_t E, const float* gs, int64_t rows_out,
                                       uint8_t* q, uint8_t* sf, hipStream_t stream);
 
+// The library's static device scratch (scratch.hip): kScratchBytes per device,
+// its address for the current device looked up once and cached.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+hipError_t scratch_device_ptr(void** out);
+
 // E2M1 codes of caller-given value pairs (see bsfp4_e2m1_convert); pairs % 4 == 0.
 hipError_t launch_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
                                uint8_t* codes, hipStream_t stream);

@@ -152,6 +152,30 @@ BSFP4_API bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, c
                       int64_t K, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * fp4_gemm_noalloc: fp4_gemm without a workspace argument, for callers that
+ * cannot allocate device memory at all (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The split-K partials
+ * that fp4_gemm keeps in the caller's workspace go to a static device array
+ * of the library instead, fp4_gemm_noalloc_max_workspace() bytes (32 MiB) on
+ * every GPU the library runs on, held until the process ends; the call
+ * itself allocates and frees nothing and issues no memset.
+ *   arguments, layouts and results as for fp4_gemm (the same kernels, tile
+ *   plan and K split, so the output equals fp4_gemm's bit for bit)
+ *   returns BSFP4_ERR_WORKSPACE, before any launch, when the shape needs
+ *   more than fp4_gemm_noalloc_max_workspace() bytes of partials, i.e. when
+ *   fp4_gemm_workspace_size(fmt, M, N, K) exceeds it (NVFP4 with M > 512 at
+ *   N = 4096, K = 7168, for example; MXFP4 never needs any)
+ * Every call on one GPU shares that GPU's array, and the partials of a call
+ * are written in full before they are read, so nothing needs clearing; calls
+ * that overlap in time on one GPU (different streams, or threads) race on
+ * the array and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+BSFP4_API size_t fp4_gemm_noalloc_max_workspace(void);
+BSFP4_API bsfp4_status fp4_gemm_noalloc(int fmt, const uint8_t* A, const uint8_t* SFA, const uint8_t* B,
+                                        const uint8_t* SFB, const float* alpha, uint16_t* D, int64_t M,
+                                        int64_t N, int64_t K, void* stream);
+
+/* ----------------------------------------------------------------------------
  * w4a16_gemm: D[M,N] = bf16_rne(alpha * sum_k A[m,k] * dec(B)[n,k]) with bf16
  * activations and NVFP4 weights ("feat: sm100 cute_dsl w4a16 gemm": bf16
  * activations x native NVFP4 weights; the tensor-wide FP32 weight scale

@@ -115,6 +115,23 @@ def test_mxfp4_grouped_validation(lib):
     assert call(a_total=1 << 16, rows=64, K=1 << 16, idx=FAKE) == SHAPE and "2^31" in _err(lib)
 
 
+def test_gemm_noalloc_validation(lib):
+    f = lib.fp4_gemm_noalloc
+    assert lib.fp4_gemm_noalloc_max_workspace() == 32 << 20
+    args = lambda **kw: [kw.get("fmt", 0), kw.get("A", FAKE), kw.get("SFA", FAKE), kw.get("B", FAKE),
+                         kw.get("SFB", FAKE), kw.get("alpha", FAKE), kw.get("D", FAKE),
+                         kw.get("M", 64), kw.get("N", 64), kw.get("K", 64), None]
+    assert f(*args(fmt=3)) == INVALID
+    assert f(*args(N=48)) == SHAPE
+    assert f(*args(A=None)) == INVALID
+    assert f(*args(D=FAKE + 8)) == ALIGN
+    assert f(*args(fmt=1, M=1 << 16, K=1 << 16)) == SHAPE
+    # partials beyond the static scratch: refused before any device query
+    assert lib.fp4_gemm_workspace_size(0, 1024, 4096, 7168) > (32 << 20)
+    assert f(*args(M=1024, N=4096, K=7168)) == WORKSPACE and "static scratch" in _err(lib)
+    assert f(*args(M=0, A=None, SFA=None, D=None)) == OK
+
+
 def test_e2m1_convert_validation(lib):
     f = lib.bsfp4_e2m1_convert
     assert f(3, FAKE, None, 8, FAKE, None) == INVALID
