@@ -1,6 +1,8 @@
 """Benchmark of the block-scaled FP4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-rows]
+    python bench.py --mode cold --no-headline --no-cpu --rows-only ROW   (profiling runs)
+    python bench.py --trace-summary kernel_trace.csv                       (no GPU)
 
 Headline (one JSON line on stdout): the NVFP4 W4A4 GEMM at M=4096, N=4096,
 K=7168 -- A and B bf16 ~ N(0,1) from seeds 120/121, quantised on the GPU by
@@ -19,7 +21,18 @@ The same line carries:
   cpu_baseline  the float64 CPU oracle timed on this host on the same inputs;
   rows          the other hot-path rows (quantiser, small-M GEMM, W4A16,
                 MXFP4 GEMM, MoE layer, the 4-layer quantise+GEMM pipeline)
-                with per-launch times, cold, warm and graph-replayed.
+                with per-launch times, cold, warm and graph-replayed, and the
+                on-box peaks (MFMA loop per dtype, streaming reads cold and
+                warm) that every fraction is also reported against;
+  gbs_at_m16    the metric's second half: the 16 x 4096 x 7168 GEMM's
+                algorithmic bytes over its cold and graph-replayed times.
+
+Cold protocol: before every cold call a 512 MiB fill (twice the 256 MB
+memory-side cache) evicts L2 and the MALL; the call is timed alone with HIP
+events.  With --mode cold every call of a row's kernels, warm-up included,
+follows a fill and no warm or graph timing runs, so that a rocprofv3 kernel
+trace of that process holds cold launches only; --trace-summary turns such a
+trace into per-kernel median / p10 / p90 durations.
 """
 from __future__ import annotations
 
@@ -52,7 +65,32 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 256 MiB device-to-device copy (3 times), the "
                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--mode", choices=["full", "cold"], default="full",
+                   help="cold: rows time cold calls only (every call after a fill)")
+    p.add_argument("--no-headline", action="store_true", help="skip the headline GEMM")
+    p.add_argument("--trace-summary", default="",
+                   help="summarise a rocprofv3 kernel_trace.csv (per-kernel duration percentiles) and exit")
     return p.parse_args()
+
+
+def trace_summary(path: str) -> str:
+    """Markdown table of kernel durations (us) per kernel name from a rocprofv3
+    --kernel-trace CSV: launches, median, p10, p90, min, max, mean."""
+    import csv
+    from collections import defaultdict
+    dur = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            dur[name].append((t1 - t0) / 1e3)
+    lines = ["| kernel | launches | median us | p10 | p90 | min | max | mean |", "|---|---|---|---|---|---|---|---|"]
+    for name, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        short = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {a.size} | {np.median(a):.2f} | {np.percentile(a, 10):.2f} | "
+                     f"{np.percentile(a, 90):.2f} | {a.min():.2f} | {a.max():.2f} | {a.mean():.2f} |")
+    return "\n".join(lines)
 
 
 def src_sha(names: str) -> str:
@@ -84,10 +122,14 @@ def stored_traffic(kernel_key: str, source: str):
 
 
 class Timer:
-    """Per-launch durations with HIP events recorded on the current stream."""
+    """Per-launch durations with HIP events recorded on the current stream.
 
-    def __init__(self, torch):
+    cold_only: every call (warm-up included) follows a flush, and warm / graph
+    timings are skipped (they return None)."""
+
+    def __init__(self, torch, cold_only=False):
         self.torch = torch
+        self.cold_only = cold_only
         self.flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
 
     def graph(self, fn, calls=20, reps=5):
@@ -96,6 +138,8 @@ class Timer:
         host's per-launch cost (which exceeds a few-microsecond kernel).  The
         replayed result is checked against the eager result of the same call
         by the caller through `check`."""
+        if self.cold_only:
+            return None
         t = self.torch
         side = t.cuda.Stream()
         side.wait_stream(t.cuda.current_stream())
@@ -129,7 +173,11 @@ class Timer:
         for kernels of a few microseconds this is bounded by the host's launch
         cost; `graph` gives the GPU time."""
         t = self.torch
+        if self.cold_only and not cold:
+            return None
         for _ in range(warmup):
+            if cold and self.cold_only:
+                self.flush.zero_()
             fn()
         t.cuda.synchronize()
         if not cold:
@@ -163,6 +211,9 @@ CLOCK_RAMP_S = 0.3
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -186,13 +237,57 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---------------------------------------------------------------- inputs
+    out = {"metric": METRIC}
+    head = None
+    if not args.no_headline:
+        head = headline(torch, bs, synth, bf16, args)
+        out.update(head["json"])
+
+    # ---------------------------------------------------------------- other rows
+    if not args.no_rows:
+        only = [r for r in args.rows_only.split(",") if r]
+        rows = run_rows(torch, bs, synth, Timer(torch, cold_only=args.mode == "cold"), only)
+        out["rows"] = rows
+        peaks = rows.get("peaks")
+        if head is not None and peaks:
+            rf = out["roofline"]
+            rf["measured_peak"] = peaks["mfma_tflops"]["f16"]
+            rf["frac_of_measured_peak"] = round(rf["achieved"] / peaks["mfma_tflops"]["f16"], 4)
+        m16 = rows.get("nvfp4_gemm_16x4096x7168")
+        if m16 and head is not None:
+            g = {"cold_gbs": m16["cold"]["gbs"], "cold_frac_hbm": m16["cold"]["frac_hbm"],
+                 "cold_us": round(m16["cold"]["median_us"], 3)}
+            if m16.get("graph"):
+                g.update({"graph_gbs": m16["graph"]["gbs"], "graph_frac_hbm": m16["graph"]["frac_hbm"],
+                          "graph_us": round(m16["graph"]["median_us"], 3),
+                          "note": "graph replay keeps the 16.7 MB weights in the 256 MB memory-side cache"})
+            if peaks:
+                g["cold_read_floor_us"] = peaks["read"]["16.7MB_cold"]["median_us"]
+                g["cold_vs_read_floor"] = round(m16["cold"]["median_us"] / peaks["read"]["16.7MB_cold"]["median_us"], 3)
+            # the metric's second half sits right after the value so that a truncated line keeps it
+            keys = list(out.keys())
+            i = keys.index("unit") + 1
+            out = {k: out[k] for k in keys[:i]} | {"gbs_at_m16": g} | {k: out[k] for k in keys[i:]}
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu and head is not None:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(torch, bs, synth, bf16, head["inputs"])
+
+    print(json.dumps(out), flush=True)
+
+
+def headline(torch, bs, synth, bf16, args):
+    """The NVFP4 GEMM at 4096 x 4096 x 7168: K launches between two HIP events
+    on the launch stream after the clock ramp and W warm-up launches."""
+    dev = "cuda:0"
     M, N, K = 4096, 4096, 7168
     a = bf16(synth.bf16_normal(120, (M, K)))
     b = bf16(synth.bf16_normal(121, (N, K)))
     gsa, gsb = bs.global_scale(a), bs.global_scale(b)
     aq, sfa = bs.quantize(a, "nvfp4", gs=gsa)
     bq, sfb = bs.quantize(b, "nvfp4", gs=gsb)
+    del a, b
     g = torch.cat([gsa, gsb]).cpu().numpy()
     alpha = torch.tensor([np.float32(1.0) / np.float32(g[0] * g[1])], dtype=torch.float32, device=dev)
     D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -200,7 +295,6 @@ def main():
     def step():
         bs.gemm(aq, sfa, bq, sfb, alpha, out=D)
 
-    # ---------------------------------------------------------------- timed region
     print(f"[bench] headline: {CLOCK_RAMP_S} s clock ramp, {args.warmup} warm-up + {args.steps} timed steps",
           file=sys.stderr, flush=True)
     t_ramp = time.perf_counter()
@@ -230,9 +324,7 @@ def main():
                 "frac": round(tflops / PEAK["f16"], 4), "traffic": traffic,
                 "frac_of_fp4_peak": round(tflops / PEAK["fp4"], 4),
                 "algorithmic_bytes": alg_bytes}
-
-    out = {
-        "metric": METRIC,
+    js = {
         "value": round(tflops, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -251,18 +343,7 @@ def main():
                    "timed_wall_s": round(wall, 4), "untimed_clock_ramp_s": CLOCK_RAMP_S},
         "roofline": roofline,
     }
-
-    # ---------------------------------------------------------------- other rows
-    if not args.no_rows:
-        only = [r for r in args.rows_only.split(",") if r]
-        out["rows"] = run_rows(torch, bs, synth, Timer(torch), only)
-
-    # ---------------------------------------------------------------- CPU oracle
-    if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(aq, sfa, bq, sfb, alpha, D)
-
-    print(json.dumps(out), flush=True)
+    return {"json": js, "inputs": (aq, sfa, bq, sfb, alpha, D)}
 
 
 def _nv_bytes(M, N, K):
@@ -270,6 +351,8 @@ def _nv_bytes(M, N, K):
 
 
 def _rate(t, flops=None, nbytes=None):
+    if t is None:
+        return None
     r = dict(t)
     us = t["median_us"]
     if flops:
@@ -306,6 +389,45 @@ def run_rows(torch, bs, synth, timer, only):
         g = torch.cat([gsa, gsb]).cpu().numpy()
         alpha = torch.tensor([np.float32(1.0) / np.float32(g[0] * g[1])], device=dev)
         return a, gsa, aq, sfa, bq, sfb, alpha
+
+    # On-box peaks: the MFMA loop per dtype (registers only) and streaming reads
+    # of the M=16 workload's byte count and of 256 MiB, cold (after the fill, as
+    # every cold row) and warm (back to back: the 16.7 MB read then runs from
+    # the memory-side cache).
+    if want("peaks"):
+        import ctypes
+        from block_scaled_fp4_e2m1_amd import binding as B
+        lib = bs.load()
+        stream = B._stream(torch.device(dev))
+        mf = {}
+        for kind, name, iters in ((0, "f16", 4096), (1, "bf16", 4096), (2, "fp8", 2048), (3, "fp4", 1024)):
+            fn = lambda: B._check(lib.bsfp4_probe_mfma(kind, iters, stream), "probe_mfma")
+            t = timer.run(fn, iters=10, warmup=3)
+            if t is not None:
+                mf[name] = round(lib.bsfp4_probe_mfma_flops(kind, iters) / t["median_us"] / 1e6, 1)
+        rd = {}
+        for label, nbytes in (("16.7MB", 16710672), ("256MiB", 256 << 20)):
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            buf.fill_(1)
+            fn = lambda: B._check(lib.bsfp4_probe_read(B._p(buf), nbytes, stream), "probe_read")
+            c = timer.run(fn, cold=True)
+            rd[f"{label}_cold"] = {"median_us": round(c["median_us"], 3), "p10_us": round(c["p10_us"], 3),
+                                   "p90_us": round(c["p90_us"], 3),
+                                   "gbs": round(nbytes / c["median_us"] / 1e3, 1)}
+            w = timer.run(fn, iters=20)
+            if w is not None:
+                rd[f"{label}_warm"] = {"median_us": round(w["median_us"], 3),
+                                       "gbs": round(nbytes / w["median_us"] / 1e3, 1)}
+            gr = timer.graph(fn)
+            if gr is not None:
+                rd[f"{label}_graph"] = {"median_us": round(gr["median_us"], 3),
+                                        "gbs": round(nbytes / gr["median_us"] / 1e3, 1)}
+            del buf
+        rows["peaks"] = {"mfma_tflops": mf, "read": rd,
+                         "published": {"mfma_tflops": {"f16": PEAK["f16"], "bf16": PEAK["bf16"], "fp8": PEAK["fp8"],
+                                                       "fp4": PEAK["fp4"]}, "hbm_gbs": HBM_PEAK_GBS},
+                         "note": "MFMA: 8 independent accumulators per wave, register operands; read: 128-bit "
+                                 "loads, 4 in flight per lane; cold = after a 512 MiB fill"}
 
     # a3/a4 at the memory-bound workload: M=16, N=4096, K=7168 (HBM roofline)
     if want("nvfp4_gemm_16x4096x7168"):
@@ -458,8 +580,9 @@ def run_rows(torch, bs, synth, timer, only):
         fn = lambda: bs.gemm(aq, sfa, bq, sfb, None, fmt="mxfp4", out=D)
         nbytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
         rows["mxfp4_gemm_4096x4096x7168"] = {
-            "warm": _rate(timer.run(fn), 2.0 * M * N * K, nbytes), "bound": "mfma (fp4)",
-            "peak_tflops": PEAK["fp4"]}
+            "warm": _rate(timer.run(fn), 2.0 * M * N * K, nbytes),
+            "cold": _rate(timer.run(fn, iters=10, cold=True), 2.0 * M * N * K, nbytes),
+            "bound": "mfma (fp4)", "peak_tflops": PEAK["fp4"]}
 
     # a2, a7-a10: the MXFP4 MoE layer (4096 tokens, hidden 2048, 128 experts, top-8, I=768)
     if want("moe_mxfp4_4096x2048_e128_top8"):
@@ -476,6 +599,7 @@ def run_rows(torch, bs, synth, timer, only):
         del w2
         W13, W13sf = W13.view(E, 2 * I, H // 2), W13sf.view(E, 2 * I, H // 32)
         W2, W2sf = W2.view(E, H, I // 2), W2sf.view(E, H, I // 32)
+        ROW_INPUTS["moe_mxfp4"] = (x, ids, tw, W13, W13sf, W2, W2sf)
         R = T * topk
         offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
         sids = torch.empty(R, dtype=torch.int32, device=dev)
@@ -614,35 +738,116 @@ def run_rows(torch, bs, synth, timer, only):
     return rows
 
 
-def cpu_baseline(aq, sfa, bq, sfb, alpha, D):
-    """The float64 oracle on the same quantised inputs, timed on this host.
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    Sample: the whole workload (all 4096 rows of A, every column, all of K):
-    dequantise A and B exactly to float64, one float64 matmul, bf16 rounding.
-    The GPU output is also checked against it element by element."""
-    from threadpoolctl import threadpool_info
+
+def _median_of_3(fn):
+    """One untimed warm run, then the median wall time of three runs."""
+    fn()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        r = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), r
+
+
+# tensors of the MoE row kept for the oracle's timing (host copies are made there)
+ROW_INPUTS = {}
+
+
+def cpu_baseline(torch, bs, synth, bf16, inputs):
+    """The oracle on this host, timed as: one warm run, then the median of three.
+
+    Headline (value): the float64 GEMM oracle on the whole 4096 x 4096 x 7168
+    workload with the BLAS pool on every core (it is also checked against the
+    GPU output element by element).  Beside it: the same GEMM on one core (a
+    256-row sample), the 16 x 4096 x 7168 GEMM, the NVFP4 quantiser of the
+    256 x 4096 activations (numpy element-wise code runs on one core), and the
+    MoE layer on a 128-token sample of the 4096-token workload (all 128
+    experts, top-8) with the workload's quantised weights."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import gemm as OG
+    from oracle import moe as OM
+    from oracle import quant as OQ
     from oracle import tolerance as TOL
 
-    rows = np.arange(0, 4096)
-    A = aq.cpu().numpy()[rows]
-    SA = sfa.cpu().numpy()[rows]
-    B = bq.cpu().numpy()
-    SB = sfb.cpu().numpy()
+    aq, sfa, bq, sfb, alpha, D = inputs
+    A, SA, B, SB = aq.cpu().numpy(), sfa.cpu().numpy(), bq.cpu().numpy(), sfb.cpu().numpy()
     al = float(alpha.cpu().numpy()[0])
-    t0 = time.perf_counter()
-    ref = OG.nvfp4_gemm(A, SA, B, SB, al)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * len(rows) * B.shape[0] * B.shape[1] * 2
-    got = D.view(__import__("torch").int16).cpu().numpy().view(np.uint16)[rows]
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    secs, ref = _median_of_3(lambda: OG.nvfp4_gemm(A, SA, B, SB, al))
+    flops = 2.0 * A.shape[0] * B.shape[0] * B.shape[1] * 2
+    got = D.view(torch.int16).cpu().numpy().view(np.uint16)
     ok, worst, nbad = TOL.check_bf16(got, ref)
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"full workload: {len(rows)} rows x 4096 columns x K=7168 "
+    per = {}
+
+    rows1 = slice(0, 256)
+    with threadpool_limits(limits=1):
+        t1, _ = _median_of_3(lambda: OG.nvfp4_gemm(A[rows1], SA[rows1], B, SB, al))
+    per["nvfp4_gemm_4096x4096x7168_1core"] = {
+        "seconds": round(t1, 4), "tflops": round(2.0 * 256 * B.shape[0] * B.shape[1] * 2 / t1 / 1e12, 6),
+        "cores": 1, "sample": "rows 0..255 of A, all 4096 columns, K=7168"}
+
+    # config 0: 16 x 4096 x 7168 (inputs quantised on the GPU, seeds 100 / 101)
+    a0 = bf16(synth.bf16_normal(100, (16, 7168)))
+    b0 = bf16(synth.bf16_normal(101, (4096, 7168)))
+    g0a, g0b = bs.global_scale(a0), bs.global_scale(b0)
+    q0a, s0a = bs.quantize(a0, "nvfp4", gs=g0a)
+    q0b, s0b = bs.quantize(b0, "nvfp4", gs=g0b)
+    g0 = torch.cat([g0a, g0b]).cpu().numpy()
+    al0 = float(np.float32(1.0) / np.float32(g0[0] * g0[1]))
+    H0 = [t.cpu().numpy() for t in (q0a, s0a, q0b, s0b)]
+    t0s, _ = _median_of_3(lambda: OG.nvfp4_gemm(*H0, al0))
+    per["nvfp4_gemm_16x4096x7168"] = {"seconds": round(t0s, 4), "cores": int(threads),
+                                      "tflops": round(2.0 * 16 * 4096 * 7168 / t0s / 1e12, 6),
+                                      "gbs": round(_nv_bytes(16, 4096, 7168) / t0s / 1e9, 3),
+                                      "sample": "the whole workload"}
+
+    # config 1's producer: the NVFP4 quantiser on 256 x 4096 bf16 with outliers
+    x1 = synth.bf16_normal_with_outliers(110, 1110, (256, 4096))
+    gs1 = OQ.global_scale(x1)
+    with threadpool_limits(limits=1):
+        tq, _ = _median_of_3(lambda: OQ.nvfp4_quantize(x1, gs1))
+    per["nvfp4_quantize_256x4096"] = {
+        "seconds": round(tq, 5), "cores": 1, "gbs": round((2 * 256 * 4096) / tq / 1e9, 4),
+        "sample": "the whole workload; numpy element-wise code runs on one core, so one core and all cores "
+                  "are the same run"}
+
+    # config 4: the MXFP4 MoE layer on a 128-token sample
+    moe = ROW_INPUTS.get("moe_mxfp4")
+    if moe is not None:
+        Ts = 128
+        x, ids, w, W13, W13sf, W2, W2sf = moe
+        xs = x[:Ts].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ids_s, w_s = ids[:Ts].cpu().numpy(), w.view(-1, ids.shape[1])[:Ts].cpu().numpy()
+        Wh = [t.cpu().numpy() for t in (W13, W13sf, W2, W2sf)]
+        tm, _ = _median_of_3(lambda: OM.moe_layer(xs, ids_s, w_s, *Wh))
+        E, I2, Hh = W13.shape
+        R = Ts * ids.shape[1]
+        mflops = 2.0 * R * I2 * (Hh * 2) + 2.0 * R * (Hh * 2) * (I2 // 2)
+        per["moe_mxfp4_4096x2048_e128_top8"] = {
+            "seconds": round(tm, 3), "cores": int(threads), "tflops": round(mflops / tm / 1e12, 6),
+            "sample": f"tokens 0..{Ts - 1} of 4096 (top-8 of 128 experts, {R} routed rows), every stage"}
+
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(secs, 3), "timing": "median of 3 after one warm run",
+            "cpu_model": _cpu_model(), "nproc": nproc,
+            "sample": "full workload: 4096 rows x 4096 columns x K=7168 "
                       "(exact float64 dequant + float64 matmul + bf16 rounding)",
-            "parity_on_sample": {"ok": ok, "worst_ratio": round(worst, 4), "n_bad": nbad}}
+            "parity_on_sample": {"ok": ok, "worst_ratio": round(worst, 4), "n_bad": nbad},
+            "per_config": per}
 
 
 if __name__ == "__main__":

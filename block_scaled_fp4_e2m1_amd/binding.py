@@ -84,6 +84,9 @@ _SIGNATURES = {
                                               _c_ptr, _c_i64, _c_i64, ctypes.c_int,
                                               ctypes.POINTER(MoeEpilogueArgs), _c_ptr, _c_size, _c_ptr]),
     "bsfp4_e2m1_convert": (ctypes.c_int, [ctypes.c_int, _c_ptr, _c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "bsfp4_probe_mfma_flops": (_c_i64, [ctypes.c_int, ctypes.c_int]),
+    "bsfp4_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_ptr]),
+    "bsfp4_probe_read": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr]),
     "fp4_gemm_noalloc_max_workspace": (_c_size, []),
     "fp4_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_i64, _c_i64, _c_i64, _c_ptr]),

@@ -32,6 +32,7 @@ SOURCES = [
     "layout.hip",
     "e2m1_convert.hip",
     "scratch.hip",
+    "probes.hip",
 ]
 
 ARCH = "gfx950"

@@ -28,6 +28,12 @@ hipError_t launch_nvfp4_experts_quant(const uint16_t* x, int64_t rows_in, int64_
 constexpr size_t kScratchBytes = (size_t)32 << 20;
 hipError_t scratch_device_ptr(void** out);
 
+// Peak probes (probes.hip): MFMA loop per kind on probe_mfma_grid() workgroups
+// of 256 threads, and a 128-bit streaming read of `bytes` (bytes % 16 == 0).
+int64_t probe_mfma_grid();
+hipError_t launch_probe_mfma(int kind, int iters, hipStream_t stream);
+hipError_t launch_probe_read(const void* buf, int64_t bytes, hipStream_t stream);
+
 // E2M1 codes of caller-given value pairs (see bsfp4_e2m1_convert); pairs % 4 == 0.
 hipError_t launch_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
                                uint8_t* codes, hipStream_t stream);

@@ -1,0 +1,107 @@
+// On-box peak probes: the rates that the roofline fractions of the hot-path
+// kernels are also reported against, measured on the device that runs them
+// (the published MI355X figures are the primary denominators).
+//
+//   mfma_probe<KIND>  every wave keeps 8 independent 32x32 accumulators and
+//                     issues MFMAs back to back from registers (no memory
+//                     traffic): KIND 0 fp16 32x32x16, 1 bf16 32x32x16,
+//                     2 fp8 (E4M3) 32x32x64, 3 fp4 (E2M1, E8M0 scale 1.0)
+//                     32x32x64 scaled MFMA.  Four 256-thread workgroups per
+//                     compute unit, i.e. four waves per SIMD.
+//   read_probe        streams a buffer once with 128-bit loads (four in
+//                     flight per lane), keeping a running XOR; nothing is
+//                     stored unless the flag (never set by the library) asks.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace bsfp4 {
+namespace {
+
+template <int KIND>
+__global__ void __launch_bounds__(256) mfma_probe(int iters, int flag, float* sink) {
+  const int lane = threadIdx.x & 63;
+  v16f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = v16f{};
+  if constexpr (KIND <= 1) {
+    v8h a, b;
+    v8bf ab, bb;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      a[i] = (_Float16)(0.001f * (lane + i));
+      b[i] = (_Float16)(0.002f * (lane - i));
+      ab[i] = (__bf16)(0.001f * (lane + i));
+      bb[i] = (__bf16)(0.002f * (lane - i));
+    }
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if constexpr (KIND == 0)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+        else
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb, acc[j], 0, 0, 0);
+      }
+    }
+  } else {
+    const int base = 0x38383838 + lane;
+    const v8i a = v8i{base, base + 1, base + 2, base + 3, base + 4, base + 5, base + 6, base + 7};
+    const v8i b = v8i{base + 7, base + 6, base + 5, base + 4, base + 3, base + 2, base + 1, base};
+    constexpr int fmt = KIND == 2 ? 0 : 4;  // 0: fp8 E4M3, 4: fp4 E2M1
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], fmt, fmt, 0, 127, 0, 127);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; j++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) s += acc[j][r];
+  if (flag) sink[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ void __launch_bounds__(256) read_probe(const uint4* __restrict__ p, int64_t n16, int flag,
+                                                  uint32_t* sink) {
+  uint32_t x = 0;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 v0 = p[i], v1 = p[i + stride], v2 = p[i + 2 * stride], v3 = p[i + 3 * stride];
+    x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w ^ v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^
+         v3.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (flag) sink[blockIdx.x * 256 + threadIdx.x] = x;
+}
+
+}  // namespace
+
+int64_t probe_mfma_grid() { return 4 * (int64_t)device_cu_count(); }
+
+hipError_t launch_probe_mfma(int kind, int iters, hipStream_t stream) {
+  const unsigned grid = (unsigned)probe_mfma_grid();
+  switch (kind) {
+    case 0: mfma_probe<0><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 1: mfma_probe<1><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 2: mfma_probe<2><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    default: mfma_probe<3><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* buf, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  // four 16-byte loads per lane in flight; enough workgroups to cover every CU
+  int64_t grid = (n16 + 4 * 256 - 1) / (4 * 256);
+  const int64_t cap = 8 * (int64_t)device_cu_count();
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  read_probe<<<(unsigned)grid, 256, 0, stream>>>(static_cast<const uint4*>(buf), n16, 0, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace bsfp4

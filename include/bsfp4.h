@@ -425,6 +425,23 @@ typedef enum bsfp4_cvt_mode {
 BSFP4_API bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_t* scale_codes, int64_t pairs,
                                           uint8_t* codes, void* stream);
 
+/* bsfp4_probe_mfma / bsfp4_probe_read: peak probes of the device, the rates
+ * the kernels' roofline fractions are also reported against (beside the
+ * published MI355X peaks).
+ *   bsfp4_probe_mfma  kind 0 fp16 (v_mfma_f32_32x32x16_f16), 1 bf16, 2 fp8
+ *                     E4M3 and 3 fp4 E2M1 (v_mfma_scale_f32_32x32x64_f8f6f4,
+ *                     unit E8M0 scales): every wave issues `iters` x 8
+ *                     independent MFMAs from registers, four waves per SIMD;
+ *                     bsfp4_probe_mfma_flops(kind, iters) is the launch's flop
+ *                     count (0 for invalid arguments), iters in [1, 2^24]
+ *   bsfp4_probe_read  reads `bytes` (> 0, % 16 == 0) of device memory at
+ *                     `buf` (16-byte aligned) once with 128-bit loads; writes
+ *                     nothing
+ * Both are asynchronous on `stream`; time them with events on that stream. */
+BSFP4_API int64_t bsfp4_probe_mfma_flops(int kind, int iters);
+BSFP4_API bsfp4_status bsfp4_probe_mfma(int kind, int iters, void* stream);
+BSFP4_API bsfp4_status bsfp4_probe_read(const void* buf, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
