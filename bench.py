@@ -70,7 +70,41 @@ def parse():
     p.add_argument("--no-headline", action="store_true", help="skip the headline GEMM")
     p.add_argument("--trace-summary", default="",
                    help="summarise a rocprofv3 kernel_trace.csv (per-kernel duration percentiles) and exit")
+    p.add_argument("--counter-summary", default="",
+                   help="summarise a rocprofv3 counter_collection.csv (median per dispatch per kernel and "
+                        "grid, FETCH_SIZE / WRITE_SIZE scaled by the 256 MiB copy) and exit")
     return p.parse_args()
+
+
+def counter_summary(path: str) -> str:
+    """Markdown table of median counter values per dispatch, per (kernel, grid
+    size).  FETCH_SIZE / WRITE_SIZE (KiB) are also scaled to bytes with the
+    factor that makes the 256 MiB device copy (__amd_rocclr_copyBuffer, run by
+    --copy-calibration) read or write exactly 256 MiB."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r.get("Grid_Size") or 0), r["Counter_Name"])
+            vals[key].append(float(r["Counter_Value"]))
+    med = {k: float(np.median(v)) for k, v in vals.items()}
+    counts = {k: len(v) for k, v in vals.items()}
+    factor = {}
+    for (name, grid, ctr), v in med.items():
+        if "copyBuffer" in name and ctr in ("FETCH_SIZE", "WRITE_SIZE") and v > 0:
+            factor[ctr] = (256 << 20) / 1024.0 / v
+    lines = ["| kernel | grid | counter | dispatches | median per dispatch | scaled MB |",
+             "|---|---|---|---|---|---|"]
+    for (name, grid, ctr), v in sorted(med.items(), key=lambda kv: (kv[0][0], kv[0][1], kv[0][2])):
+        short = name if len(name) <= 100 else name[:97] + "..."
+        mb = f"{v * 1024.0 * factor[ctr] / 1e6:.2f}" if ctr in factor else ""
+        lines.append(f"| `{short}` | {grid} | {ctr} | {counts[(name, grid, ctr)]} | {v:.1f} | {mb} |")
+    if factor:
+        lines.append("")
+        lines.append("Copy calibration factors (bytes per counter KiB / 1024): " +
+                     ", ".join(f"{k} {v:.4f}" for k, v in sorted(factor.items())))
+    return "\n".join(lines)
 
 
 def trace_summary(path: str) -> str:
@@ -213,6 +247,9 @@ def main():
     args = parse()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -398,10 +435,11 @@ def run_rows(torch, bs, synth, timer, only):
         import ctypes
         from block_scaled_fp4_e2m1_amd import binding as B
         lib = bs.load()
-        stream = B._stream(torch.device(dev))
+        stream = lambda: B._stream(torch.device(dev))   # the current stream (a capture stream in a graph)
         mf = {}
-        for kind, name, iters in ((0, "f16", 4096), (1, "bf16", 4096), (2, "fp8", 2048), (3, "fp4", 1024)):
-            fn = lambda: B._check(lib.bsfp4_probe_mfma(kind, iters, stream), "probe_mfma")
+        for kind, name, iters in ((0, "f16", 4096), (1, "bf16", 4096), (2, "fp8", 2048), (3, "fp4", 1024),
+                                  (4, "f16_3bit_operands", 4096), (5, "bf16_3bit_operands", 4096)):
+            fn = lambda: B._check(lib.bsfp4_probe_mfma(kind, iters, stream()), "probe_mfma")
             t = timer.run(fn, iters=10, warmup=3)
             if t is not None:
                 mf[name] = round(lib.bsfp4_probe_mfma_flops(kind, iters) / t["median_us"] / 1e6, 1)
@@ -409,7 +447,7 @@ def run_rows(torch, bs, synth, timer, only):
         for label, nbytes in (("16.7MB", 16710672), ("256MiB", 256 << 20)):
             buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             buf.fill_(1)
-            fn = lambda: B._check(lib.bsfp4_probe_read(B._p(buf), nbytes, stream), "probe_read")
+            fn = lambda: B._check(lib.bsfp4_probe_read(B._p(buf), nbytes, stream()), "probe_read")
             c = timer.run(fn, cold=True)
             rd[f"{label}_cold"] = {"median_us": round(c["median_us"], 3), "p10_us": round(c["p10_us"], 3),
                                    "p90_us": round(c["p90_us"], 3),

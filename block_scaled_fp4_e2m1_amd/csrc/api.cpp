@@ -318,17 +318,17 @@ bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_t* scale_c
 // ------------------------------------------------------------------ peak probes
 
 namespace {
-int64_t mfma_flops(int kind) { return kind <= 1 ? 2LL * 32 * 32 * 16 : 2LL * 32 * 32 * 64; }
+int64_t mfma_flops(int kind) { return (kind == 2 || kind == 3) ? 2LL * 32 * 32 * 64 : 2LL * 32 * 32 * 16; }
 }  // namespace
 
 int64_t bsfp4_probe_mfma_flops(int kind, int iters) {
-  if (kind < 0 || kind > 3 || iters <= 0) return 0;
+  if (kind < 0 || kind > 5 || iters <= 0) return 0;
   // 8 MFMAs per iteration per wave, 4 waves per workgroup
   return bsfp4::probe_mfma_grid() * 4 * (int64_t)iters * 8 * mfma_flops(kind);
 }
 
 bsfp4_status bsfp4_probe_mfma(int kind, int iters, void* stream) {
-  if (kind < 0 || kind > 3) return fail(BSFP4_ERR_INVALID_ARG, "unknown MFMA probe kind %d", kind);
+  if (kind < 0 || kind > 5) return fail(BSFP4_ERR_INVALID_ARG, "unknown MFMA probe kind %d", kind);
   if (iters <= 0 || iters > (1 << 24)) return fail(BSFP4_ERR_SHAPE, "iters must be in [1, 2^24] (got %d)", iters);
   if (bsfp4_status s = check_device()) return s;
   return launched(bsfp4::launch_probe_mfma(kind, iters, as_stream(stream)), "bsfp4_probe_mfma launch");

@@ -6,8 +6,12 @@
 //                     issues MFMAs back to back from registers (no memory
 //                     traffic): KIND 0 fp16 32x32x16, 1 bf16 32x32x16,
 //                     2 fp8 (E4M3) 32x32x64, 3 fp4 (E2M1, E8M0 scale 1.0)
-//                     32x32x64 scaled MFMA.  Four 256-thread workgroups per
-//                     compute unit, i.e. four waves per SIMD.
+//                     32x32x64 scaled MFMA; 4 and 5 are fp16 and bf16 with
+//                     operands of at most 3 significant bits (as the exactly
+//                     dequantised E2M1 x E4M3 values have few), since the
+//                     sustained MFMA rate of a power-limited part depends on
+//                     how many operand bits toggle.  Four 256-thread
+//                     workgroups per compute unit.
 //   read_probe        streams a buffer once with 128-bit loads (four in
 //                     flight per lane), keeping a running XOR; nothing is
 //                     stored unless the flag (never set by the library) asks.
@@ -23,20 +27,29 @@ __global__ void __launch_bounds__(256) mfma_probe(int iters, int flag, float* si
   v16f acc[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) acc[j] = v16f{};
-  if constexpr (KIND <= 1) {
+  if constexpr (KIND <= 1 || KIND >= 4) {
     v8h a, b;
     v8bf ab, bb;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      a[i] = (_Float16)(0.001f * (lane + i));
-      b[i] = (_Float16)(0.002f * (lane - i));
-      ab[i] = (__bf16)(0.001f * (lane + i));
-      bb[i] = (__bf16)(0.002f * (lane - i));
+      float x, y;
+      if constexpr (KIND >= 4) {
+        // (1 + m/4) * 2^e, m in 0..3, |e| <= 3: at most 3 significant bits
+        x = (1.0f + 0.25f * ((lane + i) & 3)) * (float)(1 << ((lane >> 2) & 3)) * 0.125f;
+        y = ((i & 1) ? -1.0f : 1.0f) * (1.0f + 0.25f * ((lane * 3 + i) & 3)) * (float)(1 << (i & 3)) * 0.25f;
+      } else {
+        x = 0.001f * (lane + i);
+        y = 0.002f * (lane - i);
+      }
+      a[i] = (_Float16)x;
+      b[i] = (_Float16)y;
+      ab[i] = (__bf16)x;
+      bb[i] = (__bf16)y;
     }
     for (int it = 0; it < iters; it++) {
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        if constexpr (KIND == 0)
+        if constexpr (KIND == 0 || KIND == 4)
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
         else
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb, acc[j], 0, 0, 0);
@@ -88,7 +101,9 @@ hipError_t launch_probe_mfma(int kind, int iters, hipStream_t stream) {
     case 0: mfma_probe<0><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
     case 1: mfma_probe<1><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
     case 2: mfma_probe<2><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
-    default: mfma_probe<3><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 3: mfma_probe<3><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 4: mfma_probe<4><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    default: mfma_probe<5><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
   }
   return hipGetLastError();
 }
