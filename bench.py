@@ -91,9 +91,12 @@ def counter_summary(path: str) -> str:
     med = {k: float(np.median(v)) for k, v in vals.items()}
     counts = {k: len(v) for k, v in vals.items()}
     factor = {}
-    for (name, grid, ctr), v in med.items():
-        if "copyBuffer" in name and ctr in ("FETCH_SIZE", "WRITE_SIZE") and v > 0:
-            factor[ctr] = (256 << 20) / 1024.0 / v
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        # the calibration copy is the largest copyBuffer dispatch (the others are
+        # small host-to-device copies of the inputs)
+        cands = [v for (name, grid, c), v in med.items() if "copyBuffer" in name and c == ctr and v > 0]
+        if cands and max(cands) > 65536:
+            factor[ctr] = (256 << 20) / 1024.0 / max(cands)
     lines = ["| kernel | grid | counter | dispatches | median per dispatch | scaled MB |",
              "|---|---|---|---|---|---|"]
     for (name, grid, ctr), v in sorted(med.items(), key=lambda kv: (kv[0][0], kv[0][1], kv[0][2])):
@@ -108,21 +111,23 @@ def counter_summary(path: str) -> str:
 
 
 def trace_summary(path: str) -> str:
-    """Markdown table of kernel durations (us) per kernel name from a rocprofv3
-    --kernel-trace CSV: launches, median, p10, p90, min, max, mean."""
+    """Markdown table of kernel durations (us) per (kernel name, grid size) from
+    a rocprofv3 --kernel-trace CSV: launches, median, p10, p90, min, max, mean."""
     import csv
     from collections import defaultdict
     dur = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+            grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-            dur[name].append((t1 - t0) / 1e3)
-    lines = ["| kernel | launches | median us | p10 | p90 | min | max | mean |", "|---|---|---|---|---|---|---|---|"]
-    for name, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+            dur[(name, grid)].append((t1 - t0) / 1e3)
+    lines = ["| kernel | grid (threads) | launches | median us | p10 | p90 | min | max | mean |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
         a = np.array(v)
         short = name if len(name) <= 110 else name[:107] + "..."
-        lines.append(f"| `{short}` | {a.size} | {np.median(a):.2f} | {np.percentile(a, 10):.2f} | "
+        lines.append(f"| `{short}` | {grid} | {a.size} | {np.median(a):.2f} | {np.percentile(a, 10):.2f} | "
                      f"{np.percentile(a, 90):.2f} | {a.min():.2f} | {a.max():.2f} | {a.mean():.2f} |")
     return "\n".join(lines)
 
