@@ -37,6 +37,7 @@
 //            slower).  The tile's f indices are loaded when the tile starts and
 //            reach the epilogue through LDS.
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 #include "launchers.h"
@@ -157,19 +158,29 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Workgroups per CU the register budget is sized for: small tiles keep two
 // resident so that one's loads overlap the other's MFMAs.
-template <int BM, int BN>
-constexpr int wg_per_cu() { return BM * BN <= 128 * 128 ? 2 : 1; }
-
-// kDMA: K % 128 == 0 required; SK = 128 and a kRing-stage LDS ring filled by
-// direct-to-LDS buffer loads.  Otherwise: register-staged double buffer, any
+// kDMA: an RING-stage LDS ring filled by direct-to-LDS buffer loads, stages of
+// SK = 128 values (64 code bytes per row: each load moves 16 rows x 64 B;
+// K % 128 == 0) or SK = 256 values (128 B per row: each load moves 8 rows x
+// 128 B, whole cache lines, which the memory pipeline serves at a higher rate
+// per request; K % 256 == 0).  Otherwise: register-staged double buffer, any
 // K % 32.
-constexpr int kRing = 4;
+template <int BM, int BN, int SK, int RING>
+constexpr int ring_lds_bytes() { return RING * (BM + BN) * (SK / 2 + SK / 32); }
+
+// Workgroups per CU the register budget and LDS are sized for: small tiles keep
+// two resident so that one's loads overlap the other's MFMAs (when two rings fit
+// in the 160 KB of LDS).
+template <int BM, int BN, int SK, int RING>
+constexpr int wg_per_cu() {
+  return (BM * BN <= 128 * 128 && 2 * (ring_lds_bytes<BM, BN, SK, RING>() + 2048) <= 160 * 1024) ? 2 : 1;
+}
 
 // kLoaders: waves that issue the ring's loads (0: all).
-template <int BM, int BN, int WGN, int SK, int EPI, bool kDMA, int kLoaders>
-__global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_grouped(Args p) {
+template <int BM, int BN, int WGN, int SK, int EPI, bool kDMA, int kLoaders, int RING>
+__global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mxfp4_grouped(Args p) {
   constexpr int NT = 128 * WGN;  // 2 x WGN waves
-  static_assert(!kDMA || SK == 128, "the LDS ring uses 128-value stages");
+  static_assert(!kDMA || SK == 128 || SK == 256, "the LDS ring uses 128- or 256-value stages");
+  static_assert(!kDMA || (RING >= 2 && RING <= 4), "ring depth");
   using Gm = Geo<SK>;
   constexpr int kRowBytes = Gm::kRowBytes, kRowScales = Gm::kRowScales;
   constexpr int WM = BM / 2, WN = BN / WGN;
@@ -187,8 +198,8 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
   // LDS-staged output tile (ring kernel): bf16 or FP32 rows padded by 16 bytes
   constexpr int kOutElem = EPI == kEpiCombine ? 4 : 2;
   constexpr int kOutPitch = BN * kOutElem + 16;
-  static_assert(!kDMA || EPI == kEpiSilu || BM * kOutPitch <= kRing * kStage, "output tile fits in the ring");
-  constexpr int kSlots = kDMA ? kRing : 2;
+  static_assert(!kDMA || EPI == kEpiSilu || BM * kOutPitch <= RING * kStage, "output tile fits in the ring");
+  constexpr int kSlots = kDMA ? RING : 2;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int row_f[EPI == kEpiCombine ? BM : 1];
@@ -319,16 +330,21 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
     const int nst = (K + SK - 1) / SK;
     if constexpr (kDMA) {
       // Direct-to-LDS ring, filled by kLoad waves (all waves, or the first
-      // kLoaders).  Per stage: (BM+BN)/16 code loads of 16 rows x 64 B and
-      // (BM+BN)/64 scale loads of 64 rows x 4 B; each lane keeps one 32-bit
-      // offset per load (kBufOOB for rows outside the problem), the stage's K
-      // offset goes in the SGPR offset.
+      // kLoaders).  Per stage: (BM+BN)/kRowsLoad code loads of kRowsLoad rows x
+      // kRowBytes (1 KB each) and (BM+BN)/kScRowsLoad scale loads of 4 B per
+      // lane; each lane keeps one 32-bit offset per load (kBufOOB for rows
+      // outside the problem), the stage's K offset goes in the SGPR offset.
       constexpr int kWaves = NT / 64;
       constexpr int kLoad = kLoaders > 0 ? kLoaders : kWaves;
-      constexpr int kCodeI = (BM + BN) / 16 / kLoad;
-      constexpr int kScaleI = (BM + BN) / 64 / kLoad;
-      static_assert(kCodeI * kLoad * 16 == BM + BN && kScaleI * kLoad * 64 == BM + BN,
+      constexpr int kLanesRow = kRowBytes / 16;        // lanes per row of a code load
+      constexpr int kRowsLoad = 64 / kLanesRow;         // rows per code load (16 or 8)
+      constexpr int kScLanesRow = kRowScales / 4;       // lanes per row of a scale load
+      constexpr int kScRowsLoad = 64 / kScLanesRow;     // rows per scale load (64 or 32)
+      constexpr int kCodeI = (BM + BN) / kRowsLoad / kLoad;
+      constexpr int kScaleI = (BM + BN) / kScRowsLoad / kLoad;
+      static_assert(kCodeI * kLoad * kRowsLoad == BM + BN && kScaleI * kLoad * kScRowsLoad == BM + BN,
                     "DMA loads must cover the tile rows exactly");
+      static_assert(BM % kScRowsLoad == 0 && BM % kRowsLoad == 0, "a load holds rows of one operand");
       constexpr int kL = kCodeI + kScaleI;  // ring loads per loading wave per stage
       const bool loader = wave < kLoad;
       const v4u32 ra_q = make_rsrc4(p.A, (int64_t)a_lim * (K / 2));
@@ -339,10 +355,10 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
 #pragma unroll
       for (int j = 0; j < kCodeI; j++) {
         const int q = (loader ? wave : 0) * kCodeI + j;  // load index in the stage
-        const bool isA = q < BM / 16;
-        const int qq = isA ? q : q - BM / 16;
-        const int row = qq * 16 + (lane >> 2);  // tile row of this lane's chunk
-        const int c = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);  // logical chunk
+        const bool isA = q < BM / kRowsLoad;
+        const int qq = isA ? q : q - BM / kRowsLoad;
+        const int row = qq * kRowsLoad + lane / kLanesRow;  // tile row of this lane's chunk
+        const int c = Gm::swz(row, lane % kLanesRow);       // logical chunk landing at LDS position lane % kLanesRow
         const int gr = isA ? amap(row) : bmap(row);
         const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
         cv[j] = ok ? (uint32_t)(gr * (K / 2) + c * 16) : kBufOOB;
@@ -350,61 +366,65 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
 #pragma unroll
       for (int j = 0; j < kScaleI; j++) {
         const int q = (loader ? wave : 0) * kScaleI + j;
-        const bool isA = q < BM / 64;
-        const int qq = isA ? q : q - BM / 64;
-        const int row = qq * 64 + lane;
+        const bool isA = q < BM / kScRowsLoad;
+        const int qq = isA ? q : q - BM / kScRowsLoad;
+        const int row = qq * kScRowsLoad + lane / kScLanesRow;
         const int gr = isA ? amap(row) : bmap(row);
         const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        sv[j] = ok ? (uint32_t)(gr * (K / 32)) : kBufOOB;
+        sv[j] = ok ? (uint32_t)(gr * (K / 32) + (lane % kScLanesRow) * 4) : kBufOOB;
       }
       const uint32_t lds0 = lds_offset(smem);
       auto issue = [&](int st) {
-        const uint32_t slot = lds0 + (uint32_t)((st % kRing) * kStage);
+        const uint32_t slot = lds0 + (uint32_t)((st % RING) * kStage);
 #pragma unroll
         for (int j = 0; j < kCodeI; j++) {
           const int q = wave * kCodeI + j;
-          const bool isA = q < BM / 16;
-          const uint32_t dst = slot + (uint32_t)((isA ? 0 : kA) + (isA ? q : q - BM / 16) * 1024);
+          const bool isA = q < BM / kRowsLoad;
+          const uint32_t dst = slot + (uint32_t)((isA ? 0 : kA) + (isA ? q : q - BM / kRowsLoad) * 1024);
           buf_lds16(uniform4(isA ? ra_q : rw_q), cv[j], (uint32_t)(st * (SK / 2)),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
         }
 #pragma unroll
         for (int j = 0; j < kScaleI; j++) {
           const int q = wave * kScaleI + j;
-          const bool isA = q < BM / 64;
+          const bool isA = q < BM / kScRowsLoad;
           const uint32_t dst =
-              slot + (uint32_t)(kA + kB + (isA ? 0 : BM * kRowScales) + (isA ? q : q - BM / 64) * 256);
+              slot + (uint32_t)(kA + kB + (isA ? 0 : BM * kRowScales) + (isA ? q : q - BM / kScRowsLoad) * 256);
           buf_lds4(uniform4(isA ? ra_s : rw_s), sv[j], (uint32_t)(st * (SK / 32)),
                    (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
         }
       };
       if (loader)
-        for (int st = 0; st < kRing - 1 && st < nst; st++) issue(st);
+        for (int st = 0; st < RING - 1 && st < nst; st++) issue(st);
       for (int s = 0; s < nst; s++) {
         if (loader) {
-          const int ahead = min(kRing - 2, nst - 1 - s);  // stages issued after s
+          const int ahead = min(RING - 2, nst - 1 - s);  // stages issued after s
           if (ahead >= 2) wait_vmcnt<2 * kL>();
           else if (ahead == 1) wait_vmcnt<kL>();
           else wait_vmcnt<0>();
         }
         __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
-        if (loader && s + kRing - 1 < nst) issue(s + kRing - 1);
-        const uint8_t* st = smem + (s % kRing) * kStage;
+        if (loader && s + RING - 1 < nst) issue(s + RING - 1);
+        const uint8_t* st = smem + (s % RING) * kStage;
         const uint8_t* qa = st;
         const uint8_t* qb = st + kA;
         const uint8_t* sa = st + kA + kB;
         const uint8_t* sb = sa + BM * kRowScales;
-        // the 4 scale bytes of a fragment row as one dword (lanes g = 0 / 1 of a
-        // row read the same dword), shifted so that byte 2j is this lane's
-        // chunk 2j + g; the MFMA's op_sel picks byte 2j
-        static_assert(kRowScales == 4, "one scale dword per row per stage");
-        uint32_t xa4[TM], xb4[TN];
+        // the scale bytes of a fragment row, one dword per 4 (lanes g = 0 / 1
+        // of a row read the same dwords), shifted so that byte 2(j%2) of dword
+        // j/2 is this lane's chunk 2j + g; the MFMA's op_sel picks that byte
+        constexpr int kScW = kRowScales / 4;
+        uint32_t xa4[TM][kScW], xb4[TN][kScW];
 #pragma unroll
         for (int i = 0; i < TN; i++)
-          xb4[i] = *reinterpret_cast<const uint32_t*>(sb + (wn * WN + i * 32 + lr) * 4) >> (8 * g);
+#pragma unroll
+          for (int d = 0; d < kScW; d++)
+            xb4[i][d] = *reinterpret_cast<const uint32_t*>(sb + (wn * WN + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
 #pragma unroll
         for (int i = 0; i < TM; i++)
-          xa4[i] = *reinterpret_cast<const uint32_t*>(sa + (wm * WM + i * 32 + lr) * 4) >> (8 * g);
+#pragma unroll
+          for (int d = 0; d < kScW; d++)
+            xa4[i][d] = *reinterpret_cast<const uint32_t*>(sa + (wm * WM + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
 #pragma unroll
         for (int j = 0; j < SK / 64; j++) {
           const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
@@ -422,16 +442,17 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN>())) mxfp4_groupe
             const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   #pragma unroll
             for (int jn = 0; jn < TN; jn++) {
-              if (j == 0)
+              const int xa = (int)xa4[i][j / 2], xb = (int)xb4[jn][j / 2];
+              if (j % 2 == 0)
                 acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fb[jn], fa, acc[i][jn], 4, 4, 0, (int)xb4[jn], 0, (int)xa4[i])
+                                         fb[jn], fa, acc[i][jn], 4, 4, 0, xb, 0, xa)
                                    : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fa, fb[jn], acc[i][jn], 4, 4, 0, (int)xa4[i], 0, (int)xb4[jn]);
+                                         fa, fb[jn], acc[i][jn], 4, 4, 0, xa, 0, xb);
               else
                 acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fb[jn], fa, acc[i][jn], 4, 4, 2, (int)xb4[jn], 2, (int)xa4[i])
+                                         fb[jn], fa, acc[i][jn], 4, 4, 2, xb, 2, xa)
                                    : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fa, fb[jn], acc[i][jn], 4, 4, 2, (int)xa4[i], 2, (int)xb4[jn]);
+                                         fa, fb[jn], acc[i][jn], 4, 4, 2, xa, 2, xb);
             }
           }
         }
@@ -633,22 +654,49 @@ int loaders() {
   return e ? atoi(e) : 0;
 }
 
-template <int BM, int BN, int WGN, int SK, int EPI>
-hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
-  constexpr int NT = 128 * WGN;
-  int64_t grid = (int64_t)device_cu_count() * wg_per_cu<BM, BN>();
-  if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
-  if (a.K % 128 == 0) {
-    const int l = loaders();
-    if (l == 2 && (BM + BN) / 64 % 2 == 0)
-      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, 2><<<(unsigned)grid, NT, 0, stream>>>(a);
-    else if (l == 4 && NT / 64 > 4 && (BM + BN) / 64 % 4 == 0)
-      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, (NT / 64 > 4 ? 4 : 0)><<<(unsigned)grid, NT, 0, stream>>>(a);
-    else
-      mxfp4_grouped<BM, BN, WGN, 128, EPI, true, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
+// Ring form (measurement overrides): BSFP4_MXFP4_RING = "128x4" (128-value
+// stages, 4 slots), "256x2" or "256x3" (256-value stages, 2 or 3 slots).
+// 0: the default for the tile.
+int ring_form(int def) {
+  const char* e = getenv("BSFP4_MXFP4_RING");
+  if (!e) return def;
+  if (!strcmp(e, "128x4")) return 0;
+  if (!strcmp(e, "256x2")) return 1;
+  if (!strcmp(e, "256x3")) return 2;
+  return def;
+}
+
+template <int BM, int BN, int WGN, int EPI, int SK, int RING, int LOADERS>
+hipError_t launch_ring(const Args& a, int64_t max_items, hipStream_t stream) {
+  if constexpr (RING > 2 && ring_lds_bytes<BM, BN, SK, RING>() + 4096 > 160 * 1024) {
+    // a deeper ring of this tile does not fit in LDS: two slots
+    return launch_ring<BM, BN, WGN, EPI, SK, 2, LOADERS>(a, max_items, stream);
   } else {
-    mxfp4_grouped<BM, BN, WGN, SK, EPI, false, 0><<<(unsigned)grid, NT, 0, stream>>>(a);
+    constexpr int NT = 128 * WGN;
+    int64_t grid = (int64_t)device_cu_count() * wg_per_cu<BM, BN, SK, RING>();
+    if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
+    mxfp4_grouped<BM, BN, WGN, SK, EPI, true, LOADERS, RING><<<(unsigned)grid, NT, 0, stream>>>(a);
+    return hipGetLastError();
   }
+}
+
+template <int BM, int BN, int WGN, int SK, int EPI>
+hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream, int def_form = 0) {
+  constexpr int NT = 128 * WGN;
+  if (a.K % 128 == 0) {
+    int form = ring_form(def_form);
+    if (form != 0 && a.K % 256 != 0) form = 0;
+    if (form == 1) return launch_ring<BM, BN, WGN, EPI, 256, 2, 0>(a, max_items, stream);
+    if (form == 2) return launch_ring<BM, BN, WGN, EPI, 256, 3, 0>(a, max_items, stream);
+    const int l = loaders();
+    if (l == 2 && (BM + BN) / 64 % 2 == 0) return launch_ring<BM, BN, WGN, EPI, 128, 4, 2>(a, max_items, stream);
+    if (l == 4 && NT / 64 > 4 && (BM + BN) / 64 % 4 == 0)
+      return launch_ring<BM, BN, WGN, EPI, 128, 4, (NT / 64 > 4 ? 4 : 0)>(a, max_items, stream);
+    return launch_ring<BM, BN, WGN, EPI, 128, 4, 0>(a, max_items, stream);
+  }
+  int64_t grid = (int64_t)device_cu_count() * wg_per_cu<BM, BN, SK, 2>();
+  if (max_items < grid) grid = max_items < 1 ? 1 : max_items;
+  mxfp4_grouped<BM, BN, WGN, SK, EPI, false, 0, 2><<<(unsigned)grid, NT, 0, stream>>>(a);
   return hipGetLastError();
 }
 
