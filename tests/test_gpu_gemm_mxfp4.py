@@ -67,8 +67,20 @@ def test_mxfp4_gemm_deterministic():
 @pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("M,N,K", [(300, 544, 2048), (256, 256, 1536), (77, 96, 4096)])
 def test_mxfp4_gemm_loader_waves(monkeypatch, sg, waves, M, N, K):
-    """Loader-wave splits of the DMA ring and both wave layouts of the dense kernel."""
+    """Loader-wave splits of the 128-value DMA ring and both wave layouts of the dense kernel."""
+    monkeypatch.setenv("BSFP4_MXFP4_RING", "128x4")
     monkeypatch.setenv("BSFP4_MXFP4_LOADERS", sg)
     monkeypatch.setenv("BSFP4_MXFP4_WAVES", waves)
     aq, sfa, bq, sfb = mxfp4_problem(M, N, K, seed=900 + M)
+    _check(_run(aq, sfa, bq, sfb), aq, sfa, bq, sfb)
+
+
+@pytest.mark.parametrize("ring", ["128x4", "256x2", "256x3"])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (255, 288, 512), (513, 800, 2048), (300, 544, 1280)])
+def test_mxfp4_gemm_ring_forms(monkeypatch, ring, M, N, K):
+    """Every ring form of the dense kernel: 128-value stages in 4 slots, 256-value
+    stages (whole 128-byte rows per DMA request) in 2 or 3 slots; K = 256 is a
+    single stage, and K % 256 != 0 falls back to 128-value stages."""
+    monkeypatch.setenv("BSFP4_MXFP4_RING", ring)
+    aq, sfa, bq, sfb = mxfp4_problem(M, N, K, seed=950 + M)
     _check(_run(aq, sfa, bq, sfb), aq, sfa, bq, sfb)

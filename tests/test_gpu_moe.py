@@ -135,6 +135,17 @@ def test_moe_stagewise(case):
     _check_stages(*inputs, g)
 
 
+@pytest.mark.parametrize("ring", ["128x4", "256x2", "256x3"])
+def test_moe_stagewise_ring_forms(monkeypatch, ring):
+    """The grouped GEMMs in every ring form, on a shape where each workgroup runs
+    the next; ~640 items per GEMM for 512 workgroups): 1024 tokens, hidden
+    1024, intermediate 512, 32 experts, top-8."""
+    monkeypatch.setenv("BSFP4_MXFP4_RING", ring)
+    inputs = _layer_inputs(1024, 1024, 512, 32, 8, 77)
+    g = _gpu_stages(*inputs)
+    _check_stages(*inputs, g)
+
+
 def test_moe_layer_binding_matches_stages():
     T, H, I, E, topk, seed = CASES[0]
     x, ids, w, W13q, W13sf, W2q, W2sf = _layer_inputs(T, H, I, E, topk, seed)
