@@ -153,6 +153,7 @@ struct Args {
   uint8_t* out_sf;         // SILU: [rows, N/64]
   const int32_t* sorted_ids;  // COMBINE
   float* y_f32;               // COMBINE: [T * topk, N], row f = flat (token, slot) index
+  int lookahead;              // ring kernel: run the ring on into the next work item
 };
 
 constexpr int kMaxGroups = (int)kMaxExperts;
@@ -600,7 +601,7 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
         if (loader)
           for (int st = 0; st < RING - 1 && st < nst; st++) issue(Lc, st, gs + st);
       }
-      const bool has_next = kPrefetch && t + G < total;
+      const bool has_next = kPrefetch && p.lookahead && t + G < total;
       Item nxt = cur;
       Rows Rn;
       Loads Ln = Lc;
@@ -687,7 +688,7 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
       __syncthreads();  // every wave is done with this item's ring slots
       // with the prefetch, the slot of this item's last stage is free (the
       // next item's loads target the other slots); without it the whole ring
-      epilogue(cur, acc, rf, kPrefetch ? smem + ((gs + nst - 1) % RING) * kStage : smem);
+      epilogue(cur, acc, rf, (kPrefetch && p.lookahead) ? smem + ((gs + nst - 1) % RING) * kStage : smem);
       gs += nst;
       cur = nxt;
       Lc = Ln;
@@ -802,8 +803,17 @@ hipError_t launch_ring(const Args& a, int64_t max_items, hipStream_t stream) {
   }
 }
 
+// Cross-item look-ahead of the grouped ring kernel (BSFP4_MXFP4_LOOKAHEAD=1,
+// measurement override; off by default).
+int lookahead() {
+  const char* e = getenv("BSFP4_MXFP4_LOOKAHEAD");
+  return (e && e[0] == '1') ? 1 : 0;
+}
+
 template <int BM, int BN, int WGN, int SK, int EPI>
-hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
+hipError_t launch(const Args& a_in, int64_t max_items, hipStream_t stream) {
+  Args a = a_in;
+  a.lookahead = lookahead();
   constexpr int NT = 128 * WGN;
   if (a.K % 128 == 0) {
     int form = ring_form(a.K % 256 == 0 ? 1 : 0);
