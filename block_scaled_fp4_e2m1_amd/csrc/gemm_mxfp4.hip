@@ -153,7 +153,6 @@ struct Args {
   uint8_t* out_sf;         // SILU: [rows, N/64]
   const int32_t* sorted_ids;  // COMBINE
   float* y_f32;               // COMBINE: [T * topk, N], row f = flat (token, slot) index
-  int lookahead;              // ring kernel: run the ring on into the next work item
 };
 
 constexpr int kMaxGroups = (int)kMaxExperts;
@@ -204,12 +203,6 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
   constexpr int kOutPitch = BN * kOutElem + 16;
   static_assert(!kDMA || EPI == kEpiSilu || BM * kOutPitch <= RING * kStage, "output tile fits in the ring");
   constexpr int kSlots = kDMA ? RING : 2;
-  // Cross-item prefetch (grouped tiles: a workgroup runs several short work
-  // items) needs the output staging of the epilogue to fit in the one ring slot
-  // it leaves free (always true for SILU, which stages nothing).  The dense
-  // 256 x 256 form runs about one tile per workgroup and keeps its registers.
-  constexpr bool kPrefetch = kDMA && BM * BN <= 128 * 128 && (EPI == kEpiSilu || (BM / 2) * kOutPitch <= kStage);
-  constexpr int kEpiBytes = (kDMA && kPrefetch) ? kStage : kSlots * kStage;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSlots * kStage];
   __shared__ int tile_start[kMaxGroups + 1];
   __shared__ int row_f[EPI == kEpiCombine ? BM : 1];
@@ -267,11 +260,8 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
   const int slot = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const float alpha = p.alpha ? p.alpha[0] : 1.0f;
 
-  // ---- a work item: expert, first problem row, column tile
-  struct Item {
-    int e, m0, tn, nvalid_a;
-  };
-  auto locate = [&](int t) -> Item {
+  for (int t = slot; t < total; t += G) {
+    // ---- locate the work item
     int e = 0, row0, row_end, nmt;
     if (p.offsets == nullptr) {
       nmt = (p.rows + BM - 1) / BM;
@@ -302,98 +292,275 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
       tn = local / nmt;
       tmi = local % nmt;
     }
-    return Item{e, row0 + tmi * BM, tn, row_end < p.rows ? row_end : p.rows};
-  };
-  // rows of A a problem row may address (the gather index is bounded by it)
-  auto a_lim_of = [&](const Item& it) { return p.a_rows ? p.a_nrows : it.nvalid_a; };
-  // problem row m0 + i -> row of A, before the gather (-1: beyond the group)
-  auto arow = [&](const Item& it, int i) -> int {
-    const int m = it.m0 + i;
-    return m < it.nvalid_a ? m : -1;
-  };
-  auto amap = [&](const Item& it, int i) -> int {
-    const int m = arow(it, i);
-    if (m < 0) return -1;
-    return p.a_rows ? p.a_rows[m] : m;
-  };
-  auto bmap = [&](const Item& it, int i) -> int {
-    if constexpr (EPI == kEpiSilu) {
-      // LDS row i: wave column half wc = i / WN, column tile jn = (i % WN) / 32;
-      // even jn = gate, odd jn = up, act block b = tn*(BN/64) + wc*(TN/2) + jn/2
-      const int wc = i / WN, jn = (i % WN) >> 5;
-      const int b = it.tn * (BN / 64) + wc * (TN / 2) + (jn >> 1);
-      if (32 * b >= p.N / 2) return -1;
-      return ((jn & 1) ? p.N / 2 : 0) + 32 * b + (i & 31);
-    } else {
-      return it.tn * BN + i;
-    }
-  };
-  // COMBINE: flat (token, slot) index of tile row tid
-  auto row_flat = [&](const Item& it) -> int {
-    if constexpr (EPI == kEpiCombine) {
-      if (tid < BM && it.m0 + tid < it.nvalid_a) return p.sorted_ids[it.m0 + tid];
-    }
-    return -1;
-  };
+    const int m0 = row0 + tmi * BM;
+    const int nvalid_a = row_end < p.rows ? row_end : p.rows;
+    const uint8_t* Wq = p.W + (int64_t)e * p.N * (K / 2);
+    const uint8_t* Ws = p.WSF + (int64_t)e * p.N * (K / 32);
 
-  // ---- epilogues.  A first: acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) +
-  //      4g + r%4, tile column wn*WN + 32jn + lr.  B first: acc[i][jn][r] =
-  //      tile row wm*WM + 32i + lr, tile column wn*WN + 32jn + 8(r/4) + 4g + r%4.
-  //      `buf` (ring kernel): kStage bytes of LDS that no load targets now.
-  auto epilogue = [&](const Item& it, v16f (&acc)[TM][TN], int rf, uint8_t* buf) {
-    const int m0 = it.m0, tn = it.tn, nvalid_a = it.nvalid_a;
+    // A row of problem row m0 + i (-1: beyond this group / the problem)
+    auto amap = [&](int i) -> int {
+      const int m = m0 + i;
+      if (m >= nvalid_a) return -1;
+      return p.a_rows ? p.a_rows[m] : m;
+    };
+    const int a_lim = p.a_rows ? p.a_nrows : nvalid_a;
+    auto bmap = [&](int i) -> int {
+      if constexpr (EPI == kEpiSilu) {
+        // LDS row i: wave column half wc = i / WN, column tile jn = (i % WN) / 32;
+        // even jn = gate, odd jn = up, act block b = tn*(BN/64) + wc*(TN/2) + jn/2
+        const int wc = i / WN, jn = (i % WN) >> 5;
+        const int b = tn * (BN / 64) + wc * (TN / 2) + (jn >> 1);
+        if (32 * b >= p.N / 2) return -1;
+        return ((jn & 1) ? p.N / 2 : 0) + 32 * b + (i & 31);
+      } else {
+        return tn * BN + i;
+      }
+    };
+
+    // COMBINE: flat index of tile row tid, loaded before the K loop's loads so
+    // that it has arrived when the epilogue needs it
+    int rf = -1;
+    if constexpr (EPI == kEpiCombine) {
+      if (tid < BM && m0 + tid < nvalid_a) rf = p.sorted_ids[m0 + tid];
+    }
+
+    v16f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+      for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
+
+    const int nst = (K + SK - 1) / SK;
+    if constexpr (kDMA) {
+      // Direct-to-LDS ring, filled by kLoad waves (all waves, or the first
+      // kLoaders).  Per stage: (BM+BN)/kRowsLoad code loads of kRowsLoad rows x
+      // kRowBytes (1 KB each) and (BM+BN)/kScRowsLoad scale loads of 4 B per
+      // lane; each lane keeps one 32-bit offset per load (kBufOOB for rows
+      // outside the problem), the stage's K offset goes in the SGPR offset.
+      constexpr int kWaves = NT / 64;
+      constexpr int kLoad = kLoaders > 0 ? kLoaders : kWaves;
+      constexpr int kLanesRow = kRowBytes / 16;        // lanes per row of a code load
+      constexpr int kRowsLoad = 64 / kLanesRow;         // rows per code load (16 or 8)
+      constexpr int kScLanesRow = kRowScales / 4;       // lanes per row of a scale load
+      constexpr int kScRowsLoad = 64 / kScLanesRow;     // rows per scale load (64 or 32)
+      constexpr int kCodeI = (BM + BN) / kRowsLoad / kLoad;
+      constexpr int kScaleI = (BM + BN) / kScRowsLoad / kLoad;
+      static_assert(kCodeI * kLoad * kRowsLoad == BM + BN && kScaleI * kLoad * kScRowsLoad == BM + BN,
+                    "DMA loads must cover the tile rows exactly");
+      static_assert(BM % kScRowsLoad == 0 && BM % kRowsLoad == 0, "a load holds rows of one operand");
+      constexpr int kL = kCodeI + kScaleI;  // ring loads per loading wave per stage
+      const bool loader = wave < kLoad;
+      const v4u32 ra_q = make_rsrc4(p.A, (int64_t)a_lim * (K / 2));
+      const v4u32 ra_s = make_rsrc4(p.SFA, (int64_t)a_lim * (K / 32));
+      const v4u32 rw_q = make_rsrc4(Wq, (int64_t)p.N * (K / 2));
+      const v4u32 rw_s = make_rsrc4(Ws, (int64_t)p.N * (K / 32));
+      uint32_t cv[kCodeI], sv[kScaleI];
+#pragma unroll
+      for (int j = 0; j < kCodeI; j++) {
+        const int q = (loader ? wave : 0) * kCodeI + j;  // load index in the stage
+        const bool isA = q < BM / kRowsLoad;
+        const int qq = isA ? q : q - BM / kRowsLoad;
+        const int row = qq * kRowsLoad + lane / kLanesRow;  // tile row of this lane's chunk
+        const int c = Gm::swz(row, lane % kLanesRow);       // logical chunk landing at LDS position lane % kLanesRow
+        const int gr = isA ? amap(row) : bmap(row);
+        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
+        cv[j] = ok ? (uint32_t)(gr * (K / 2) + c * 16) : kBufOOB;
+      }
+#pragma unroll
+      for (int j = 0; j < kScaleI; j++) {
+        const int q = (loader ? wave : 0) * kScaleI + j;
+        const bool isA = q < BM / kScRowsLoad;
+        const int qq = isA ? q : q - BM / kScRowsLoad;
+        const int row = qq * kScRowsLoad + lane / kScLanesRow;
+        const int gr = isA ? amap(row) : bmap(row);
+        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
+        sv[j] = ok ? (uint32_t)(gr * (K / 32) + (lane % kScLanesRow) * 4) : kBufOOB;
+      }
+      const uint32_t lds0 = lds_offset(smem);
+      auto issue = [&](int st) {
+        const uint32_t slot = lds0 + (uint32_t)((st % RING) * kStage);
+#pragma unroll
+        for (int j = 0; j < kCodeI; j++) {
+          const int q = wave * kCodeI + j;
+          const bool isA = q < BM / kRowsLoad;
+          const uint32_t dst = slot + (uint32_t)((isA ? 0 : kA) + (isA ? q : q - BM / kRowsLoad) * 1024);
+          buf_lds16(uniform4(isA ? ra_q : rw_q), cv[j], (uint32_t)(st * (SK / 2)),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
+        }
+#pragma unroll
+        for (int j = 0; j < kScaleI; j++) {
+          const int q = wave * kScaleI + j;
+          const bool isA = q < BM / kScRowsLoad;
+          const uint32_t dst =
+              slot + (uint32_t)(kA + kB + (isA ? 0 : BM * kRowScales) + (isA ? q : q - BM / kScRowsLoad) * 256);
+          buf_lds4(uniform4(isA ? ra_s : rw_s), sv[j], (uint32_t)(st * (SK / 32)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
+        }
+      };
+      if (loader)
+        for (int st = 0; st < RING - 1 && st < nst; st++) issue(st);
+      for (int s = 0; s < nst; s++) {
+        if (loader) {
+          const int ahead = min(RING - 2, nst - 1 - s);  // stages issued after s
+          if (ahead >= 2) wait_vmcnt<2 * kL>();
+          else if (ahead == 1) wait_vmcnt<kL>();
+          else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
+        if (loader && s + RING - 1 < nst) issue(s + RING - 1);
+        const uint8_t* st = smem + (s % RING) * kStage;
+        const uint8_t* qa = st;
+        const uint8_t* qb = st + kA;
+        const uint8_t* sa = st + kA + kB;
+        const uint8_t* sb = sa + BM * kRowScales;
+        // the scale bytes of a fragment row, one dword per 4 (lanes g = 0 / 1
+        // of a row read the same dwords), shifted so that byte 2(j%2) of dword
+        // j/2 is this lane's chunk 2j + g; the MFMA's op_sel picks that byte
+        constexpr int kScW = kRowScales / 4;
+        uint32_t xa4[TM][kScW], xb4[TN][kScW];
+#pragma unroll
+        for (int i = 0; i < TN; i++)
+#pragma unroll
+          for (int d = 0; d < kScW; d++)
+            xb4[i][d] = *reinterpret_cast<const uint32_t*>(sb + (wn * WN + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+          for (int d = 0; d < kScW; d++)
+            xa4[i][d] = *reinterpret_cast<const uint32_t*>(sa + (wm * WM + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
+#pragma unroll
+        for (int j = 0; j < SK / 64; j++) {
+          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
+          v8i fb[TN];
+  #pragma unroll
+          for (int i = 0; i < TN; i++) {
+            const int r = wn * WN + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
+            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          }
+  #pragma unroll
+          for (int i = 0; i < TM; i++) {
+            const int r = wm * WM + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
+            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  #pragma unroll
+            for (int jn = 0; jn < TN; jn++) {
+              const int xa = (int)xa4[i][j / 2], xb = (int)xb4[jn][j / 2];
+              if (j % 2 == 0)
+                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fb[jn], fa, acc[i][jn], 4, 4, 0, xb, 0, xa)
+                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fa, fb[jn], acc[i][jn], 4, 4, 0, xa, 0, xb);
+              else
+                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fb[jn], fa, acc[i][jn], 4, 4, 2, xb, 2, xa)
+                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                         fa, fb[jn], acc[i][jn], 4, 4, 2, xa, 2, xb);
+            }
+          }
+        }
+      }
+      __syncthreads();  // all waves are done with the ring before it is reused
+    } else {
+    Stage<BM, SK, NT> ra;
+      Stage<BN, SK, NT> rb;
+      load_stage<BM, SK, NT>(ra, p.A, p.SFA, amap, a_lim, K, 0, sc_aligned, tid);
+      load_stage<BN, SK, NT>(rb, Wq, Ws, bmap, p.N, K, 0, sc_aligned, tid);
+      store_stage<BM, SK, NT>(ra, smem, smem + kA + kB, tid);
+      store_stage<BN, SK, NT>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
+      __syncthreads();
+  
+      for (int s = 0; s < nst; s++) {
+        const bool more = s + 1 < nst;
+        if (more) {
+          load_stage<BM, SK, NT>(ra, p.A, p.SFA, amap, a_lim, K, (s + 1) * SK, sc_aligned, tid);
+          load_stage<BN, SK, NT>(rb, Wq, Ws, bmap, p.N, K, (s + 1) * SK, sc_aligned, tid);
+        }
+        const uint8_t* st = smem + (s & 1) * kStage;
+        const uint8_t* qa = st;
+        const uint8_t* qb = st + kA;
+        const uint8_t* sa = st + kA + kB;
+        const uint8_t* sb = sa + BM * kRowScales;
+  #pragma unroll
+        for (int j = 0; j < SK / 64; j++) {
+          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
+          v8i fb[TN];
+          int xb[TN];
+  #pragma unroll
+          for (int i = 0; i < TN; i++) {
+            const int r = wn * WN + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
+            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            xb[i] = sb[r * kRowScales + c];
+          }
+  #pragma unroll
+          for (int i = 0; i < TM; i++) {
+            const int r = wm * WM + i * 32 + lr;
+            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
+            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            const int xa = sa[r * kRowScales + c];
+  #pragma unroll
+            for (int jn = 0; jn < TN; jn++)
+              acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jn], fa, acc[i][jn], 4, 4, 0,
+                                                                                   xb[jn], 0, xa)
+                                 : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0,
+                                                                                   xa, 0, xb[jn]);
+          }
+        }
+        if (more) {
+          uint8_t* nx = smem + ((s + 1) & 1) * kStage;
+          store_stage<BM, SK, NT>(ra, nx, nx + kA + kB, tid);
+          store_stage<BN, SK, NT>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
+        }
+        __syncthreads();
+      }
+  
+    }
+
+    // ---- epilogues.  A first: acc[i][jn][r] = tile row wm*WM + 32i + 8(r/4) +
+    //      4g + r%4, tile column wn*WN + 32jn + lr.  B first: acc[i][jn][r] =
+    //      tile row wm*WM + 32i + lr, tile column wn*WN + 32jn + 8(r/4) + 4g + r%4.
     if constexpr (kDMA && EPI != kEpiSilu) {
-      // the tile goes through LDS: each lane writes its 4-column runs, then each
-      // store writes 16 contiguous bytes per lane, whole row segments of BN
-      // columns; a tile larger than one ring slot goes in two passes of one
-      // wave row each
-      constexpr int kPasses = BM * kOutPitch <= kEpiBytes ? 1 : 2;
-      static_assert(kPasses == 1 || (BM / 2) * kOutPitch <= kEpiBytes, "the output tile fits in the free LDS");
-      constexpr int kPassRows = BM / kPasses;
+      // the tile goes through LDS (the ring is free after the K loop's last
+      // barrier): each lane writes its 4-column runs, then each store writes
+      // 16 contiguous bytes per lane, whole row segments of BN columns
       if constexpr (EPI == kEpiCombine) {
         if (tid < BM) row_f[tid] = rf;
       }
 #pragma unroll
-      for (int ps = 0; ps < kPasses; ps++) {
-        if (kPasses == 1 || wm == ps) {
+      for (int i = 0; i < TM; i++) {
+        const int r = wm * WM + i * 32 + lr;
 #pragma unroll
-          for (int i = 0; i < TM; i++) {
-            const int r = wm * WM + i * 32 + lr - ps * kPassRows;
+        for (int jn = 0; jn < TN; jn++)
 #pragma unroll
-            for (int jn = 0; jn < TN; jn++)
-#pragma unroll
-              for (int q = 0; q < 4; q++) {
-                const int c = wn * WN + jn * 32 + 8 * q + 4 * g;
-                uint8_t* dst = buf + r * kOutPitch + c * kOutElem;
-                if constexpr (EPI == kEpiCombine)
-                  *reinterpret_cast<float4*>(dst) = make_float4(acc[i][jn][4 * q], acc[i][jn][4 * q + 1],
-                                                                acc[i][jn][4 * q + 2], acc[i][jn][4 * q + 3]);
-                else
-                  *reinterpret_cast<uint2*>(dst) =
-                      make_uint2(pack_bf16x2(alpha * acc[i][jn][4 * q], alpha * acc[i][jn][4 * q + 1]),
-                                 pack_bf16x2(alpha * acc[i][jn][4 * q + 2], alpha * acc[i][jn][4 * q + 3]));
-              }
+          for (int q = 0; q < 4; q++) {
+            const int c = wn * WN + jn * 32 + 8 * q + 4 * g;
+            uint8_t* dst = smem + r * kOutPitch + c * kOutElem;
+            if constexpr (EPI == kEpiCombine)
+              *reinterpret_cast<float4*>(dst) =
+                  make_float4(acc[i][jn][4 * q], acc[i][jn][4 * q + 1], acc[i][jn][4 * q + 2], acc[i][jn][4 * q + 3]);
+            else
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(pack_bf16x2(alpha * acc[i][jn][4 * q], alpha * acc[i][jn][4 * q + 1]),
+                             pack_bf16x2(alpha * acc[i][jn][4 * q + 2], alpha * acc[i][jn][4 * q + 3]));
           }
+      }
+      __syncthreads();
+      constexpr int kChunksPerRow = BN * kOutElem / 16;
+      for (int idx = tid; idx < BM * kChunksPerRow; idx += NT) {
+        const int r = idx / kChunksPerRow, cb = (idx % kChunksPerRow) * 16;  // byte offset in the row
+        const int n = tn * BN + cb / kOutElem;
+        if (n >= p.N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kOutPitch + cb);
+        if constexpr (EPI == kEpiCombine) {
+          // y[f] = row, f = flat (token, slot) index of the row; the weighted
+          // top-k sum is done afterwards in a fixed order (no atomics)
+          const int f = row_f[r];
+          if (f >= 0) *reinterpret_cast<uint4*>(p.y_f32 + (int64_t)f * p.N + n) = v;
+        } else {
+          const int m = m0 + r;
+          if (m < nvalid_a) *reinterpret_cast<uint4*>(p.out + (int64_t)m * p.N + n) = v;
         }
-        __syncthreads();
-        constexpr int kChunksPerRow = BN * kOutElem / 16;
-        for (int idx = tid; idx < kPassRows * kChunksPerRow; idx += NT) {
-          const int rl = idx / kChunksPerRow, cb = (idx % kChunksPerRow) * 16;  // byte offset in the row
-          const int r = rl + ps * kPassRows;
-          const int n = tn * BN + cb / kOutElem;
-          if (n >= p.N) continue;
-          const uint4 v = *reinterpret_cast<const uint4*>(buf + rl * kOutPitch + cb);
-          if constexpr (EPI == kEpiCombine) {
-            // y[f] = row, f = flat (token, slot) index of the row; the weighted
-            // top-k sum is done afterwards in a fixed order (no atomics)
-            const int f = row_f[r];
-            if (f >= 0) *reinterpret_cast<uint4*>(p.y_f32 + (int64_t)f * p.N + n) = v;
-          } else {
-            const int m = m0 + r;
-            if (m < nvalid_a) *reinterpret_cast<uint4*>(p.out + (int64_t)m * p.N + n) = v;
-          }
-        }
-        __syncthreads();
       }
     } else if constexpr (EPI == kEpiStore) {
 #pragma unroll
@@ -478,291 +645,7 @@ __global__ void __launch_bounds__(128 * WGN, (wg_per_cu<BM, BN, SK, RING>())) mx
         }
       }
     }
-  };
-
-  const int nst = (K + SK - 1) / SK;
-  if constexpr (kDMA) {
-    // Direct-to-LDS ring, filled by kLoad waves (all waves, or the first
-    // kLoaders).  Per stage: (BM+BN)/kRowsLoad code loads of kRowsLoad rows x
-    // kRowBytes (1 KB each) and (BM+BN)/kScRowsLoad scale loads of 4 B per
-    // lane; each lane keeps one 32-bit offset per load (kBufOOB for rows
-    // outside the problem), the stage's K offset goes in the SGPR offset.
-    // Stages are numbered across work items, so the ring runs on from one
-    // item into the next: the next item's rows are looked up during the
-    // current item's first stage and its first stages are issued in the
-    // current item's last RING-1 stages.
-    constexpr int kWaves = NT / 64;
-    constexpr int kLoad = kLoaders > 0 ? kLoaders : kWaves;
-    constexpr int kLanesRow = kRowBytes / 16;        // lanes per row of a code load
-    constexpr int kRowsLoad = 64 / kLanesRow;         // rows per code load (16 or 8)
-    constexpr int kScLanesRow = kRowScales / 4;       // lanes per row of a scale load
-    constexpr int kScRowsLoad = 64 / kScLanesRow;     // rows per scale load (64 or 32)
-    constexpr int kCodeI = (BM + BN) / kRowsLoad / kLoad;
-    constexpr int kScaleI = (BM + BN) / kScRowsLoad / kLoad;
-    static_assert(kCodeI * kLoad * kRowsLoad == BM + BN && kScaleI * kLoad * kScRowsLoad == BM + BN,
-                  "DMA loads must cover the tile rows exactly");
-    static_assert(BM % kScRowsLoad == 0 && BM % kRowsLoad == 0, "a load holds rows of one operand");
-    constexpr int kL = kCodeI + kScaleI;  // ring loads per loading wave per stage
-    const bool loader = wave < kLoad;
-    const int lw = loader ? wave : 0;
-    // tile row of this lane's chunk in code load j / scale load j
-    auto code_row = [&](int j, bool& isA) {
-      const int q = lw * kCodeI + j;
-      isA = q < BM / kRowsLoad;
-      return (isA ? q : q - BM / kRowsLoad) * kRowsLoad + lane / kLanesRow;
-    };
-    auto scale_row = [&](int j, bool& isA) {
-      const int q = lw * kScaleI + j;
-      isA = q < BM / kScRowsLoad;
-      return (isA ? q : q - BM / kScRowsLoad) * kScRowsLoad + lane / kScLanesRow;
-    };
-    struct Loads {
-      v4u32 ra_q, ra_s, rw_q, rw_s;
-      uint32_t cv[kCodeI], sv[kScaleI];
-    };
-    // the gathered A rows of an item's A-operand loads (p.a_rows lookups,
-    // issued early so that their latency hides behind a stage)
-    struct Rows {
-      int ca[kCodeI], sa[kScaleI];
-    };
-    auto fetch_rows = [&](const Item& it, Rows& R) {
-#pragma unroll
-      for (int j = 0; j < kCodeI; j++) {
-        bool isA;
-        const int row = code_row(j, isA);
-        R.ca[j] = isA ? amap(it, row) : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < kScaleI; j++) {
-        bool isA;
-        const int row = scale_row(j, isA);
-        R.sa[j] = isA ? amap(it, row) : -1;
-      }
-    };
-    auto setup = [&](const Item& it, const Rows& R, Loads& L) {
-      const int a_lim = a_lim_of(it);
-      const uint8_t* Wq = p.W + (int64_t)it.e * p.N * (K / 2);
-      const uint8_t* Ws = p.WSF + (int64_t)it.e * p.N * (K / 32);
-      L.ra_q = make_rsrc4(p.A, (int64_t)a_lim * (K / 2));
-      L.ra_s = make_rsrc4(p.SFA, (int64_t)a_lim * (K / 32));
-      L.rw_q = make_rsrc4(Wq, (int64_t)p.N * (K / 2));
-      L.rw_s = make_rsrc4(Ws, (int64_t)p.N * (K / 32));
-#pragma unroll
-      for (int j = 0; j < kCodeI; j++) {
-        bool isA;
-        const int row = code_row(j, isA);
-        const int c = Gm::swz(row, lane % kLanesRow);  // logical chunk landing at LDS position lane % kLanesRow
-        const int gr = isA ? R.ca[j] : bmap(it, row);
-        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        L.cv[j] = ok ? (uint32_t)(gr * (K / 2) + c * 16) : kBufOOB;
-      }
-#pragma unroll
-      for (int j = 0; j < kScaleI; j++) {
-        bool isA;
-        const int row = scale_row(j, isA);
-        const int gr = isA ? R.sa[j] : bmap(it, row);
-        const bool ok = gr >= 0 && gr < (isA ? a_lim : p.N);
-        L.sv[j] = ok ? (uint32_t)(gr * (K / 32) + (lane % kScLanesRow) * 4) : kBufOOB;
-      }
-    };
-    const uint32_t lds0 = lds_offset(smem);
-    // stage st of an item into ring slot gst % RING
-    auto issue = [&](const Loads& L, int st, int gst) {
-      const uint32_t slotb = lds0 + (uint32_t)((gst % RING) * kStage);
-#pragma unroll
-      for (int j = 0; j < kCodeI; j++) {
-        const int q = wave * kCodeI + j;
-        const bool isA = q < BM / kRowsLoad;
-        const uint32_t dst = slotb + (uint32_t)((isA ? 0 : kA) + (isA ? q : q - BM / kRowsLoad) * 1024);
-        buf_lds16(uniform4(isA ? L.ra_q : L.rw_q), L.cv[j], (uint32_t)(st * (SK / 2)),
-                  (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
-      }
-#pragma unroll
-      for (int j = 0; j < kScaleI; j++) {
-        const int q = wave * kScaleI + j;
-        const bool isA = q < BM / kScRowsLoad;
-        const uint32_t dst =
-            slotb + (uint32_t)(kA + kB + (isA ? 0 : BM * kRowScales) + (isA ? q : q - BM / kScRowsLoad) * 256);
-        buf_lds4(uniform4(isA ? L.ra_s : L.rw_s), L.sv[j], (uint32_t)(st * (SK / 32)),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
-      }
-    };
-
-    Item cur{0, 0, 0, 0};
-    Loads Lc;
-    bool primed = false;  // the current item's first RING-1 stages are issued
-    int gs = 0;           // ring stage number of the current item's stage 0
-    for (int t = slot; t < total; t += G) {
-      if (!primed) {
-        cur = locate(t);
-        Rows R;
-        fetch_rows(cur, R);
-        setup(cur, R, Lc);
-        if (loader)
-          for (int st = 0; st < RING - 1 && st < nst; st++) issue(Lc, st, gs + st);
-      }
-      const bool has_next = kPrefetch && p.lookahead && t + G < total;
-      Item nxt = cur;
-      Rows Rn;
-      Loads Ln = Lc;
-      const int rf = row_flat(cur);
-      v16f acc[TM][TN];
-#pragma unroll
-      for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
-      for (int s = 0; s < nst; s++) {
-        if (loader) {
-          // stages issued after stage s: the rest of this item's look-ahead and
-          // the next item's stages already issued
-          const int ahead = has_next ? RING - 2 : min(RING - 2, nst - 1 - s);
-          if (ahead >= 2) wait_vmcnt<2 * kL>();
-          else if (ahead == 1) wait_vmcnt<kL>();
-          else wait_vmcnt<0>();
-        }
-        __builtin_amdgcn_s_barrier();  // stage s visible; every wave is past stage s-1
-        if (s == 0 && has_next) {
-          // look the next item up now: its row-index loads land during this item
-          nxt = locate(t + G);
-          fetch_rows(nxt, Rn);
-        }
-        const int st_i = s + RING - 1;  // stage issued now
-        if (st_i < nst) {
-          if (loader) issue(Lc, st_i, gs + st_i);
-        } else if (has_next) {
-          if (st_i == nst) setup(nxt, Rn, Ln);
-          if (loader && st_i - nst < nst) issue(Ln, st_i - nst, gs + st_i);
-        }
-        const uint8_t* st = smem + ((gs + s) % RING) * kStage;
-        const uint8_t* qa = st;
-        const uint8_t* qb = st + kA;
-        const uint8_t* sa = st + kA + kB;
-        const uint8_t* sb = sa + BM * kRowScales;
-        // the scale bytes of a fragment row, one dword per 4 (lanes g = 0 / 1
-        // of a row read the same dwords), shifted so that byte 2(j%2) of dword
-        // j/2 is this lane's chunk 2j + g; the MFMA's op_sel picks that byte
-        constexpr int kScW = kRowScales / 4;
-        uint32_t xa4[TM][kScW], xb4[TN][kScW];
-#pragma unroll
-        for (int i = 0; i < TN; i++)
-#pragma unroll
-          for (int d = 0; d < kScW; d++)
-            xb4[i][d] = *reinterpret_cast<const uint32_t*>(sb + (wn * WN + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-          for (int d = 0; d < kScW; d++)
-            xa4[i][d] = *reinterpret_cast<const uint32_t*>(sa + (wm * WM + i * 32 + lr) * kRowScales + 4 * d) >> (8 * g);
-#pragma unroll
-        for (int j = 0; j < SK / 64; j++) {
-          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
-          v8i fb[TN];
-#pragma unroll
-          for (int i = 0; i < TN; i++) {
-            const int r = wn * WN + i * 32 + lr;
-            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
-            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int i = 0; i < TM; i++) {
-            const int r = wm * WM + i * 32 + lr;
-            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
-            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-#pragma unroll
-            for (int jn = 0; jn < TN; jn++) {
-              const int xa = (int)xa4[i][j / 2], xb = (int)xb4[jn][j / 2];
-              if (j % 2 == 0)
-                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fb[jn], fa, acc[i][jn], 4, 4, 0, xb, 0, xa)
-                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fa, fb[jn], acc[i][jn], 4, 4, 0, xa, 0, xb);
-              else
-                acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fb[jn], fa, acc[i][jn], 4, 4, 2, xb, 2, xa)
-                                   : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                         fa, fb[jn], acc[i][jn], 4, 4, 2, xa, 2, xb);
-            }
-          }
-        }
-      }
-      __syncthreads();  // every wave is done with this item's ring slots
-      // with the prefetch, the slot of this item's last stage is free (the
-      // next item's loads target the other slots); without it the whole ring
-      epilogue(cur, acc, rf, (kPrefetch && p.lookahead) ? smem + ((gs + nst - 1) % RING) * kStage : smem);
-      gs += nst;
-      cur = nxt;
-      Lc = Ln;
-      primed = has_next;
-    }
-  } else {
-    for (int t = slot; t < total; t += G) {
-      const Item it = locate(t);
-      const uint8_t* Wq = p.W + (int64_t)it.e * p.N * (K / 2);
-      const uint8_t* Ws = p.WSF + (int64_t)it.e * p.N * (K / 32);
-      const int a_lim = a_lim_of(it);
-      auto am = [&](int i) { return amap(it, i); };
-      auto bm = [&](int i) { return bmap(it, i); };
-      const int rf = row_flat(it);
-      v16f acc[TM][TN];
-#pragma unroll
-      for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = v16f{};
-      Stage<BM, SK, NT> ra;
-      Stage<BN, SK, NT> rb;
-      load_stage<BM, SK, NT>(ra, p.A, p.SFA, am, a_lim, K, 0, sc_aligned, tid);
-      load_stage<BN, SK, NT>(rb, Wq, Ws, bm, p.N, K, 0, sc_aligned, tid);
-      store_stage<BM, SK, NT>(ra, smem, smem + kA + kB, tid);
-      store_stage<BN, SK, NT>(rb, smem + kA, smem + kA + kB + BM * kRowScales, tid);
-      __syncthreads();
-
-      for (int s = 0; s < nst; s++) {
-        const bool more = s + 1 < nst;
-        if (more) {
-          load_stage<BM, SK, NT>(ra, p.A, p.SFA, am, a_lim, K, (s + 1) * SK, sc_aligned, tid);
-          load_stage<BN, SK, NT>(rb, Wq, Ws, bm, p.N, K, (s + 1) * SK, sc_aligned, tid);
-        }
-        const uint8_t* st = smem + (s & 1) * kStage;
-        const uint8_t* qa = st;
-        const uint8_t* qb = st + kA;
-        const uint8_t* sa = st + kA + kB;
-        const uint8_t* sb = sa + BM * kRowScales;
-#pragma unroll
-        for (int j = 0; j < SK / 64; j++) {
-          const int c = 2 * j + g;  // 16-byte chunk = K values 64j + 32g .. +32 of the stage
-          v8i fb[TN];
-          int xb[TN];
-#pragma unroll
-          for (int i = 0; i < TN; i++) {
-            const int r = wn * WN + i * 32 + lr;
-            const uint4 v = *reinterpret_cast<const uint4*>(qb + r * kRowBytes + Gm::swz(r, c) * 16);
-            fb[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            xb[i] = sb[r * kRowScales + c];
-          }
-#pragma unroll
-          for (int i = 0; i < TM; i++) {
-            const int r = wm * WM + i * 32 + lr;
-            const uint4 v = *reinterpret_cast<const uint4*>(qa + r * kRowBytes + Gm::swz(r, c) * 16);
-            const v8i fa = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            const int xa = sa[r * kRowScales + c];
-#pragma unroll
-            for (int jn = 0; jn < TN; jn++)
-              acc[i][jn] = kSwap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jn], fa, acc[i][jn], 4, 4, 0,
-                                                                                   xb[jn], 0, xa)
-                                 : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jn], acc[i][jn], 4, 4, 0,
-                                                                                   xa, 0, xb[jn]);
-          }
-        }
-        if (more) {
-          uint8_t* nx = smem + ((s + 1) & 1) * kStage;
-          store_stage<BM, SK, NT>(ra, nx, nx + kA + kB, tid);
-          store_stage<BN, SK, NT>(rb, nx + kA, nx + kA + kB + BM * kRowScales, tid);
-        }
-        __syncthreads();
-      }
-      epilogue(it, acc, rf, smem);
-      __syncthreads();  // LDS is reused by the next work item
-    }
+    __syncthreads();  // LDS is reused by the next work item
   }
 }
 
@@ -803,17 +686,8 @@ hipError_t launch_ring(const Args& a, int64_t max_items, hipStream_t stream) {
   }
 }
 
-// Cross-item look-ahead of the grouped ring kernel (BSFP4_MXFP4_LOOKAHEAD=1,
-// measurement override; off by default).
-int lookahead() {
-  const char* e = getenv("BSFP4_MXFP4_LOOKAHEAD");
-  return (e && e[0] == '1') ? 1 : 0;
-}
-
 template <int BM, int BN, int WGN, int SK, int EPI>
-hipError_t launch(const Args& a_in, int64_t max_items, hipStream_t stream) {
-  Args a = a_in;
-  a.lookahead = lookahead();
+hipError_t launch(const Args& a, int64_t max_items, hipStream_t stream) {
   constexpr int NT = 128 * WGN;
   if (a.K % 128 == 0) {
     int form = ring_form(a.K % 256 == 0 ? 1 : 0);
