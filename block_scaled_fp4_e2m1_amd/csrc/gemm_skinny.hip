@@ -432,6 +432,59 @@ __global__ void __launch_bounds__(512)
 // row's end only ever multiply zero codes.
 constexpr int kLdsMaxWaves = 8;
 
+// Code units of 128 K values are moved in pairs: one DMA instruction carries 8
+// rows x 128 B (a pair of units of 8 rows: whole cache lines; 16 rows x 64 B
+// per instruction, half lines, measured slower), so a pair of units of 16 rows
+// is two instructions into LDS laid out [pair][row][128 B].  16-byte piece p
+// (0..7) of row r sits at position p ^ (r & 7), so the 8 lanes of a 128-bit LDS
+// read (rows c .. c+7, one piece each) hit distinct banks.
+// LDS byte offset of unit i's piece g (0..3) of row c inside a wave's region:
+__device__ __forceinline__ int pair_rd(int i, int c, int g) {
+  return 2048 * (i >> 1) + c * 128 + ((((i & 1) * 4 + g) ^ (c & 7)) * 16);
+}
+
+// Issue the UW/2 unit pairs of 16 rows starting at global byte offset row0_off
+// (row r at row0_off + r * row_bytes), K values [k_lo, k_lo + 128 UW) of each
+// row; rows >= nrows and K beyond K read as zero.  dst: the wave's region.
+template <int UW>
+__device__ __forceinline__ void issue_pairs(v4u32 rsrc, uint32_t row0_off, uint32_t row_bytes, int nrows, int k_lo,
+                                            int K, const uint8_t* dst, int lane) {
+  static_assert(UW % 2 == 0, "units come in pairs");
+#pragma unroll
+  for (int u = 0; u < UW / 2; u++) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int r = h * 8 + (lane >> 3);
+      const int lp = (lane & 7) ^ (r & 7);  // logical piece landing at position lane & 7
+      const bool ok = r < nrows && k_lo + 256 * u + 32 * lp < K;
+      buf_lds16(rsrc, ok ? row0_off + (uint32_t)r * row_bytes + (uint32_t)(k_lo / 2 + 128 * u + 16 * lp) : kBufOOB, 0,
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(dst + 2048 * u + 1024 * h)));
+    }
+  }
+}
+
+// s_waitcnt vmcnt(n) for a run-time n that is a compile-time constant after
+// unrolling (n <= 14)
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    default: wait_vmcnt<14>(); break;
+  }
+}
+
 template <int UW>
 __global__ void __launch_bounds__(512)
     skinny_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
@@ -459,26 +512,11 @@ __global__ void __launch_bounds__(512)
     buf_lds16(ras, off < M * kb16 ? (uint32_t)off : kBufOOB, 0,
               (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsa + wave * 1024)));
   }
-  const int r = lane >> 2;                        // row of the DMA lane
-  const int piece = (lane & 3) ^ ((r >> 2) & 3);  // 16-byte piece it fetches
-  const uint32_t arow = (uint32_t)(r * (K / 2) + k_lo / 2 + 16 * piece);
-  const uint32_t brow = (uint32_t)((n0 + r) * (K / 2) + k_lo / 2 + 16 * piece);
-#pragma unroll
-  for (int i = 0; i < UW; i++) {
-    const bool ok = r < M && k_lo + 128 * i + 32 * piece < K;
-    buf_lds16(raq, ok ? arow + 64 * i : kBufOOB, 0,
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(laq + 1024 * i)));
-  }
-#pragma unroll
-  for (int i = 0; i < UW; i++) {
-    const bool ok = k_lo + 128 * i + 32 * piece < K;
-    buf_lds16(rbq, ok ? brow + 64 * i : kBufOOB, 0,
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lbq + 1024 * i)));
-  }
+  issue_pairs<UW>(raq, 0u, (uint32_t)(K / 2), M, k_lo, K, laq, lane);
+  issue_pairs<UW>(rbq, (uint32_t)(n0 * (K / 2)), (uint32_t)(K / 2), 16, k_lo, K, lbq, lane);
 
   // MFMA lane (c, g): row c, K values 128i + 32g + 8s (s = word of the piece)
   const int c = lane & 15, g = lane >> 4;
-  const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
   wait_vmcnt<UW>();  // scales and activations have landed; only weight units may be in flight
   __builtin_amdgcn_s_barrier();
   const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
@@ -491,7 +529,7 @@ __global__ void __launch_bounds__(512)
   v8h fa[UW][4];
 #pragma unroll
   for (int i = 0; i < UW; i++) {
-    const uint4 w = *reinterpret_cast<const uint4*>(laq + 1024 * i + rd);
+    const uint4 w = *reinterpret_cast<const uint4*>(laq + pair_rd(i, c, g));
     const v2h s = scales2(*reinterpret_cast<const uint16_t*>(sarow + 8 * i));
     fa[i][0] = dq8_f16(w.x, s[0]);
     fa[i][1] = dq8_f16(w.y, s[0]);
@@ -503,17 +541,8 @@ __global__ void __launch_bounds__(512)
   v4f acc = v4f{};
 #pragma unroll
   for (int i = 0; i < UW; i++) {
-    switch (UW - 1 - i) {  // weight unit i has landed
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1>(); break;
-      case 2: wait_vmcnt<2>(); break;
-      case 3: wait_vmcnt<3>(); break;
-      case 4: wait_vmcnt<4>(); break;
-      case 5: wait_vmcnt<5>(); break;
-      case 6: wait_vmcnt<6>(); break;
-      default: wait_vmcnt<7>(); break;
-    }
-    const uint4 w = *reinterpret_cast<const uint4*>(lbq + 1024 * i + rd);
+    if ((i & 1) == 0) wait_vmcnt_upto(UW - 2 - i);  // the weight pair of unit i has landed
+    const uint4 w = *reinterpret_cast<const uint4*>(lbq + pair_rd(i, c, g));
     const v2h s = scales2(*reinterpret_cast<const uint16_t*>(sbrow + 8 * i));
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.x, s[0]), fa[i][0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(w.y, s[0]), fa[i][1], acc, 0, 0, 0);
@@ -613,14 +642,7 @@ __global__ void __launch_bounds__(512)
     }
   }
   // ---- weight units
-  const int r = lane >> 2;
-  const int piece = (lane & 3) ^ ((r >> 2) & 3);
-  const uint32_t brow = (uint32_t)((n0 + r) * (K / 2) + k_lo / 2 + 16 * piece);
-#pragma unroll
-  for (int i = 0; i < UW; i++) {
-    const bool ok = k_lo + 128 * i + 32 * piece < K;
-    buf_lds16(rbq, ok ? brow + 64 * i : kBufOOB, 0, lds_u(lbq + 1024 * i));
-  }
+  issue_pairs<UW>(rbq, (uint32_t)(n0 * (K / 2)), (uint32_t)(K / 2), 16, k_lo, K, lbq, lane);
   wait_vmcnt<UW>();  // activations and scales have landed
   __builtin_amdgcn_s_barrier();
   if constexpr (AKIND == 0) {  // dequantise the activation rows once: 8 values per item
@@ -685,23 +707,13 @@ __global__ void __launch_bounds__(512)
   }
 
   const int c = lane & 15, g = lane >> 4;
-  const int rd = c * 64 + ((g ^ ((c >> 2) & 3)) * 16);
   const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
   const uint8_t* arow = lav + c * (2 * K) + 2 * (k_lo + 32 * g);
   v4f acc = v4f{};
 #pragma unroll
   for (int i = 0; i < UW; i++) {
-    switch (UW - 1 - i) {  // weight unit i has landed
-      case 0: wait_vmcnt<0>(); break;
-      case 1: wait_vmcnt<1>(); break;
-      case 2: wait_vmcnt<2>(); break;
-      case 3: wait_vmcnt<3>(); break;
-      case 4: wait_vmcnt<4>(); break;
-      case 5: wait_vmcnt<5>(); break;
-      case 6: wait_vmcnt<6>(); break;
-      default: wait_vmcnt<7>(); break;
-    }
-    const uint4 w = *reinterpret_cast<const uint4*>(lbq + 1024 * i + rd);
+    if ((i & 1) == 0) wait_vmcnt_upto(UW - 2 - i);  // the weight pair of unit i has landed
+    const uint4 w = *reinterpret_cast<const uint4*>(lbq + pair_rd(i, c, g));
     if constexpr (AKIND == 3) {
       // Re-blocked onto the scaled FP4 MFMA with unit scales: the second
       // operand is block-diagonal -- its row c holds activation row c/8's
@@ -895,7 +907,8 @@ struct LdsPlan {
 };
 LdsPlan lds_plan(int64_t K) {
   const int u = (int)((K + 127) / 128);
-  const int uw = (u + kLdsMaxWaves - 1) / kLdsMaxWaves;
+  int uw = (u + kLdsMaxWaves - 1) / kLdsMaxWaves;
+  uw += uw & 1;  // units move in pairs
   return LdsPlan{uw, (u + uw - 1) / uw};
 }
 
@@ -938,8 +951,7 @@ hipError_t launch_few(const void* A, const uint8_t* SFA, const uint8_t* B, const
   case u:                                                                                                  \
     skinny_lds_few<AKIND, u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, gs); \
     break;
-    BSFP4_FEW_CASE(1) BSFP4_FEW_CASE(2) BSFP4_FEW_CASE(3) BSFP4_FEW_CASE(4)
-    BSFP4_FEW_CASE(5) BSFP4_FEW_CASE(6) BSFP4_FEW_CASE(7) BSFP4_FEW_CASE(8)
+    BSFP4_FEW_CASE(2) BSFP4_FEW_CASE(4) BSFP4_FEW_CASE(6) BSFP4_FEW_CASE(8)
 #undef BSFP4_FEW_CASE
     default: return hipErrorInvalidValue;
   }
@@ -953,8 +965,7 @@ hipError_t launch_lds(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, co
   switch (pl.uw) {
 #define BSFP4_LDS_CASE(u) \
   case u: skinny_lds<u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K); break;
-    BSFP4_LDS_CASE(1) BSFP4_LDS_CASE(2) BSFP4_LDS_CASE(3) BSFP4_LDS_CASE(4)
-    BSFP4_LDS_CASE(5) BSFP4_LDS_CASE(6) BSFP4_LDS_CASE(7) BSFP4_LDS_CASE(8)
+    BSFP4_LDS_CASE(2) BSFP4_LDS_CASE(4) BSFP4_LDS_CASE(6) BSFP4_LDS_CASE(8)
 #undef BSFP4_LDS_CASE
     default: return hipErrorInvalidValue;
   }
