@@ -318,18 +318,25 @@ bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_t* scale_c
 // ------------------------------------------------------------------ peak probes
 
 namespace {
-int64_t mfma_flops(int kind) { return (kind == 2 || kind == 3) ? 2LL * 32 * 32 * 64 : 2LL * 32 * 32 * 16; }
+int64_t mfma_flops(int kind) {
+  return (kind == 2 || kind == 3 || kind == 6) ? 2LL * 32 * 32 * 64 : 2LL * 32 * 32 * 16;
+}
+// kinds 6 and 7 rotate four operand pairs: iters is a multiple of 4
+bool probe_args_ok(int kind, int iters) {
+  return kind >= 0 && kind <= 7 && iters > 0 && iters <= (1 << 24) && (kind < 6 || iters % 4 == 0);
+}
 }  // namespace
 
 int64_t bsfp4_probe_mfma_flops(int kind, int iters) {
-  if (kind < 0 || kind > 5 || iters <= 0) return 0;
+  if (!probe_args_ok(kind, iters)) return 0;
   // 8 MFMAs per iteration per wave, 4 waves per workgroup
   return bsfp4::probe_mfma_grid() * 4 * (int64_t)iters * 8 * mfma_flops(kind);
 }
 
 bsfp4_status bsfp4_probe_mfma(int kind, int iters, void* stream) {
-  if (kind < 0 || kind > 5) return fail(BSFP4_ERR_INVALID_ARG, "unknown MFMA probe kind %d", kind);
-  if (iters <= 0 || iters > (1 << 24)) return fail(BSFP4_ERR_SHAPE, "iters must be in [1, 2^24] (got %d)", iters);
+  if (kind < 0 || kind > 7) return fail(BSFP4_ERR_INVALID_ARG, "unknown MFMA probe kind %d", kind);
+  if (!probe_args_ok(kind, iters))
+    return fail(BSFP4_ERR_SHAPE, "iters must be in [1, 2^24] and a multiple of 4 for kinds 6 and 7 (got %d)", iters);
   if (bsfp4_status s = check_device()) return s;
   return launched(bsfp4::launch_probe_mfma(kind, iters, as_stream(stream)), "bsfp4_probe_mfma launch");
 }

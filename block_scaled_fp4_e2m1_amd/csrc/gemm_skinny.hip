@@ -410,27 +410,38 @@ __global__ void __launch_bounds__(512)
 
 // ---------------------------------------------------------------------------
 // LDS-staged single-pass form for NVFP4 activations, M <= 16, K <= 8192: one
-// workgroup per 16 output columns, nw <= 8 waves each owning UW units of 128 K
-// values.  Measured on the GPU, the per-lane register loads of the forms above
-// spend most of their time in the vector memory pipeline (each 16-lane quarter
-// of a load touches 16 rows, and 2-byte scale loads cost as much as code
-// loads), so here every operand reaches LDS through direct-to-LDS DMA:
-//   * scales: the workgroup's 16 weight rows of scales are one contiguous
-//     16 x K/16-byte block in memory (row-major [N, K/16]), likewise the 16
-//     activation rows; wave w copies the w-th KB of each, and one barrier makes
-//     them visible to every wave;
-//   * codes: per unit, one instruction moves 16 rows x 64 bytes (four lanes per
-//     row segment) into [unit][row][64 B]; the 16-byte piece p of row r lands at
-//     position p ^ ((r >> 2) & 3), so the MFMA's 128-bit reads (lane = row) hit
-//     distinct banks;
+// workgroup per 16 output columns, nw <= 15 waves each owning UW units of 128
+// K values (UW = 4 and 14 waves at K = 7168).  Measured on the GPU, the
+// per-lane register loads of the forms above spend most of their time in the
+// vector memory pipeline (each 16-lane quarter of a load touches 16 rows, and
+// 2-byte scale loads cost as much as code loads), so here every operand
+// reaches LDS through direct-to-LDS DMA:
+//   * scales: when a row's scale bytes are a multiple of 16 (K % 256 == 0),
+//     each wave copies the 16 x 64 bytes of its own K range for the weight and
+//     for the activation rows (one instruction each) and needs no other
+//     wave's data, so no barrier precedes the dequantisation: a wave starts as
+//     soon as its own loads land (a workgroup barrier there made every wave
+//     wait for the slowest one's whole issue, measured 10.3 -> 9.3 us at
+//     16 x 4096 x 7168 cold).  Otherwise the workgroup's 16 weight rows of
+//     scales, one contiguous 16 x K/16-byte block in memory (row-major
+//     [N, K/16]), and likewise the 16 activation rows are copied KB by KB by
+//     the waves and one barrier makes them visible to all;
+//   * codes: weight and activation units move in pairs of 8 rows x 128 B (see
+//     below);
 //   * the activations are issued first (L2-resident) and dequantised into
 //     registers while the weight stream is still in flight; then each weight
 //     unit is consumed as soon as its own DMA has landed (s_waitcnt vmcnt);
+//     more, shorter waves (4 units each instead of 8) shorten the dequantise
+//     and MFMA tail of the wave whose loads are served last (9.3 -> 9.0 us);
 //   * partial 16 x 16 tiles are summed in LDS in wave order (deterministic),
 //     multiplied by alpha and rounded once to bf16.
 // Lanes past the problem (rows >= M, K >= K) read zeros; scale bytes past a
 // row's end only ever multiply zero codes.
-constexpr int kLdsMaxWaves = 8;
+constexpr int kLdsMaxWaves = 8;  // waves of the few-row form
+
+// Waves of the M <= 16 LDS form with UW units per wave: as many as fit in the
+// 160 KB of LDS (2 + 2 UW KB per wave), at most 15.
+__host__ __device__ constexpr int lds_waves(int uw) { return 160 / (2 + 2 * uw) < 15 ? 160 / (2 + 2 * uw) : 15; }
 
 // Code units of 128 K values are moved in pairs: one DMA instruction carries 8
 // rows x 128 B (a pair of units of 8 rows: whole cache lines; 16 rows x 64 B
@@ -486,11 +497,11 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 }
 
 template <int UW>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(1024)
     skinny_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
                const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
                int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[(2 + 2 * UW) * kLdsMaxWaves * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[(2 + 2 * UW) * lds_waves(UW) * 1024];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
@@ -505,7 +516,16 @@ __global__ void __launch_bounds__(512)
   const v4u32 rbs = make_rsrc4(SFB, (int64_t)N * kb16);
   const v4u32 raq = make_rsrc4(A, (int64_t)M * (K / 2));
   const v4u32 ras = make_rsrc4(SFA, (int64_t)M * kb16);
-  {
+  const bool own_scales = (kb16 % 16) == 0;  // 16-byte aligned pieces of every row's scale bytes
+  if (own_scales) {
+    // this wave's K range [k_lo, k_lo + 128 UW): 8 UW scale bytes of each of 16 rows, lane = (row, 16-byte piece);
+    // the pieces past the range belong to the next wave and are never read here
+    const int r = lane >> 2, pc = k_lo / 16 + 16 * (lane & 3);
+    buf_lds16(rbs, pc < kb16 ? (uint32_t)((n0 + r) * kb16 + pc) : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsb + wave * 1024)));
+    buf_lds16(ras, (r < M && pc < kb16) ? (uint32_t)(r * kb16 + pc) : kBufOOB, 0,
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsa + wave * 1024)));
+  } else {
     const int off = wave * 1024 + lane * 16;  // byte of the 16 x K/16 scale block
     buf_lds16(rbs, off < 16 * kb16 ? (uint32_t)(n0 * kb16 + off) : kBufOOB, 0,
               (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lsb + wave * 1024)));
@@ -518,9 +538,9 @@ __global__ void __launch_bounds__(512)
   // MFMA lane (c, g): row c, K values 128i + 32g + 8s (s = word of the piece)
   const int c = lane & 15, g = lane >> 4;
   wait_vmcnt<UW>();  // scales and activations have landed; only weight units may be in flight
-  __builtin_amdgcn_s_barrier();
-  const uint8_t* sbrow = lsb + c * kb16 + k_lo / 16 + 2 * g;
-  const uint8_t* sarow = lsa + c * kb16 + k_lo / 16 + 2 * g;
+  if (!own_scales) __builtin_amdgcn_s_barrier();  // the scale block was copied by all waves
+  const uint8_t* sbrow = own_scales ? lsb + wave * 1024 + c * 64 + 2 * g : lsb + c * kb16 + k_lo / 16 + 2 * g;
+  const uint8_t* sarow = own_scales ? lsa + wave * 1024 + c * 64 + 2 * g : lsa + c * kb16 + k_lo / 16 + 2 * g;
   // two E4M3 scale bytes -> two fp16 values (exact): magnitude bits at fp16 bit 7, times 2^8
   auto scales2 = [](uint32_t s) {
     return __builtin_bit_cast(v2h, ((s & 0x7Fu) << 7) | ((s & 0x7F00u) << 15)) *
@@ -916,6 +936,15 @@ LdsPlan lds_plan(int64_t K) {
 // 8 units), M * K a multiple of 256 and operands whose byte offsets fit 31 bits; BSFP4_SKINNY_LDS=0
 // selects the register-load single-pass form instead, BSFP4_SKINNY_SPLIT=1 the
 // split-K form (measurement overrides).
+// Plan of the M <= 16 LDS form: the fewest units per wave (even, <= 6) whose
+// wave count fits lds_waves; {0, 0} if none does.
+LdsPlan lds_plan_m16(int64_t K) {
+  const int u = (int)((K + 127) / 128);
+  for (int uw = 2; uw <= 6; uw += 2)
+    if ((u + uw - 1) / uw <= lds_waves(uw)) return LdsPlan{uw, (u + uw - 1) / uw};
+  return LdsPlan{0, 0};
+}
+
 bool use_lds(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_SKINNY_LDS");
   if (e && e[0] == '0') return false;
@@ -925,8 +954,8 @@ bool use_lds(int64_t M, int64_t N, int64_t K) {
   // the activation scale block (M x K/16 bytes) is copied in whole 16-byte pieces:
   // its length must be a multiple of 16 so that no piece straddles the buffer's end
   if ((M * (K / 16)) % 16 != 0) return false;
-  const LdsPlan pl = lds_plan(K);
-  return pl.nw * 1024 >= K;  // one 1 KB scale piece per wave covers the 16 x K/16 block
+  const LdsPlan pl = lds_plan_m16(K);
+  return pl.uw > 0 && pl.nw * 1024 >= K;  // one 1 KB scale piece per wave covers the 16 x K/16 block
 }
 
 // The few-row form: M <= 4 and otherwise the LDS form's conditions (for bf16
@@ -960,12 +989,12 @@ hipError_t launch_few(const void* A, const uint8_t* SFA, const uint8_t* B, const
 
 hipError_t launch_lds(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                       const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  const LdsPlan pl = lds_plan(K);
+  const LdsPlan pl = lds_plan_m16(K);
   const dim3 grid((unsigned)(N / 16)), block((unsigned)(64 * pl.nw));
   switch (pl.uw) {
 #define BSFP4_LDS_CASE(u) \
   case u: skinny_lds<u><<<grid, block, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K); break;
-    BSFP4_LDS_CASE(2) BSFP4_LDS_CASE(4) BSFP4_LDS_CASE(6) BSFP4_LDS_CASE(8)
+    BSFP4_LDS_CASE(2) BSFP4_LDS_CASE(4) BSFP4_LDS_CASE(6)
 #undef BSFP4_LDS_CASE
     default: return hipErrorInvalidValue;
   }

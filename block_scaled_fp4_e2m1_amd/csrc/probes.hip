@@ -10,8 +10,12 @@
 //                     operands of at most 3 significant bits (as the exactly
 //                     dequantised E2M1 x E4M3 values have few), since the
 //                     sustained MFMA rate of a power-limited part depends on
-//                     how many operand bits toggle.  Four 256-thread
-//                     workgroups per compute unit.
+//                     how many operand bits toggle.  6 and 7 feed operands
+//                     that change from one MFMA to the next, as in a GEMM
+//                     (four A and four B registers, rotated): 6 fp4 with
+//                     random codes, 7 fp16 with random E2M1 x E4M3 products
+//                     (the values the exact NVFP4 path multiplies).  Four
+//                     256-thread workgroups per compute unit.
 //   read_probe        streams a buffer once with 128-bit loads (four in
 //                     flight per lane), keeping a running XOR; nothing is
 //                     stored unless the flag (never set by the library) asks.
@@ -21,13 +25,64 @@
 namespace bsfp4 {
 namespace {
 
+// 32-bit linear congruential step (Numerical Recipes constants) with an
+// xor-shift of the output: operand bits for the changing-operand kinds
+__device__ __forceinline__ uint32_t lcg_next(uint32_t& s) {
+  s = s * 1664525u + 1013904223u;
+  return s ^ (s >> 13);
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(256) mfma_probe(int iters, int flag, float* sink) {
   const int lane = threadIdx.x & 63;
   v16f acc[8];
 #pragma unroll
   for (int j = 0; j < 8; j++) acc[j] = v16f{};
-  if constexpr (KIND <= 1 || KIND >= 4) {
+  if constexpr (KIND >= 6) {
+    // four A and four B operands per lane; MFMA j of step u multiplies A j%4
+    // by B (j/2 + u)%4, so consecutive MFMAs never repeat an operand pair
+    uint32_t st = 0x9e3779b9u * (threadIdx.x + 1) + blockIdx.x * 7919u;
+    if constexpr (KIND == 6) {
+      v8i a[4], b[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          a[j][i] = i < 4 ? (int)lcg_next(st) : 0;
+          b[j][i] = i < 4 ? (int)lcg_next(st) : 0;
+        }
+      for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[((j >> 1) + u) & 3], acc[j], 4, 4,
+                                                                     0, 127, 0, 127);
+      }
+    } else {
+      const float e2[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+      v8h a[4], b[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          // E2M1 value x E4M3 mantissa (1 + m/8) x 2^(0..3) x sign / 8
+          uint32_t r = lcg_next(st);
+          a[j][i] = (_Float16)(e2[r & 7] * (1.0f + 0.125f * ((r >> 3) & 7)) * (float)(1 << ((r >> 6) & 3)) *
+                               (((r >> 9) & 1) ? -0.125f : 0.125f));
+          r = lcg_next(st);
+          b[j][i] = (_Float16)(e2[r & 7] * (1.0f + 0.125f * ((r >> 3) & 7)) * (float)(1 << ((r >> 6) & 3)) *
+                               (((r >> 9) & 1) ? -0.125f : 0.125f));
+        }
+      for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[j & 3], b[((j >> 1) + u) & 3], acc[j], 0, 0, 0);
+      }
+    }
+  } else if constexpr (KIND <= 1 || KIND >= 4) {
     v8h a, b;
     v8bf ab, bb;
 #pragma unroll
@@ -103,7 +158,9 @@ hipError_t launch_probe_mfma(int kind, int iters, hipStream_t stream) {
     case 2: mfma_probe<2><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
     case 3: mfma_probe<3><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
     case 4: mfma_probe<4><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
-    default: mfma_probe<5><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 5: mfma_probe<5><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    case 6: mfma_probe<6><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
+    default: mfma_probe<7><<<grid, 256, 0, stream>>>(iters, 0, nullptr); break;
   }
   return hipGetLastError();
 }

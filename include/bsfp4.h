@@ -431,10 +431,15 @@ BSFP4_API bsfp4_status bsfp4_e2m1_convert(int mode, const void* in, const uint8_
  *   bsfp4_probe_mfma  kind 0 fp16 (v_mfma_f32_32x32x16_f16), 1 bf16, 2 fp8
  *                     E4M3 and 3 fp4 E2M1 (v_mfma_scale_f32_32x32x64_f8f6f4,
  *                     unit E8M0 scales), 4 / 5 fp16 / bf16 with operands of at
- *                     most 3 significant bits: every wave issues `iters` x 8
- *                     independent MFMAs from registers, four waves per SIMD;
- *                     bsfp4_probe_mfma_flops(kind, iters) is the launch's flop
- *                     count (0 for invalid arguments), iters in [1, 2^24]
+ *                     most 3 significant bits, 6 fp4 with random codes and 7
+ *                     fp16 with random E2M1 x E4M3 products, both with
+ *                     operands that change from one MFMA to the next (as in a
+ *                     GEMM; the sustained rate of the power-limited part
+ *                     depends on the operand data): every wave issues
+ *                     `iters` x 8 independent MFMAs from registers, four
+ *                     waves per SIMD; bsfp4_probe_mfma_flops(kind, iters) is
+ *                     the launch's flop count (0 for invalid arguments), iters
+ *                     in [1, 2^24] and a multiple of 4 for kinds 6 and 7
  *   bsfp4_probe_read  reads `bytes` (> 0, % 16 == 0) of device memory at
  *                     `buf` (16-byte aligned) once with 128-bit loads; writes
  *                     nothing

@@ -225,3 +225,23 @@ def test_quantize_gemm_validation(lib):
     assert f(*args(ws=FAKE + 8, ws_bytes=need)) == ALIGN
     assert f(*args(M=0, x=None, D=None)) == OK
     assert lib.nvfp4_quantize_gemm_workspace_size(0, 64, 64) == 0
+
+
+def test_probe_validation(lib):
+    flops = lib.bsfp4_probe_mfma_flops
+    # flops per launch scale with iters; the 64-deep fp8 / fp4 forms do 4x the fp16 work per MFMA
+    assert flops(0, 8) > 0 and flops(0, 16) == 2 * flops(0, 8)
+    assert flops(3, 8) == 4 * flops(0, 8) and flops(6, 8) == flops(3, 8)
+    assert flops(7, 8) == flops(0, 8) and flops(2, 8) == flops(3, 8)
+    for kind, iters in ((-1, 8), (8, 8), (0, 0), (0, (1 << 24) + 1), (6, 6), (7, 2)):
+        assert flops(kind, iters) == 0, (kind, iters)
+    probe = lib.bsfp4_probe_mfma
+    assert probe(8, 16, None) == INVALID
+    assert probe(-1, 16, None) == INVALID
+    assert probe(0, 0, None) == SHAPE
+    assert probe(6, 6, None) == SHAPE and "multiple of 4" in _err(lib)
+    assert probe(7, 1 << 25, None) == SHAPE
+    read = lib.bsfp4_probe_read
+    assert read(FAKE, 0, None) == SHAPE
+    assert read(FAKE, 24, None) == SHAPE
+    assert read(None, 32, None) == INVALID

@@ -183,13 +183,14 @@ def test_nvfp4_gemm_forced_other_tiles(monkeypatch, tile, variant, M, N, K, spli
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (3, 96, 4000 - 4000 % 32), (16, 4096, 7168), (9, 1056, 16384),
                                    (16, 288, 32), (5, 160, 1088), (16, 128, 8192), (2, 96, 8224),
                                    (11, 4096, 4064), (16, 64, 96), (7, 1056, 2304), (1, 32, 256),
-                                   (4, 4096, 4032), (8, 288, 1056)])
+                                   (4, 4096, 4032), (8, 288, 1056), (13, 160, 3840)])
 @pytest.mark.parametrize("form", ["few", "lds", "onepass", "split"])
 def test_nvfp4_gemm_small_m_forms(monkeypatch, form, M, N, K):
     """The small-M forms (few-row and 16-row LDS-staged, register single pass,
     split-K + reduce) on ragged shapes: K tails inside a 128-value unit, K up to
-    the LDS forms' 8192 limit and just past it, several wave counts (shapes
-    outside a form's conditions take the next form)."""
+    the LDS forms' 8192 limit and just past it, several wave counts and units
+    per wave, the 16-row form's per-wave scale copies (K % 256 == 0) and its
+    whole-block copy (shapes outside a form's conditions take the next form)."""
     if form != "few":
         monkeypatch.setenv("BSFP4_SKINNY_FEW", "0")
     if form == "onepass":
