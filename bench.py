@@ -70,6 +70,9 @@ def parse():
     p.add_argument("--no-headline", action="store_true", help="skip the headline GEMM")
     p.add_argument("--trace-summary", default="",
                    help="summarise a rocprofv3 kernel_trace.csv (per-kernel duration percentiles) and exit")
+    p.add_argument("--counter-derived", nargs=2, metavar=("CSVS", "KERNEL"), default=None,
+                   help="print derived rates (clock, MFMA pipe busy, ...) of KERNEL from comma-joined "
+                        "rocprofv3 SQ counter CSVs of one command, and exit")
     p.add_argument("--counter-summary", default="",
                    help="summarise a rocprofv3 counter_collection.csv (median per dispatch per kernel and "
                         "grid, FETCH_SIZE / WRITE_SIZE scaled by the 256 MiB copy) and exit")
@@ -107,6 +110,59 @@ def counter_summary(path: str) -> str:
         lines.append("")
         lines.append("Copy calibration factors (bytes per counter KiB / 1024): " +
                      ", ".join(f"{k} {v:.4f}" for k, v in sorted(factor.items())))
+    return "\n".join(lines)
+
+
+def counter_derived(paths: str, kernel: str, cus: int = 256) -> str:
+    """Per-dispatch rates of one kernel from rocprofv3 SQ counter CSVs (a
+    comma-joined list of passes of the same command, matched by dispatch
+    order), medians over dispatches:
+      * effective clock = SQ_BUSY_CU_CYCLES / CUs / kernel duration (the
+        counter sums the busy cycles of every CU);
+      * MFMA pipe busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x CUs) over the
+        per-CU busy cycles;
+      * VALU instructions per MFMA; LDS busy = SQ_LDS_IDX_ACTIVE per CU over
+        the busy cycles; TA address / command FIFO full likewise; waves'
+        waiting share = SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles)."""
+    import csv
+    per = []
+    for path in paths.split(","):
+        by = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                d = by.setdefault(int(r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.append([by[k] for k in sorted(by)])
+    n = min(len(p) for p in per)
+    rows = []
+    for i in range(n):
+        d = {}
+        for p in per:
+            d.update(p[i])
+        rows.append(d)
+    out = {"dispatches": n, "median duration us": float(np.median([d["dur_us"] for d in rows]))}
+
+    def add(name, fn):
+        try:
+            out[name] = float(np.median([fn(d) for d in rows]))
+        except KeyError:
+            pass
+    add("effective clock GHz", lambda d: d["SQ_BUSY_CU_CYCLES"] / cus / (d["dur_us"] * 1e3))
+    add("MFMA pipe busy (fraction of CU busy cycles)",
+        lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cus) / (d["SQ_BUSY_CU_CYCLES"] / cus))
+    add("VALU instructions per MFMA", lambda d: d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"])
+    add("LDS instructions per MFMA", lambda d: d["SQ_INSTS_LDS"] / d["SQ_INSTS_MFMA"])
+    busy = float(np.median([d["SQ_BUSY_CU_CYCLES"] / cus for d in rows])) if "SQ_BUSY_CU_CYCLES" in rows[0] else None
+    if busy:
+        add("LDS busy (fraction)", lambda d: d["SQ_LDS_IDX_ACTIVE"] / cus / busy)
+        add("TA address FIFO full (fraction)", lambda d: d["SQ_VMEM_TA_ADDR_FIFO_FULL"] / cus / busy)
+        add("TA command FIFO full (fraction)", lambda d: d["SQ_VMEM_TA_CMD_FIFO_FULL"] / cus / busy)
+    add("waves' waiting share", lambda d: d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"])
+    lines = ["| quantity | median |", "|---|---|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in out.items()]
     return "\n".join(lines)
 
 
@@ -252,6 +308,9 @@ def main():
     args = parse()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.counter_derived:
+        print(counter_derived(args.counter_derived[0], args.counter_derived[1]))
         return
     if args.counter_summary:
         print(counter_summary(args.counter_summary))
