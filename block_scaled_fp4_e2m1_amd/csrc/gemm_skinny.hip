@@ -474,28 +474,6 @@ __device__ __forceinline__ void issue_pairs(v4u32 rsrc, uint32_t row0_off, uint3
   }
 }
 
-// s_waitcnt vmcnt(n) for a run-time n that is a compile-time constant after
-// unrolling (n <= 14)
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    default: wait_vmcnt<14>(); break;
-  }
-}
-
 template <int UW>
 __global__ void __launch_bounds__(1024)
     skinny_lds(const uint8_t* __restrict__ A, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,

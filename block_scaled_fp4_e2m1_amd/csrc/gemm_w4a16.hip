@@ -249,20 +249,24 @@ __global__ void __launch_bounds__(kNT, 1)
 // four K quarters are summed in LDS at the end, in quarter order.  The weight
 // stream is what costs at these shapes; the activations (at most 64 rows) stay
 // L2-resident and are re-read once per 128-column block.
-//   * the weight codes of the workgroup's whole K range (128 rows x K/S/2 bytes,
-//     rows padded by 16 bytes) are copied into LDS first, each row by
-//     consecutive lanes and loads so that HBM sees long row segments, and so
-//     are the range's weight scales (8 bytes per row and stage);
-//   * the activations follow in stages of 128 K values through a 4-slot ring
-//     (64 rows x 256 bytes of bf16, the 16-byte chunk x of row r at position
-//     x ^ (r & 15), conflict-free fragment reads), two loads per wave and stage;
+//   * the range's weight scales (8 bytes per row and stage) are copied into
+//     LDS first; then the weight codes of the whole range, stage by stage
+//     (one load per wave and stage: 16 rows x 64 bytes into [stage][row][64 B],
+//     the 16-byte piece p of row r at position p ^ ((r >> 2) & 3), so the
+//     MFMA's 4-byte reads are conflict-free), with the activations of the
+//     first three stages in between, so each stage waits only for its own
+//     loads and the MFMAs follow the weight stream instead of starting after
+//     all of it has landed (measured 17.7 -> 16.6 us at 64 x 4096 x 7168 cold);
+//   * the activations go through a 4-slot ring of 128-value stages (64 rows x
+//     256 bytes of bf16, the 16-byte chunk x of row r at position x ^ (r & 15),
+//     conflict-free fragment reads), two loads per wave and stage;
 //   * K ranges of one column block are summed by splitk_reduce in range order.
 constexpr int kRBM = 64, kRBN = 128, kRNT = 512;
 constexpr int kRSK = 128;                   // K values per stage
 constexpr int kRA = kRBM * kRSK * 2;         // 16 KB of bf16 activations per stage
 constexpr int kRRing = 4;                   // activation stages in LDS: 3 in flight ahead of the one in use
 constexpr int kRMaxStages = 8;              // stages per K range
-constexpr int kRQ = kRBN * (4 * kRMaxStages + 1) * 16;  // weight codes of the range, padded rows
+constexpr int kRQ = kRMaxStages * kRBN * 64;  // weight codes of the range: [stage][row][64 B]
 constexpr int kRScales = kRBN * kRMaxStages * 8;
 constexpr int kRSmem = kRRing * kRA + kRQ + kRScales;
 
@@ -279,30 +283,32 @@ __global__ void __launch_bounds__(kRNT)
   const int sb = (int)((int64_t)total * split / splits);
   const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
   const int k_lo = sb * kRSK;
-  uint8_t* const sq = smem + kRRing * kRA;  // [128 rows][(4 nst + 1) 16-byte pieces]
+  uint8_t* const sq = smem + kRRing * kRA;  // [stage][128 rows][64 B], pieces swizzled
   uint8_t* const sc = sq + kRQ;             // [128 rows][8 nst bytes]
-  const int qpitch = (4 * nst + 1) * 16, pitch = 8 * nst;
+  const int pitch = 8 * nst;
   const v4u32 ra = make_rsrc4(A, (int64_t)M * K * 2);
   const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
   const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
   auto lds_u = [](const void* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(p)); };
 
-  // ---- weight codes of the range: LDS slot P (16 bytes) = row P / (4 nst + 1), piece P % (4 nst + 1)
-  {
-    const int per_row = 4 * nst + 1, slots = kRBN * per_row;
-    for (int i = wave; i * 64 < slots; i += kRNT / 64) {
-      const int p = 64 * i + lane, row = p / per_row, piece = p - row * per_row;
-      const bool ok = row < kRBN && piece < 4 * nst && n0 + row < N;
-      buf_lds16(rq, ok ? (uint32_t)((n0 + row) * (K / 2) + k_lo / 2 + 16 * piece) : kBufOOB, 0,
-                lds_u(sq + 1024 * i));
-    }
-  }
-  // ---- the range's weight scales: 4 * nst loads of 64 dwords (2 dwords per row and stage)
+  // ---- the range's weight scales first: 4 * nst loads of 64 dwords (2 dwords per row and stage)
+  int n_sc = 0;  // this wave's scale loads
   for (int i = wave; i < 4 * nst; i += kRNT / 64) {
     const int d = 64 * i + lane, row = d / (2 * nst), word = d - row * (2 * nst);
     const uint32_t off = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
     buf_lds4(rs, off, 0, lds_u(sc + 256 * i));
+    n_sc++;
   }
+  // ---- weight codes, one load per wave and stage: rows 16 wave + lane / 4, logical piece
+  // (lane & 3) ^ ((row >> 2) & 3) of the stage's 64 bytes at LDS position lane & 3
+  const int wrow = 16 * wave + (lane >> 2);
+  const uint32_t vw = n0 + wrow < N
+                          ? (uint32_t)((n0 + wrow) * (K / 2) + k_lo / 2 + 16 * ((lane & 3) ^ ((wrow >> 2) & 3)))
+                          : kBufOOB;
+  auto issue_w = [&](int st) {
+    buf_lds16(rq, vw, (uint32_t)__builtin_amdgcn_readfirstlane(st * 64),
+              lds_u(sq + st * (kRBN * 64) + wave * 1024));
+  };
   // ---- activation ring (the stage's K offset goes in the SGPR offset)
   uint32_t va[2];
 #pragma unroll
@@ -317,7 +323,14 @@ __global__ void __launch_bounds__(kRNT)
     buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
     buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
   };
-  for (int st = 0; st < kRRing - 1 && st < nst; st++) issue(st);
+  // issue order: scales, then W(0) A(0) W(1) A(1) W(2) A(2), then W(3) .. W(nst - 1); the loop
+  // issues A(s + 3) at stage s.  Loads complete in order, so stage s waits for its own W and A.
+  for (int st = 0; st < nst; st++) {
+    issue_w(st);
+    if (st < kRRing - 1) issue(st);
+  }
+  const int first3 = nst < kRRing - 1 ? nst : kRRing - 1;
+  const int prologue = n_sc + 3 * first3 + (nst - first3);  // loads issued before the loop
 
   // wave = (column half h: 64 columns, K quarter q of every stage: 32 values);
   // lane (c, g) of the 16x16x32 MFMAs: weight row / activation row c, K 8g..8g+7
@@ -328,13 +341,12 @@ __global__ void __launch_bounds__(kRNT)
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
+  static_assert(kRRing == 4, "three activation stages issued ahead");
   for (int s = 0; s < nst; s++) {
-    // everything issued before activation stage s (weights, scales) has landed
-    const int ahead = nst - 1 - s < kRRing - 2 ? nst - 1 - s : kRRing - 2;  // later stages in flight
-    static_assert(kRRing - 2 == 2, "wait counts below");
-    if (ahead >= 2) wait_vmcnt<4>();  // two loads per stage
-    else if (ahead == 1) wait_vmcnt<2>();
-    else wait_vmcnt<0>();
+    // this wave's loads up to W(s) and A(s) have landed (index of A(s)'s last load in issue order)
+    const int issued = prologue + 2 * min(s, nst > kRRing - 1 ? nst - (kRRing - 1) : 0);
+    const int last = s < kRRing - 1 ? n_sc + 3 * s + 2 : prologue + 2 * (s - (kRRing - 1)) + 1;
+    wait_vmcnt_upto(issued - 1 - last);
     __builtin_amdgcn_s_barrier();  // stage s visible everywhere; every wave is past stage s-1
     if (s + kRRing - 1 < nst) issue(s + kRRing - 1);
     const uint8_t* sa = smem + (s % kRRing) * kRA;
@@ -348,7 +360,8 @@ __global__ void __launch_bounds__(kRNT)
     for (int j = 0; j < 4; j++) {
       const int col = 64 * h + 16 * j + c;
       // K values 32q + 8g .. +7 of the stage: code word 4q + g, scale byte 2q + g/2
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(sq + col * qpitch + 64 * s + q * 16 + 4 * g);
+      const uint32_t word =
+          *reinterpret_cast<const uint32_t*>(sq + s * (kRBN * 64) + col * 64 + ((q ^ ((col >> 2) & 3)) * 16) + 4 * g);
       const uint32_t sb = sc[col * pitch + 8 * s + 2 * q + (g >> 1)];
       const v8bf fb = dq8_bf16(word, e4m3_to_f32(sb));
 #pragma unroll
