@@ -250,13 +250,17 @@ __global__ void __launch_bounds__(kNT, 1)
 // stream is what costs at these shapes; the activations (at most 64 rows) stay
 // L2-resident and are re-read once per 128-column block.
 //   * the range's weight scales (8 bytes per row and stage) are copied into
-//     LDS first; then the weight codes of the whole range, stage by stage
-//     (one load per wave and stage: 16 rows x 64 bytes into [stage][row][64 B],
-//     the 16-byte piece p of row r at position p ^ ((r >> 2) & 3), so the
-//     MFMA's 4-byte reads are conflict-free), with the activations of the
-//     first three stages in between, so each stage waits only for its own
-//     loads and the MFMAs follow the weight stream instead of starting after
-//     all of it has landed (measured 17.7 -> 16.6 us at 64 x 4096 x 7168 cold);
+//     LDS first; then the weight codes and the activations stage by stage,
+//     three stages ahead of the one in use: per wave and stage one load of
+//     weight codes (16 rows x 64 bytes into [stage][row][64 B], the 16-byte
+//     piece p of row r at position p ^ ((r >> 2) & 3), so the MFMA's 4-byte
+//     reads are conflict-free) and two of activations, so each stage waits
+//     only for its own loads and the MFMAs follow the stream.  Measured at
+//     64 x 4096 x 7168 cold (both kernels, events): weights of the whole
+//     range issued before the first stage 22.7 us, 5 / 4 / 3 stages ahead
+//     22.4 / 21.7 / 21.4 us (the first of these is 16.6 us of this kernel
+//     in a rocprofv3 trace, against 17.7 us when the range was copied in
+//     long row segments ahead of everything);
 //   * the activations go through a 4-slot ring of 128-value stages (64 rows x
 //     256 bytes of bf16, the 16-byte chunk x of row r at position x ^ (r & 15),
 //     conflict-free fragment reads), two loads per wave and stage;
@@ -323,14 +327,15 @@ __global__ void __launch_bounds__(kRNT)
     buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
     buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
   };
-  // issue order: scales, then W(0) A(0) W(1) A(1) W(2) A(2), then W(3) .. W(nst - 1); the loop
-  // issues A(s + 3) at stage s.  Loads complete in order, so stage s waits for its own W and A.
-  for (int st = 0; st < nst; st++) {
+  // issue order: scales, then W(0) A(0) W(1) A(1) W(2) A(2); the loop issues W(s + 3) A(s + 3)
+  // at stage s (three loads a stage).  Loads complete in order, so stage s waits for its own A.
+  constexpr int kAhead = kRRing - 1;
+  const int first = min(nst, kAhead);
+  for (int st = 0; st < first; st++) {
     issue_w(st);
-    if (st < kRRing - 1) issue(st);
+    issue(st);
   }
-  const int first3 = nst < kRRing - 1 ? nst : kRRing - 1;
-  const int prologue = n_sc + 3 * first3 + (nst - first3);  // loads issued before the loop
+  const int prologue = n_sc + 3 * first;  // loads issued before the loop
 
   // wave = (column half h: 64 columns, K quarter q of every stage: 32 values);
   // lane (c, g) of the 16x16x32 MFMAs: weight row / activation row c, K 8g..8g+7
@@ -341,14 +346,17 @@ __global__ void __launch_bounds__(kRNT)
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
-  static_assert(kRRing == 4, "three activation stages issued ahead");
   for (int s = 0; s < nst; s++) {
     // this wave's loads up to W(s) and A(s) have landed (index of A(s)'s last load in issue order)
-    const int issued = prologue + 2 * min(s, nst > kRRing - 1 ? nst - (kRRing - 1) : 0);
-    const int last = s < kRRing - 1 ? n_sc + 3 * s + 2 : prologue + 2 * (s - (kRRing - 1)) + 1;
+    // this wave's loads issued so far, and the index of A(s)'s second load in that order
+    const int issued = prologue + 3 * min(s, max(nst - kAhead, 0));
+    const int last = s < kAhead ? n_sc + 3 * s + 2 : prologue + 3 * (s - kAhead) + 2;
     wait_vmcnt_upto(issued - 1 - last);
     __builtin_amdgcn_s_barrier();  // stage s visible everywhere; every wave is past stage s-1
-    if (s + kRRing - 1 < nst) issue(s + kRRing - 1);
+    if (s + kAhead < nst) {
+      issue_w(s + kAhead);
+      issue(s + kAhead);
+    }
     const uint8_t* sa = smem + (s % kRRing) * kRA;
     v8bf fa[4];
 #pragma unroll
