@@ -62,4 +62,25 @@ __device__ __forceinline__ v8bf dq8_bf16(uint32_t word, float s) {
   return __builtin_bit_cast(v8bf, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// E4M3 byte -> fp16 (exact): the 7 magnitude bits at fp16 bit 7 give the value
+// times 2^-8 for normal and subnormal codes; multiplying by 256 restores it.
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
+  const uint16_t bits = (uint16_t)((c & 0x7Fu) << 7);
+  return __builtin_bit_cast(_Float16, bits) * (_Float16)256.0f;
+}
+
+// Eight E2M1 values (one 32-bit word, first value in the low nibble) times the
+// fp16 block scale `s` -> eight fp16 values (exact: at most 6 significant bits,
+// magnitudes in [2^-10, 2688]).
+__device__ __forceinline__ v8h dq8_f16(uint32_t word, _Float16 s) {
+  const v2h ss = {s, s};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * ss;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * ss;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * ss;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * ss;
+  const v4h lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const v4h hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 }  // namespace bsfp4

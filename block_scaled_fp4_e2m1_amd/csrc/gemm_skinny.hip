@@ -70,27 +70,6 @@ __device__ __forceinline__ uint32_t byte_of(const uint4& v, int i) {
   return (w >> (8 * (i & 3))) & 0xFFu;
 }
 
-// E4M3 byte -> fp16 (exact): the 7 magnitude bits at fp16 bit 7 give the value
-// times 2^-8 for normal and subnormal codes; multiplying by 256 restores it.
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
-  const uint16_t bits = (uint16_t)((c & 0x7Fu) << 7);
-  return __builtin_bit_cast(_Float16, bits) * (_Float16)256.0f;
-}
-
-
-__device__ __forceinline__ v8h dq8_f16(uint32_t word, _Float16 s) {
-  const v2h ss = {s, s};
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * ss;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * ss;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * ss;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * ss;
-  const v4h lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
-  const v4h hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Eight E2M1 values times an f32 scale -> eight bf16 (exact: <= 6 significant bits).
-
 // AKIND 0: activations are NVFP4 (codes + E4M3 scales), fp16 MFMA.
 // AKIND 1: activations are bf16, bf16 MFMA.
 template <int AKIND, int MT, bool kAligned>
@@ -987,7 +966,8 @@ bool use_onepass(int64_t M, int64_t N, int64_t K) {
   return M <= 16 && onepass_nl(K) > 0 && N * (K / 2) < ((int64_t)1 << 31);
 }
 
-// Rows 33..64: the split form with four M tiles for bf16 activations (the
+// Rows 33..64 where the 64-row kernel does not apply (K % 128 != 0, or
+// switched off): the split form with four M tiles for bf16 activations (the
 // single-tile kernel would load them just in time); NVFP4 activations keep the
 // per-wave kernel unless BSFP4_SKINNY_MT4=1.
 bool split_mt4(int akind) {
@@ -1028,6 +1008,9 @@ hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, cons
 hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                                const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                                hipStream_t stream) {
+  // the caller's workspace holds skinny_workspace(M, N, K, true) bytes
+  if (nvfp4_rows64_ok(M, N, K))
+    return launch_nvfp4_rows64(A, SFA, B, SFB, alpha, D, M, N, K, part, w4a16_rows64_workspace(M, N, K), stream);
   return launch_kind<0>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
 }
 
@@ -1048,6 +1031,7 @@ hipError_t launch_nvfp4_fused_quant_gemm(const uint16_t* x, const float* gs, con
 
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
   if (M <= 0 || M > 64 || N * (K / 2) >= ((int64_t)1 << 31)) return 0;
+  if (fp4_activations && nvfp4_rows64_ok(M, N, K)) return w4a16_rows64_workspace(M, N, K);
   if (use_few(fp4_activations ? 0 : 1, M, N, K)) return 0;
   if (fp4_activations && (use_lds(M, N, K) || use_onepass(M, N, K))) return 0;
   if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;

@@ -240,44 +240,60 @@ __global__ void __launch_bounds__(kNT, 1)
 
 
 // ---------------------------------------------------------------------------
-// W4A16 for 33 <= M <= 64 (fewer rows use the kernels of gemm_skinny.hip):
-// one workgroup = all 64 rows x 128 output columns x one K
-// range, 8 waves = 2 column halves x 4 K quarters of every stage: a wave owns
-// 64 columns x 64 rows (16 v_mfma_f32_16x16x32_bf16 tiles) for 32 of the
-// stage's 128 K values, so every weight value is dequantised exactly once per
-// workgroup and each activation fragment read from LDS feeds four MFMAs; the
-// four K quarters are summed in LDS at the end, in quarter order.  The weight
-// stream is what costs at these shapes; the activations (at most 64 rows) stay
-// L2-resident and are re-read once per 128-column block.
-//   * the range's weight scales (8 bytes per row and stage) are copied into
-//     LDS first; then the weight codes and the activations stage by stage,
-//     three stages ahead of the one in use: per wave and stage one load of
-//     weight codes (16 rows x 64 bytes into [stage][row][64 B], the 16-byte
-//     piece p of row r at position p ^ ((r >> 2) & 3), so the MFMA's 4-byte
-//     reads are conflict-free) and two of activations, so each stage waits
-//     only for its own loads and the MFMAs follow the stream.  Measured at
-//     64 x 4096 x 7168 cold (both kernels, events): weights of the whole
-//     range issued before the first stage 22.7 us, 5 / 4 / 3 stages ahead
-//     22.4 / 21.7 / 21.4 us (the first of these is 16.6 us of this kernel
-//     in a rocprofv3 trace, against 17.7 us when the range was copied in
-//     long row segments ahead of everything);
-//   * the activations go through a 4-slot ring of 128-value stages (64 rows x
-//     256 bytes of bf16, the 16-byte chunk x of row r at position x ^ (r & 15),
+// 64-row GEMM for 17 <= M <= 64 (fewer rows use the kernels of
+// gemm_skinny.hip), W4A16 (AKIND 1: bf16 activations, bf16 MFMA) or NVFP4 W4A4
+// (AKIND 0: NVFP4 activations dequantised to fp16, fp16 MFMA; E2M1 x E4M3
+// values are exact in either type): one workgroup = all 64 rows x 128 output
+// columns x one K range, 8 waves = 2 column halves x 4 K quarters of every
+// stage: a wave owns 64 columns x 64 rows (16 v_mfma_f32_16x16x32 tiles) for 32
+// of the stage's 128 K values, so every weight value is dequantised exactly
+// once per workgroup and each activation fragment read from LDS feeds four
+// MFMAs; the four K quarters are summed in LDS at the end, in quarter order.
+// The weight stream is what costs at these shapes; the activations (at most 64
+// rows) stay L2-resident and are re-read once per 128-column block.
+//   * the range's scales (8 bytes per row and stage; weights, and for NVFP4
+//     the activation rows too) are copied into LDS first; then the weight
+//     codes and the activations stage by stage, three stages ahead of the one
+//     in use: per wave and stage one load of weight codes (16 rows x 64 bytes
+//     into [stage][row][64 B], the 16-byte piece p of row r at position
+//     p ^ ((r >> 2) & 3), so the MFMA's 4-byte reads are conflict-free) and
+//     the stage's activations, so each stage waits only for its own loads and
+//     the MFMAs follow the stream.  Measured for W4A16 at 64 x 4096 x 7168
+//     cold (both kernels, events): weights of the whole range issued before
+//     the first stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us
+//     (the first of these is 16.6 us of this kernel in a rocprofv3 trace,
+//     against 17.7 us when the range was copied in long row segments ahead of
+//     everything);
+//   * bf16 activations go through a 4-slot ring of 128-value stages (64 rows x
+//     256 bytes, the 16-byte chunk x of row r at position x ^ (r & 15),
 //     conflict-free fragment reads), two loads per wave and stage;
+//   * NVFP4 activations: the stage's 64 rows x 64 code bytes go through a
+//     4-slot ring (one load each for waves 0-3) and are dequantised once per
+//     workgroup, one stage ahead of the MFMAs, into a 2-slot fp16 buffer laid
+//     out like the bf16 ring (each thread one 16-value block: two code words,
+//     one scale byte), so stage s waits for its weights and for the codes of
+//     stage s + 1;
 //   * K ranges of one column block are summed by splitk_reduce in range order.
 constexpr int kRBM = 64, kRBN = 128, kRNT = 512;
 constexpr int kRSK = 128;                   // K values per stage
-constexpr int kRA = kRBM * kRSK * 2;         // 16 KB of bf16 activations per stage
+constexpr int kRA = kRBM * kRSK * 2;         // 16 KB of bf16 / fp16 activations per stage
 constexpr int kRRing = 4;                   // activation stages in LDS: 3 in flight ahead of the one in use
 constexpr int kRMaxStages = 8;              // stages per K range
 constexpr int kRQ = kRMaxStages * kRBN * 64;  // weight codes of the range: [stage][row][64 B]
 constexpr int kRScales = kRBN * kRMaxStages * 8;
 constexpr int kRSmem = kRRing * kRA + kRQ + kRScales;
+// NVFP4 activations, inside the first kRRing * kRA bytes: 2 fp16 stages, the
+// 4-slot code ring (64 rows x 64 B each) and the range's activation scales
+constexpr int kRAq = kRBM * 64;
+constexpr int kRAScales = kRBM * kRMaxStages * 8;
+static_assert(2 * kRA + kRRing * kRAq + kRAScales <= kRRing * kRA, "NVFP4 activation buffers fit");
 
+template <int AKIND>
 __global__ void __launch_bounds__(kRNT)
-    w4a16_rows64(const uint16_t* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ SFB,
-                 const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D, int M, int N, int K, int splits,
-                 float* __restrict__ part) {
+    rows64_gemm(const void* __restrict__ Aptr, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
+                const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
+                int M, int N, int K, int splits, float* __restrict__ part) {
+  constexpr bool kFp4A = AKIND == 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRSmem];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -289,18 +305,29 @@ __global__ void __launch_bounds__(kRNT)
   const int k_lo = sb * kRSK;
   uint8_t* const sq = smem + kRRing * kRA;  // [stage][128 rows][64 B], pieces swizzled
   uint8_t* const sc = sq + kRQ;             // [128 rows][8 nst bytes]
+  uint8_t* const saq = smem + 2 * kRA;      // NVFP4: [slot][64 rows][64 B] activation codes
+  uint8_t* const sas = saq + kRRing * kRAq;  // NVFP4: [64 rows][8 nst bytes] activation scales
   const int pitch = 8 * nst;
-  const v4u32 ra = make_rsrc4(A, (int64_t)M * K * 2);
+  const v4u32 ra = make_rsrc4(Aptr, kFp4A ? (int64_t)M * (K / 2) : (int64_t)M * K * 2);
   const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
   const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
   auto lds_u = [](const void* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(p)); };
 
-  // ---- the range's weight scales first: 4 * nst loads of 64 dwords (2 dwords per row and stage)
+  // ---- the range's scales first, 64 dwords per load (2 dwords per row and
+  // stage): 4 nst loads of weight scales, then (NVFP4) 2 nst of activation scales
   int n_sc = 0;  // this wave's scale loads
-  for (int i = wave; i < 4 * nst; i += kRNT / 64) {
-    const int d = 64 * i + lane, row = d / (2 * nst), word = d - row * (2 * nst);
-    const uint32_t off = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
-    buf_lds4(rs, off, 0, lds_u(sc + 256 * i));
+  const int sc_loads = (kFp4A ? 6 : 4) * nst;
+  for (int i = wave; i < sc_loads; i += kRNT / 64) {
+    if (i < 4 * nst) {
+      const int d = 64 * i + lane, row = d / (2 * nst), word = d - row * (2 * nst);
+      const uint32_t off = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
+      buf_lds4(rs, off, 0, lds_u(sc + 256 * i));
+    } else {
+      const v4u32 ras = make_rsrc4(SFA, (int64_t)M * (K / 16));
+      const int d = 64 * (i - 4 * nst) + lane, row = d / (2 * nst), word = d - row * (2 * nst);
+      const uint32_t off = row < M ? (uint32_t)(row * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
+      buf_lds4(ras, off, 0, lds_u(sas + 256 * (i - 4 * nst)));
+    }
     n_sc++;
   }
   // ---- weight codes, one load per wave and stage: rows 16 wave + lane / 4, logical piece
@@ -313,29 +340,61 @@ __global__ void __launch_bounds__(kRNT)
     buf_lds16(rq, vw, (uint32_t)__builtin_amdgcn_readfirstlane(st * 64),
               lds_u(sq + st * (kRBN * 64) + wave * 1024));
   };
-  // ---- activation ring (the stage's K offset goes in the SGPR offset)
+  // ---- activations (the stage's K offset goes in the SGPR offset)
   uint32_t va[2];
+  if constexpr (kFp4A) {
+    // waves 0-3: rows 16 wave + lane / 4, 16-byte piece lane & 3 of the stage's 64 code bytes
+    const int r = 16 * wave + (lane >> 2);
+    va[0] = r < M ? (uint32_t)(r * (K / 2) + k_lo / 2 + 16 * (lane & 3)) : kBufOOB;
+    va[1] = kBufOOB;
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int r = 4 * (2 * wave + j) + (lane >> 4);
-    const int x = (lane & 15) ^ (r & 15);  // global chunk landing at position lane & 15
-    va[j] = r < M ? (uint32_t)(r * (K * 2) + x * 16) : kBufOOB;
+    for (int j = 0; j < 2; j++) {
+      const int r = 4 * (2 * wave + j) + (lane >> 4);
+      const int x = (lane & 15) ^ (r & 15);  // global chunk landing at position lane & 15
+      va[j] = r < M ? (uint32_t)(r * (K * 2) + x * 16) : kBufOOB;
+    }
   }
+  // loads per stage of this wave, issued in this order: NVFP4 A (waves 0-3) then W; bf16 W then A, A
+  const int per_stage = kFp4A ? (wave < 4 ? 2 : 1) : 3;
   auto issue = [&](int st) {
-    uint8_t* base = smem + (st % kRRing) * kRA;
-    const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((k_lo + st * kRSK) * 2);
-    buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
-    buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
+    if constexpr (kFp4A) {
+      if (wave < 4)
+        buf_lds16(ra, va[0], (uint32_t)__builtin_amdgcn_readfirstlane(st * 64),
+                  lds_u(saq + (st % kRRing) * kRAq + wave * 1024));
+      issue_w(st);
+    } else {
+      issue_w(st);
+      uint8_t* base = smem + (st % kRRing) * kRA;
+      const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((k_lo + st * kRSK) * 2);
+      buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
+      buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
+    }
   };
-  // issue order: scales, then W(0) A(0) W(1) A(1) W(2) A(2); the loop issues W(s + 3) A(s + 3)
-  // at stage s (three loads a stage).  Loads complete in order, so stage s waits for its own A.
+  // NVFP4: dequantise stage st's activation codes into fp16 slot st % 2; thread
+  // = (row tid / 8, 16-value block tid % 8), chunks 2b and 2b + 1 of the row
+  auto dequant_a = [&](int st) {
+    const int r = tid >> 3, b = tid & 7;
+    const uint2 w = *reinterpret_cast<const uint2*>(saq + (st % kRRing) * kRAq + r * 64 + 8 * b);
+    const _Float16 s = e4m3_to_f16(sas[r * pitch + 8 * st + b]);
+    uint8_t* row = smem + (st & 1) * kRA + r * 256;
+    *reinterpret_cast<v8h*>(row + (((2 * b) ^ (r & 15)) * 16)) = dq8_f16(w.x, s);
+    *reinterpret_cast<v8h*>(row + (((2 * b + 1) ^ (r & 15)) * 16)) = dq8_f16(w.y, s);
+  };
+  // Load st is the group of per_stage loads at n_sc + per_stage * st in this
+  // wave's issue order (three stages before the loop, one more per stage).
+  // Loads complete in order; waiting for "issued - 1 - index" outstanding
+  // means the load at that index has landed.
   constexpr int kAhead = kRRing - 1;
   const int first = min(nst, kAhead);
-  for (int st = 0; st < first; st++) {
-    issue_w(st);
-    issue(st);
+  for (int st = 0; st < first; st++) issue(st);
+  auto issued_before = [&](int s) { return n_sc + per_stage * min(nst, s + kAhead); };
+  if constexpr (kFp4A) {
+    // scales and the codes of stage 0 (the first load of a waves-0-3 group)
+    wait_vmcnt_upto(issued_before(0) - 1 - (wave < 4 ? n_sc : n_sc - 1));
+    __builtin_amdgcn_s_barrier();
+    dequant_a(0);
   }
-  const int prologue = n_sc + 3 * first;  // loads issued before the loop
 
   // wave = (column half h: 64 columns, K quarter q of every stage: 32 values);
   // lane (c, g) of the 16x16x32 MFMAs: weight row / activation row c, K 8g..8g+7
@@ -347,22 +406,28 @@ __global__ void __launch_bounds__(kRNT)
 #pragma unroll
     for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
   for (int s = 0; s < nst; s++) {
-    // this wave's loads up to W(s) and A(s) have landed (index of A(s)'s last load in issue order)
-    // this wave's loads issued so far, and the index of A(s)'s second load in that order
-    const int issued = prologue + 3 * min(s, max(nst - kAhead, 0));
-    const int last = s < kAhead ? n_sc + 3 * s + 2 : prologue + 3 * (s - kAhead) + 2;
-    wait_vmcnt_upto(issued - 1 - last);
+    // bf16: this wave's group of stage s (its last load); NVFP4: the weights
+    // of stage s (last load of group s) and the codes of stage s + 1 (first
+    // load of group s + 1, waves 0-3)
+    int last = n_sc + per_stage * s + per_stage - 1;
+    if (kFp4A && wave < 4 && s + 1 < nst) last = n_sc + per_stage * (s + 1);
+    wait_vmcnt_upto(issued_before(s) - 1 - last);
     __builtin_amdgcn_s_barrier();  // stage s visible everywhere; every wave is past stage s-1
-    if (s + kAhead < nst) {
-      issue_w(s + kAhead);
-      issue(s + kAhead);
+    if (s + kAhead < nst) issue(s + kAhead);
+    if constexpr (kFp4A) {
+      if (s + 1 < nst) dequant_a(s + 1);  // read after the barrier at stage s + 1
     }
-    const uint8_t* sa = smem + (s % kRRing) * kRA;
+    const uint8_t* sa = smem + (kFp4A ? (s & 1) : (s % kRRing)) * kRA;
+    v8h fh[4];
     v8bf fa[4];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       const int r = 16 * t + c;
-      fa[t] = *reinterpret_cast<const v8bf*>(sa + r * 256 + (((4 * q + g) ^ (r & 15)) * 16));
+      const uint4 v = *reinterpret_cast<const uint4*>(sa + r * 256 + (((4 * q + g) ^ (r & 15)) * 16));
+      if constexpr (kFp4A)
+        fh[t] = __builtin_bit_cast(v8h, v);
+      else
+        fa[t] = __builtin_bit_cast(v8bf, v);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -370,10 +435,16 @@ __global__ void __launch_bounds__(kRNT)
       // K values 32q + 8g .. +7 of the stage: code word 4q + g, scale byte 2q + g/2
       const uint32_t word =
           *reinterpret_cast<const uint32_t*>(sq + s * (kRBN * 64) + col * 64 + ((q ^ ((col >> 2) & 3)) * 16) + 4 * g);
-      const uint32_t sb = sc[col * pitch + 8 * s + 2 * q + (g >> 1)];
-      const v8bf fb = dq8_bf16(word, e4m3_to_f32(sb));
+      const uint32_t sbw = sc[col * pitch + 8 * s + 2 * q + (g >> 1)];
+      if constexpr (kFp4A) {
+        const v8h fb = dq8_f16(word, e4m3_to_f16(sbw));
 #pragma unroll
-      for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[t], acc[j][t], 0, 0, 0);
+        for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb, fh[t], acc[j][t], 0, 0, 0);
+      } else {
+        const v8bf fb = dq8_bf16(word, e4m3_to_f32(sbw));
+#pragma unroll
+        for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[t], acc[j][t], 0, 0, 0);
+      }
     }
   }
   // ---- sum the four K quarters in LDS (in quarter order), then store
@@ -459,14 +530,14 @@ hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t
 
 namespace bsfp4 {
 
-// Used for 33..64 rows: measured with graph replay at N = 4096, K = 7168 it is
-// 4.3 us faster than the chunked small-M kernels at 64 rows, even at 32 rows
-// and slower below.  Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for
-// any 5..64 rows.
+// Used for 17..64 rows.  Measured cold at N = 4096, K = 7168 (both kernels,
+// events) against the split-K small-M kernels: M = 16 17.6 / 16.9 us (so 16
+// and fewer rows keep those), M = 17 17.8 / 18.7, M = 32 18.8 / 20.4.
+// Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for any 5..64 rows.
 bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_W4A16_ROWS64");
   if (e && e[0] == '0') return false;
-  const int64_t min_rows = (e && e[0] == '1') ? 5 : 33;
+  const int64_t min_rows = (e && e[0] == '1') ? 5 : 17;
   const int64_t lim = (int64_t)1 << 31;
   return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
          w4a16_rows64_splits(N, K, device_cu_count()) > 0;
@@ -477,17 +548,46 @@ size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K) {
   return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
-hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
-                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
-                               hipStream_t stream) {
+// NVFP4 activations: used for 17..64 rows (16 and fewer take the single-pass
+// LDS kernel).  Measured cold at N = 4096, K = 7168 (both kernels, events)
+// against the split / per-wave small-M kernels: M = 17 18.3 / 18.6 us,
+// M = 32 19.2 / 20.3, M = 33 19.2 / 21.9, M = 64 21.7 / 23.6.  Measurement
+// overrides: BSFP4_NVFP4_ROWS64=0 never, =1 for any 5..64 rows.
+bool nvfp4_rows64_ok(int64_t M, int64_t N, int64_t K) {
+  const char* e = getenv("BSFP4_NVFP4_ROWS64");
+  if (e && e[0] == '0') return false;
+  const int64_t min_rows = (e && e[0] == '1') ? 5 : 17;
+  const int64_t lim = (int64_t)1 << 31;
+  return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * (K / 2) < lim && N * (K / 2) < lim &&
+         w4a16_rows64_splits(N, K, device_cu_count()) > 0;
+}
+
+namespace {
+template <int AKIND>
+hipError_t launch_rows64(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                         const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
+                         size_t part_bytes, hipStream_t stream) {
   const int splits = w4a16_rows64_splits(N, K, device_cu_count());
   if (splits < 1 || (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))))
     return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(((N + kRBN - 1) / kRBN) * splits);
-  w4a16_rows64<<<grid, kRNT, 0, stream>>>(A, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
+  rows64_gemm<AKIND><<<grid, kRNT, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, alpha, D, M * N, stream);
+}
+}  // namespace
+
+hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
+                               uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
+                               hipStream_t stream) {
+  return launch_rows64<1>(A, nullptr, B, SFB, alpha, D, M, N, K, part, part_bytes, stream);
+}
+
+hipError_t launch_nvfp4_rows64(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
+                               size_t part_bytes, hipStream_t stream) {
+  return launch_rows64<0>(A, SFA, B, SFB, alpha, D, M, N, K, part, part_bytes, stream);
 }
 
 }  // namespace bsfp4

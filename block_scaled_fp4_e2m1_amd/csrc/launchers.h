@@ -58,8 +58,6 @@ hipError_t launch_skinny_w4a16(const uint16_t* A, const uint8_t* B, const uint8_
                                uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, hipStream_t stream);
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations);
 
-// D = bf16(alpha * sum_s part[s]) over `splits` FP32 partials of MN elements
-// (MN % 4 == 0), summed in split order.
 // Tiled W4A16 for M > kSkinnyMaxM (K % 64 == 0, operands below 2^31 bytes).
 bool w4a16_tiled_ok(int64_t M, int64_t N, int64_t K);
 size_t w4a16_tiled_workspace(int64_t M, int64_t N, int64_t K);
@@ -72,6 +70,14 @@ size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16_rows64(const uint16_t* A, const uint8_t* B, const uint8_t* SFB, const float* alpha,
                                uint16_t* D, int64_t M, int64_t N, int64_t K, float* part, size_t part_bytes,
                                hipStream_t stream);
+// The same 64-row kernel with NVFP4 activations (fp16 MFMA); its K split and
+// workspace are those of the W4A16 form (w4a16_rows64_workspace).
+bool nvfp4_rows64_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_nvfp4_rows64(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
+                               const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
+                               size_t part_bytes, hipStream_t stream);
+// D = bf16(alpha * sum_s part[s]) over `splits` FP32 partials of MN elements
+// (MN % 4 == 0), summed in split order.
 hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,
                                 hipStream_t stream);
 

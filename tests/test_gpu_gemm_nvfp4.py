@@ -215,10 +215,40 @@ def test_nvfp4_gemm_few_rows_fp4_mfma(monkeypatch, form, M, N, K):
     _check(got, aq, sfa, bq, sfb, alpha)
 
 
-@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
+@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160), (24, 160, 2048),
+                                   (32, 4096, 7168)])
 @pytest.mark.parametrize("mt4", ["1", "0"])
-def test_nvfp4_gemm_rows_33_to_64(monkeypatch, mt4, M, N, K):
+def test_nvfp4_gemm_rows_17_to_64_small_m_kernels(monkeypatch, mt4, M, N, K):
+    """Rows 17..64 through the chunked small-M kernels (split form with two or
+    four M tiles, per-wave form), the 64-row kernel switched off."""
+    monkeypatch.setenv("BSFP4_NVFP4_ROWS64", "0")
     monkeypatch.setenv("BSFP4_SKINNY_MT4", mt4)
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=600 + M)
     got = _run(aq, sfa, bq, sfb, alpha)
     _check(got, aq, sfa, bq, sfb, alpha)
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 128, 128), (16, 96, 1024), (33, 4096, 7168), (63, 288, 2048),
+                                   (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160),
+                                   (50, 4000, 5120), (36, 4096, 6144), (64, 4096, 8192), (47, 4096, 7168)])
+def test_nvfp4_gemm_rows64_kernel(monkeypatch, M, N, K):
+    """The 64 x 128 kernel with NVFP4 activations forced for any 5..64 rows
+    with K % 128 == 0: partial row and column tiles, one to eight 128-value
+    stages per K range (1, 2-4, 7, and 5 / 6 / 8 in the three shapes before
+    the last); K % 128 != 0 takes the other small-M kernels."""
+    monkeypatch.setenv("BSFP4_NVFP4_ROWS64", "1")
+    aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=640 + M)
+    got = _run(aq, sfa, bq, sfb, alpha)
+    _check(got, aq, sfa, bq, sfb, alpha)
+
+
+def test_nvfp4_gemm_rows64_every_scale_code():
+    """Every E4M3 scale code on both operands (incl. subnormal codes and zero)
+    through the 64-row kernel's fp16 dequantisation."""
+    M, N, K = 64, 256, 2048
+    aq = synth.random_bytes(661, (M, K // 2))
+    bq = synth.random_bytes(662, (N, K // 2))
+    sfa = (np.arange(M * (K // 16)) % 0x7F).astype(np.uint8).reshape(M, K // 16)
+    sfb = ((np.arange(N * (K // 16)) * 5 + 3) % 0x7F).astype(np.uint8).reshape(N, K // 16)
+    got = _run(aq, sfa, bq, sfb, None)
+    _check(got, aq, sfa, bq, sfb, None)

@@ -63,22 +63,25 @@ def test_w4a16_every_scale_code_no_alpha(M):
     _run_check(a, wq, wsf, None)
 
 
-@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160)])
+@pytest.mark.parametrize("M,N,K", [(33, 96, 1024), (64, 4096, 7168), (48, 160, 4160), (24, 160, 2048),
+                                   (32, 4096, 7168)])
 @pytest.mark.parametrize("mt4", ["1", "0"])
-def test_w4a16_rows_33_to_64(monkeypatch, mt4, M, N, K):
-    """Rows 33..64 through the chunked small-M kernels (split form with four M
-    tiles, per-wave form), the 64-row tiled kernel switched off."""
+def test_w4a16_rows_17_to_64_small_m_kernels(monkeypatch, mt4, M, N, K):
+    """Rows 17..64 through the chunked small-M kernels (split form with two or
+    four M tiles, per-wave form), the 64-row tiled kernel switched off."""
     monkeypatch.setenv("BSFP4_W4A16_ROWS64", "0")
     monkeypatch.setenv("BSFP4_SKINNY_MT4", mt4)
     _run_check(*_problem(M, N, K, 700 + M))
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 128, 128), (16, 96, 1024), (33, 4096, 7168), (63, 288, 2048),
-                                   (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160)])
+                                   (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160),
+                                   (50, 4000, 5120), (36, 4096, 6144), (64, 4096, 8192)])
 def test_w4a16_rows64_kernel(monkeypatch, M, N, K):
     """The 64 x 128 tiled kernel forced for any 5..64 rows with K % 128 == 0
-    (partial row and column tiles, one or several K ranges, one stage per
-    range); K % 128 != 0 takes the chunked small-M kernels."""
+    (partial row and column tiles, one or several K ranges, 1 to 8 stages per
+    range: 1, 2-4, 7, and 5 / 6 / 8 in the last three shapes); K % 128 != 0
+    takes the chunked small-M kernels."""
     monkeypatch.setenv("BSFP4_W4A16_ROWS64", "1")
     _run_check(*_problem(M, N, K, 720 + M))
 
