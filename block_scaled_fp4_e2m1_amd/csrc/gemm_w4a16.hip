@@ -22,6 +22,7 @@
 // consecutive output columns of one row; the tile leaves through LDS in row
 // bands (bf16 output, or FP32 partials of a K split that splitk_reduce sums in
 // split order).
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -251,42 +252,50 @@ __global__ void __launch_bounds__(kNT, 1)
 // MFMAs; the four K quarters are summed in LDS at the end, in quarter order.
 // The weight stream is what costs at these shapes; the activations (at most 64
 // rows) stay L2-resident and are re-read once per 128-column block.
-//   * the range's scales (8 bytes per row and stage; weights, and for NVFP4
-//     the activation rows too) are copied into LDS first; then the weight
-//     codes and the activations stage by stage, three stages ahead of the one
-//     in use: per wave and stage one load of weight codes (16 rows x 64 bytes
-//     into [stage][row][64 B], the 16-byte piece p of row r at position
-//     p ^ ((r >> 2) & 3), so the MFMA's 4-byte reads are conflict-free) and
-//     the stage's activations, so each stage waits only for its own loads and
-//     the MFMAs follow the stream.  Measured for W4A16 at 64 x 4096 x 7168
-//     cold (both kernels, events): weights of the whole range issued before
-//     the first stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us
-//     (the first of these is 16.6 us of this kernel in a rocprofv3 trace,
-//     against 17.7 us when the range was copied in long row segments ahead of
-//     everything);
-//   * bf16 activations go through a 4-slot ring of 128-value stages (64 rows x
-//     256 bytes, the 16-byte chunk x of row r at position x ^ (r & 15),
-//     conflict-free fragment reads), two loads per wave and stage;
-//   * NVFP4 activations: the stage's 64 rows x 64 code bytes go through a
-//     4-slot ring (one load each for waves 0-3) and are dequantised once per
-//     workgroup, one stage ahead of the MFMAs, into a 2-slot fp16 buffer laid
-//     out like the bf16 ring (each thread one 16-value block: two code words,
-//     one scale byte), so stage s waits for its weights and for the codes of
+//   * codes move stage by stage through 4-slot LDS rings, three stages ahead
+//     of the one in use, so each stage waits only for its own loads and the
+//     MFMAs follow the stream: per stage the weight codes (one load per wave:
+//     16 rows x 64 bytes into [row][64 B], the 16-byte piece p of row r at
+//     position p ^ ((r >> 2) & 3), so the MFMA's 4-byte reads are
+//     conflict-free) and the activations; the scales (8 bytes per row and
+//     stage) come in chunks of eight stages, 64 bytes per row (16 lanes of 4
+//     bytes per row, 4 rows per load, dwords swizzled within the row so that
+//     the scale reads are conflict-free), double-buffered: chunk 0
+//     before the first stage, chunk k with the codes of stage 8k - 1 (one
+//     load of 8 bytes per row and stage measured 1.7 us slower at
+//     64 x 4096 x 7168: each such load touches 32 rows; unswizzled chunks
+//     0.4 us slower again, from 8-way bank conflicts).  Measured for W4A16
+//     at 64 x 4096 x 7168 cold (both
+//     kernels, events): weights of the whole range issued before the first
+//     stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us (the first
+//     of these is 16.6 us of this kernel in a rocprofv3 trace, against 17.7 us
+//     when the range was copied in long row segments ahead of everything);
+//   * bf16 activations: 64 rows x 256 bytes a stage, the 16-byte chunk x of
+//     row r at position x ^ (r & 15) (conflict-free fragment reads), two loads
+//     per wave;
+//   * NVFP4 activations: the stage's 64 rows x 64 code bytes (waves 0-3; the
+//     scale chunks by all waves) are dequantised once per workgroup, one
+//     stage ahead of the MFMAs, into a 2-slot fp16 buffer laid out like the
+//     bf16 stages (each thread one 16-value block: two code words, one scale
+//     byte), so stage s waits for its weights and for the activations of
 //     stage s + 1;
-//   * K ranges of one column block are summed by splitk_reduce in range order.
+//   * K ranges of one column block are summed by splitk_reduce in range order;
+//     a range may hold any number of stages (the K split is planned by rounds
+//     of workgroups, rows64_splits).
 constexpr int kRBM = 64, kRBN = 128, kRNT = 512;
-constexpr int kRSK = 128;                   // K values per stage
-constexpr int kRA = kRBM * kRSK * 2;         // 16 KB of bf16 / fp16 activations per stage
-constexpr int kRRing = 4;                   // activation stages in LDS: 3 in flight ahead of the one in use
-constexpr int kRMaxStages = 8;              // stages per K range
-constexpr int kRQ = kRMaxStages * kRBN * 64;  // weight codes of the range: [stage][row][64 B]
-constexpr int kRScales = kRBN * kRMaxStages * 8;
-constexpr int kRSmem = kRRing * kRA + kRQ + kRScales;
-// NVFP4 activations, inside the first kRRing * kRA bytes: 2 fp16 stages, the
-// 4-slot code ring (64 rows x 64 B each) and the range's activation scales
-constexpr int kRAq = kRBM * 64;
-constexpr int kRAScales = kRBM * kRMaxStages * 8;
-static_assert(2 * kRA + kRRing * kRAq + kRAScales <= kRRing * kRA, "NVFP4 activation buffers fit");
+constexpr int kRSK = 128;                     // K values per stage
+constexpr int kRA = kRBM * kRSK * 2;           // 16 KB of bf16 / fp16 activations per stage
+constexpr int kRRing = 4;                     // stages in LDS: 3 in flight ahead of the one in use
+constexpr int kRW = kRBN * 64;                 // weight codes of a stage [128 rows][64 B]
+constexpr int kRAq = kRBM * 64;                // NVFP4 activation codes of a stage [64 rows][64 B]
+constexpr int kRChunk = 8;                     // stages per scale chunk
+constexpr int kRScW = kRBN * 8 * kRChunk, kRScA = kRBM * 8 * kRChunk;  // [rows][64 B] per chunk
+constexpr int kRActBytes = kRRing * kRA;       // bf16 ring; NVFP4: 2 fp16 stages + the code ring
+static_assert(2 * kRA + kRRing * kRAq <= kRActBytes, "NVFP4 activation buffers fit");
+constexpr int kRScBase = kRActBytes + kRRing * kRW;  // two scale chunks: [buf][W 8 KB | A 4 KB]
+constexpr int kRLoadBytes = kRScBase + 2 * (kRScW + kRScA);
+constexpr int kRedBytes = 4 * kRBM * (kRBN + 4) * 4;  // the four K quarters' FP32 tiles at the end
+constexpr int kRSmem = kRLoadBytes > kRedBytes ? kRLoadBytes : kRedBytes;
 
 template <int AKIND>
 __global__ void __launch_bounds__(kRNT)
@@ -303,44 +312,39 @@ __global__ void __launch_bounds__(kRNT)
   const int sb = (int)((int64_t)total * split / splits);
   const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
   const int k_lo = sb * kRSK;
-  uint8_t* const sq = smem + kRRing * kRA;  // [stage][128 rows][64 B], pieces swizzled
-  uint8_t* const sc = sq + kRQ;             // [128 rows][8 nst bytes]
-  uint8_t* const saq = smem + 2 * kRA;      // NVFP4: [slot][64 rows][64 B] activation codes
-  uint8_t* const sas = saq + kRRing * kRAq;  // NVFP4: [64 rows][8 nst bytes] activation scales
-  const int pitch = 8 * nst;
+  uint8_t* const sw = smem + kRActBytes;  // [slot][codes 128 x 64 B]
+  uint8_t* const saq = smem + 2 * kRA;    // NVFP4: [slot][codes 64 x 64 B]
+  uint8_t* const ssc = smem + kRScBase;   // [chunk % 2][W scales 128 x 64 B | A scales 64 x 64 B]
   const v4u32 ra = make_rsrc4(Aptr, kFp4A ? (int64_t)M * (K / 2) : (int64_t)M * K * 2);
   const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
   const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
   auto lds_u = [](const void* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(p)); };
+  auto soff = [](int v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); };
 
-  // ---- the range's scales first, 64 dwords per load (2 dwords per row and
-  // stage): 4 nst loads of weight scales, then (NVFP4) 2 nst of activation scales
-  int n_sc = 0;  // this wave's scale loads
-  const int sc_loads = (kFp4A ? 6 : 4) * nst;
-  for (int i = wave; i < sc_loads; i += kRNT / 64) {
-    if (i < 4 * nst) {
-      const int d = 64 * i + lane, row = d / (2 * nst), word = d - row * (2 * nst);
-      const uint32_t off = n0 + row < N ? (uint32_t)((n0 + row) * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
-      buf_lds4(rs, off, 0, lds_u(sc + 256 * i));
-    } else {
-      const v4u32 ras = make_rsrc4(SFA, (int64_t)M * (K / 16));
-      const int d = 64 * (i - 4 * nst) + lane, row = d / (2 * nst), word = d - row * (2 * nst);
-      const uint32_t off = row < M ? (uint32_t)(row * (K / 16) + k_lo / 16 + 4 * word) : kBufOOB;
-      buf_lds4(ras, off, 0, lds_u(sas + 256 * (i - 4 * nst)));
-    }
-    n_sc++;
-  }
-  // ---- weight codes, one load per wave and stage: rows 16 wave + lane / 4, logical piece
-  // (lane & 3) ^ ((row >> 2) & 3) of the stage's 64 bytes at LDS position lane & 3
+  // ---- per-lane offsets (the stage's K offset goes in the SGPR offset)
+  // weight codes: rows 16 wave + lane / 4, logical piece (lane & 3) ^ ((row >> 2) & 3)
+  // of the stage's 64 bytes at LDS position lane & 3
   const int wrow = 16 * wave + (lane >> 2);
   const uint32_t vw = n0 + wrow < N
                           ? (uint32_t)((n0 + wrow) * (K / 2) + k_lo / 2 + 16 * ((lane & 3) ^ ((wrow >> 2) & 3)))
                           : kBufOOB;
-  auto issue_w = [&](int st) {
-    buf_lds16(rq, vw, (uint32_t)__builtin_amdgcn_readfirstlane(st * 64),
-              lds_u(sq + st * (kRBN * 64) + wave * 1024));
-  };
-  // ---- activations (the stage's K offset goes in the SGPR offset)
+  // scale chunks: load j (0..3) of wave w covers weight rows 4 (4 w + j) +
+  // lane / 16, NVFP4 activation load j (0..1) rows 4 (2 w + j) + lane / 16;
+  // dword d of the chunk's 64 bytes of row r lands at position d ^ (r & 15) of
+  // the row, so the 16 rows that one scale read spans hit distinct banks
+  uint32_t vws[4], vas[2];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int wr = 4 * (4 * wave + j) + (lane >> 4);
+    vws[j] = n0 + wr < N ? (uint32_t)((n0 + wr) * (K / 16) + k_lo / 16 + 4 * ((lane & 15) ^ (wr & 15))) : kBufOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int ar = 4 * (2 * wave + j) + (lane >> 4);
+    vas[j] = ar < M ? (uint32_t)(ar * (K / 16) + k_lo / 16 + 4 * ((lane & 15) ^ (ar & 15))) : kBufOOB;
+  }
+  // byte `byte` of row r's 64 chunk bytes (dword swizzle above)
+  auto sc_at = [](int r, int byte) { return r * 64 + (((byte >> 2) ^ (r & 15)) << 2) + (byte & 3); };
   uint32_t va[2];
   if constexpr (kFp4A) {
     // waves 0-3: rows 16 wave + lane / 4, 16-byte piece lane & 3 of the stage's 64 code bytes
@@ -355,18 +359,35 @@ __global__ void __launch_bounds__(kRNT)
       va[j] = r < M ? (uint32_t)(r * (K * 2) + x * 16) : kBufOOB;
     }
   }
-  // loads per stage of this wave, issued in this order: NVFP4 A (waves 0-3) then W; bf16 W then A, A
-  const int per_stage = kFp4A ? (wave < 4 ? 2 : 1) : 3;
+  // This wave's loads of one stage, in issue order: NVFP4 the activation
+  // codes (waves 0-3) then the weight codes; bf16 weight codes then two
+  // activation loads.  A scale chunk is cl loads: 4 of weight scales, and for
+  // NVFP4 2 more of activation scales.
+  const int n_act = kFp4A ? (wave < 4 ? 1 : 0) : 2;
+  const int per_stage = n_act + 1;
+  constexpr int cl = kFp4A ? 6 : 4;
+  const int nchunks = (nst + kRChunk - 1) / kRChunk;
+  auto issue_chunk = [&](int k) {
+    uint8_t* buf = ssc + (k & 1) * (kRScW + kRScA);
+#pragma unroll
+    for (int j = 0; j < 4; j++) buf_lds4(rs, vws[j], soff(64 * k), lds_u(buf + (4 * wave + j) * 256));
+    if constexpr (kFp4A) {
+      const v4u32 ras = make_rsrc4(SFA, (int64_t)M * (K / 16));
+#pragma unroll
+      for (int j = 0; j < 2; j++) buf_lds4(ras, vas[j], soff(64 * k), lds_u(buf + kRScW + (2 * wave + j) * 256));
+    }
+  };
+  auto issue_w = [&](int st) {
+    buf_lds16(rq, vw, soff(st * 64), lds_u(sw + (st % kRRing) * kRW + wave * 1024));
+  };
   auto issue = [&](int st) {
     if constexpr (kFp4A) {
-      if (wave < 4)
-        buf_lds16(ra, va[0], (uint32_t)__builtin_amdgcn_readfirstlane(st * 64),
-                  lds_u(saq + (st % kRRing) * kRAq + wave * 1024));
+      if (wave < 4) buf_lds16(ra, va[0], soff(st * 64), lds_u(saq + (st % kRRing) * kRAq + wave * 1024));
       issue_w(st);
     } else {
       issue_w(st);
       uint8_t* base = smem + (st % kRRing) * kRA;
-      const uint32_t k0 = (uint32_t)__builtin_amdgcn_readfirstlane((k_lo + st * kRSK) * 2);
+      const uint32_t k0 = soff((k_lo + st * kRSK) * 2);
       buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
       buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
     }
@@ -376,22 +397,29 @@ __global__ void __launch_bounds__(kRNT)
   auto dequant_a = [&](int st) {
     const int r = tid >> 3, b = tid & 7;
     const uint2 w = *reinterpret_cast<const uint2*>(saq + (st % kRRing) * kRAq + r * 64 + 8 * b);
-    const _Float16 s = e4m3_to_f16(sas[r * pitch + 8 * st + b]);
+    const uint8_t* asc = ssc + ((st / kRChunk) & 1) * (kRScW + kRScA) + kRScW;
+    const _Float16 s = e4m3_to_f16(asc[sc_at(r, (st % kRChunk) * 8 + b)]);
     uint8_t* row = smem + (st & 1) * kRA + r * 256;
     *reinterpret_cast<v8h*>(row + (((2 * b) ^ (r & 15)) * 16)) = dq8_f16(w.x, s);
     *reinterpret_cast<v8h*>(row + (((2 * b + 1) ^ (r & 15)) * 16)) = dq8_f16(w.y, s);
   };
-  // Load st is the group of per_stage loads at n_sc + per_stage * st in this
-  // wave's issue order (three stages before the loop, one more per stage).
-  // Loads complete in order; waiting for "issued - 1 - index" outstanding
-  // means the load at that index has landed.
+  // This wave's issue order: chunk 0, stages 0, 1, 2, then at stage s the
+  // loads of stage s + 3, followed by chunk k when s + 3 == 8k - 1.  Loads
+  // complete in order; waiting for "issued - 1 - index" outstanding means the
+  // load at that index has landed.
   constexpr int kAhead = kRRing - 1;
-  const int first = min(nst, kAhead);
-  for (int st = 0; st < first; st++) issue(st);
-  auto issued_before = [&](int s) { return n_sc + per_stage * min(nst, s + kAhead); };
+  auto chunks_before = [&](int st) { return min(st / kRChunk, nchunks - 1); };  // chunks k >= 1 before stage st
+  auto last_of_stage = [&](int st) { return cl - 1 + per_stage * (st + 1) + cl * chunks_before(st); };
+  auto last_of_chunk = [&](int k) { return k == 0 ? cl - 1 : last_of_stage(kRChunk * k - 1) + cl; };
+  auto issued_before = [&](int s) {  // loads issued before stage s's wait
+    const int g = min(nst, s + kAhead);
+    return cl + per_stage * g + cl * min(g / kRChunk, nchunks - 1);
+  };
+  issue_chunk(0);
+  for (int st = 0; st < min(nst, kAhead); st++) issue(st);
   if constexpr (kFp4A) {
-    // scales and the codes of stage 0 (the first load of a waves-0-3 group)
-    wait_vmcnt_upto(issued_before(0) - 1 - (wave < 4 ? n_sc : n_sc - 1));
+    // the activation codes (waves 0-3) and scales (waves 4-7) of stage 0
+    wait_vmcnt_upto(issued_before(0) - 1 - (n_act > 0 ? last_of_stage(0) - per_stage + n_act : last_of_chunk(0)));
     __builtin_amdgcn_s_barrier();
     dequant_a(0);
   }
@@ -406,14 +434,18 @@ __global__ void __launch_bounds__(kRNT)
 #pragma unroll
     for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
   for (int s = 0; s < nst; s++) {
-    // bf16: this wave's group of stage s (its last load); NVFP4: the weights
-    // of stage s (last load of group s) and the codes of stage s + 1 (first
-    // load of group s + 1, waves 0-3)
-    int last = n_sc + per_stage * s + per_stage - 1;
-    if (kFp4A && wave < 4 && s + 1 < nst) last = n_sc + per_stage * (s + 1);
+    // this wave's loads of stage s (and so its scale chunk); NVFP4 also the
+    // activation codes of stage s + 1 (waves 0-3) or the scale chunk of stage
+    // s + 1 (waves 4-7)
+    int last = last_of_stage(s);
+    if (kFp4A && s + 1 < nst)
+      last = n_act > 0 ? last_of_stage(s + 1) - per_stage + n_act : max(last, last_of_chunk((s + 1) / kRChunk));
     wait_vmcnt_upto(issued_before(s) - 1 - last);
     __builtin_amdgcn_s_barrier();  // stage s visible everywhere; every wave is past stage s-1
-    if (s + kAhead < nst) issue(s + kAhead);
+    if (s + kAhead < nst) {
+      issue(s + kAhead);
+      if ((s + kAhead) % kRChunk == kRChunk - 1 && s + kAhead + 1 < nst) issue_chunk((s + kAhead + 1) / kRChunk);
+    }
     if constexpr (kFp4A) {
       if (s + 1 < nst) dequant_a(s + 1);  // read after the barrier at stage s + 1
     }
@@ -433,9 +465,9 @@ __global__ void __launch_bounds__(kRNT)
     for (int j = 0; j < 4; j++) {
       const int col = 64 * h + 16 * j + c;
       // K values 32q + 8g .. +7 of the stage: code word 4q + g, scale byte 2q + g/2
-      const uint32_t word =
-          *reinterpret_cast<const uint32_t*>(sq + s * (kRBN * 64) + col * 64 + ((q ^ ((col >> 2) & 3)) * 16) + 4 * g);
-      const uint32_t sbw = sc[col * pitch + 8 * s + 2 * q + (g >> 1)];
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(sw + (s % kRRing) * kRW + col * 64 +
+                                                               ((q ^ ((col >> 2) & 3)) * 16) + 4 * g);
+      const uint32_t sbw = ssc[((s / kRChunk) & 1) * (kRScW + kRScA) + sc_at(col, (s % kRChunk) * 8 + 2 * q + (g >> 1))];
       if constexpr (kFp4A) {
         const v8h fb = dq8_f16(word, e4m3_to_f16(sbw));
 #pragma unroll
@@ -450,7 +482,7 @@ __global__ void __launch_bounds__(kRNT)
   // ---- sum the four K quarters in LDS (in quarter order), then store
   __syncthreads();  // LDS is free
   constexpr int kRedPitch = kRBN + 4;  // floats per row of one quarter's 64 x 128 tile
-  static_assert(4 * kRBM * kRedPitch * 4 <= kRSmem, "quarter tiles fit in LDS");
+  static_assert(4 * kRBM * kRedPitch * 4 <= kRSmem && kRedBytes == 4 * kRBM * kRedPitch * 4, "quarter tiles fit");
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int j = 0; j < 4; j++)
@@ -481,14 +513,30 @@ __global__ void __launch_bounds__(kRNT)
   }
 }
 
-// K split of the 64-row kernel: enough work items for the CUs, at least two
-// stages per range, at most kRMaxStages; 0 if no split fits.
-int w4a16_rows64_splits(int64_t N, int64_t K, int cus) {
+// K split of the 64-row kernel: the number of K ranges that minimises an
+// estimate of the time in units of one stage (~0.6 us, measured cold): rounds
+// of workgroups (one per CU) x (stages per range + ~3 for the set-up and the
+// quarter sum), plus for a split the FP32 partials written and read back (M x N
+// x 8 bytes per range at ~5 TB/s) and the reduce launch (~6).  Measurement
+// override BSFP4_ROWS64_SPLITS=n.
+int rows64_splits(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = (N + kRBN - 1) / kRBN, total = K / kRSK;
-  int64_t s = 1;
-  while (s < 16 && tiles * (s + 1) <= cus && total / (s + 1) >= 2) s++;
-  while ((total + s - 1) / s > kRMaxStages && s < total) s++;
-  return (total + s - 1) / s <= kRMaxStages ? (int)s : 0;
+  if (total < 1) return 0;
+  const char* e = getenv("BSFP4_ROWS64_SPLITS");
+  if (e && atoi(e) > 0) return (int)std::min<int64_t>(atoi(e), total);
+  constexpr double kStageUs = 0.6, kBytesPerUs = 5.0e6;
+  int best = 1;
+  double best_t = 1e300;
+  for (int64_t sp = 1; sp <= std::min<int64_t>(total, 64); sp++) {
+    const int64_t rounds = (tiles * sp + cus - 1) / cus;
+    double t = (double)rounds * ((total + sp - 1) / sp + 3);
+    if (sp > 1) t += 8.0 * sp * M * N / kBytesPerUs / kStageUs + 6;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = (int)sp;
+    }
+  }
+  return best;
 }
 
 int w4a16_splits(int64_t M, int64_t N, int64_t K, int cus) {
@@ -532,7 +580,9 @@ namespace bsfp4 {
 
 // Used for 17..64 rows.  Measured cold at N = 4096, K = 7168 (both kernels,
 // events) against the split-K small-M kernels: M = 16 17.6 / 16.9 us (so 16
-// and fewer rows keep those), M = 17 17.8 / 18.7, M = 32 18.8 / 20.4.
+// and fewer rows keep those), M = 17 17.8 / 18.7, M = 32 19.2 / 20.4; at the
+// projection shapes (M = 32; N x K = 6656 x 19968 / 19968 x 6656) 46.8 /
+// 49.4 us, where K ranges of up to 8 stages took 67.8 / 65.6 us.
 // Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for any 5..64 rows.
 bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_W4A16_ROWS64");
@@ -540,26 +590,25 @@ bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const int64_t min_rows = (e && e[0] == '1') ? 5 : 17;
   const int64_t lim = (int64_t)1 << 31;
   return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
-         w4a16_rows64_splits(N, K, device_cu_count()) > 0;
+         rows64_splits(M, N, K, device_cu_count()) > 0;
 }
 
 size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K) {
-  const int s = w4a16_rows64_splits(N, K, device_cu_count());
+  const int s = rows64_splits(M, N, K, device_cu_count());
   return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
-// NVFP4 activations: used for 17..64 rows (16 and fewer take the single-pass
-// LDS kernel).  Measured cold at N = 4096, K = 7168 (both kernels, events)
-// against the split / per-wave small-M kernels: M = 17 18.3 / 18.6 us,
-// M = 32 19.2 / 20.3, M = 33 19.2 / 21.9, M = 64 21.7 / 23.6.  Measurement
-// overrides: BSFP4_NVFP4_ROWS64=0 never, =1 for any 5..64 rows.
+// NVFP4 activations: used for 24..64 rows.  Measured cold at N = 4096,
+// K = 7168 (both kernels, events) against the split / per-wave small-M
+// kernels: M = 17 18.8 / 18.4 us, M = 32 19.8 / 20.2, M = 64 22.2 / 23.6.
+// Measurement overrides: BSFP4_NVFP4_ROWS64=0 never, =1 for any 5..64 rows.
 bool nvfp4_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_NVFP4_ROWS64");
   if (e && e[0] == '0') return false;
-  const int64_t min_rows = (e && e[0] == '1') ? 5 : 17;
+  const int64_t min_rows = (e && e[0] == '1') ? 5 : 24;
   const int64_t lim = (int64_t)1 << 31;
   return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * (K / 2) < lim && N * (K / 2) < lim &&
-         w4a16_rows64_splits(N, K, device_cu_count()) > 0;
+         rows64_splits(M, N, K, device_cu_count()) > 0;
 }
 
 namespace {
@@ -567,7 +616,7 @@ template <int AKIND>
 hipError_t launch_rows64(const void* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                          const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                          size_t part_bytes, hipStream_t stream) {
-  const int splits = w4a16_rows64_splits(N, K, device_cu_count());
+  const int splits = rows64_splits(M, N, K, device_cu_count());
   if (splits < 1 || (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))))
     return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(((N + kRBN - 1) / kRBN) * splits);

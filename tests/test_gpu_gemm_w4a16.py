@@ -86,6 +86,16 @@ def test_w4a16_rows64_kernel(monkeypatch, M, N, K):
     _run_check(*_problem(M, N, K, 720 + M))
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(64, 256, 8192, "1"), (40, 640, 4096, "3"), (17, 6656, 19968, ""),
+                                          (33, 1024, 2048, "16")])
+def test_w4a16_rows64_long_ranges(monkeypatch, M, N, K, splits):
+    """The 64-row kernel with K ranges of many stages (64 in one range, the
+    planner's 4 x 39 at the down-projection shape) and with one stage per range."""
+    if splits:
+        monkeypatch.setenv("BSFP4_ROWS64_SPLITS", splits)
+    _run_check(*_problem(M, N, K, 740 + M))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 7168), (16, 288, 4160), (29, 1056, 16384)])
 def test_w4a16_split_forms(M, N, K):
     """Split-K form (one or two M tiles) incl. K longer than 16 loads per lane."""
