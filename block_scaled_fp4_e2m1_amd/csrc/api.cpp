@@ -238,8 +238,8 @@ bsfp4_status fp4_gemm_noalloc(int fmt, const uint8_t* A, const uint8_t* SFA, con
 
 size_t w4a16_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  if (bsfp4::w4a16_tiled_ok(M, N, K)) return bsfp4::w4a16_tiled_workspace(M, N, K);
   if (bsfp4::w4a16_rows64_ok(M, N, K)) return bsfp4::w4a16_rows64_workspace(M, N, K);
+  if (bsfp4::w4a16_tiled_ok(M, N, K)) return bsfp4::w4a16_tiled_workspace(M, N, K);
   // rows run in chunks of at most kSkinnyMaxM; the partials of one chunk are
   // reduced before the next chunk starts on the same stream
   const int64_t mc = M < bsfp4::kSkinnyMaxM ? M : bsfp4::kSkinnyMaxM;
@@ -277,13 +277,13 @@ bsfp4_status w4a16_gemm(const uint16_t* A, const uint8_t* B, const uint8_t* SFB,
   }
   if (M == 0) return ok();
   if (bsfp4_status s = check_device()) return s;
-  if (bsfp4::w4a16_tiled_ok(M, N, K))
-    return launched(bsfp4::launch_w4a16_tiled(A, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), ws_bytes,
-                                              as_stream(stream)),
-                    "w4a16_gemm launch");
   if (bsfp4::w4a16_rows64_ok(M, N, K))
     return launched(bsfp4::launch_w4a16_rows64(A, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), ws_bytes,
                                                as_stream(stream)),
+                    "w4a16_gemm launch");
+  if (bsfp4::w4a16_tiled_ok(M, N, K))
+    return launched(bsfp4::launch_w4a16_tiled(A, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), ws_bytes,
+                                              as_stream(stream)),
                     "w4a16_gemm launch");
   // rows in chunks of kSkinnyMaxM (the weight stream is re-read once per chunk)
   for (int64_t m0 = 0; m0 < M; m0 += bsfp4::kSkinnyMaxM) {

@@ -517,6 +517,8 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
                              const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (nvfp4_rows64_ok(M, N, K))
+    return launch_nvfp4_rows64(A, SFA, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), ws_bytes, stream);
   if (M <= kSkinnyMaxM)
     return launch_skinny_nvfp4(A, SFA, B, SFB, alpha, D, M, N, K, static_cast<float*>(ws), stream);
   const int v = nvfp4_variant(M, N, K);
@@ -577,6 +579,7 @@ int device_cu_count() {
 }
 
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  if (nvfp4_rows64_ok(M, N, K)) return w4a16_rows64_workspace(M, N, K);
   if (M <= kSkinnyMaxM) return skinny_workspace(M, N, K, true);
   const Plan pl = plan_tiled(M, N, K, device_cu_count(), dequant_once(nvfp4_variant(M, N, K)));
   return pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;

@@ -1008,9 +1008,6 @@ hipError_t launch_kind(const void* A, const uint8_t* SFA, const uint8_t* B, cons
 hipError_t launch_skinny_nvfp4(const uint8_t* A, const uint8_t* SFA, const uint8_t* B, const uint8_t* SFB,
                                const float* alpha, uint16_t* D, int64_t M, int64_t N, int64_t K, float* part,
                                hipStream_t stream) {
-  // the caller's workspace holds skinny_workspace(M, N, K, true) bytes
-  if (nvfp4_rows64_ok(M, N, K))
-    return launch_nvfp4_rows64(A, SFA, B, SFB, alpha, D, M, N, K, part, w4a16_rows64_workspace(M, N, K), stream);
   return launch_kind<0>(A, SFA, B, SFB, alpha, D, M, N, K, part, stream);
 }
 
@@ -1031,7 +1028,6 @@ hipError_t launch_nvfp4_fused_quant_gemm(const uint16_t* x, const float* gs, con
 
 size_t skinny_workspace(int64_t M, int64_t N, int64_t K, bool fp4_activations) {
   if (M <= 0 || M > 64 || N * (K / 2) >= ((int64_t)1 << 31)) return 0;
-  if (fp4_activations && nvfp4_rows64_ok(M, N, K)) return w4a16_rows64_workspace(M, N, K);
   if (use_few(fp4_activations ? 0 : 1, M, N, K)) return 0;
   if (fp4_activations && (use_lds(M, N, K) || use_onepass(M, N, K))) return 0;
   if (M > 32 && !split_mt4(fp4_activations ? 0 : 1)) return 0;

@@ -241,18 +241,20 @@ __global__ void __launch_bounds__(kNT, 1)
 
 
 // ---------------------------------------------------------------------------
-// 64-row GEMM for 17 <= M <= 64 (fewer rows use the kernels of
+// Row GEMM for 17 <= M <= 128 (fewer rows use the kernels of
 // gemm_skinny.hip), W4A16 (AKIND 1: bf16 activations, bf16 MFMA) or NVFP4 W4A4
 // (AKIND 0: NVFP4 activations dequantised to fp16, fp16 MFMA; E2M1 x E4M3
-// values are exact in either type): one workgroup = all 64 rows x 128 output
-// columns x one K range, 8 waves = 2 column halves x 4 K quarters of every
-// stage: a wave owns 64 columns x 64 rows (16 v_mfma_f32_16x16x32 tiles) for 32
-// of the stage's 128 K values, so every weight value is dequantised exactly
-// once per workgroup and each activation fragment read from LDS feeds four
-// MFMAs; the four K quarters are summed in LDS at the end, in quarter order.
-// The weight stream is what costs at these shapes; the activations (at most 64
-// rows) stay L2-resident and are re-read once per 128-column block.
-//   * codes move stage by stage through 4-slot LDS rings, three stages ahead
+// values are exact in either type): one workgroup = all BM = 64 or 128 rows x
+// 128 output columns x one K range, 8 waves = 2 column halves x 4 K quarters
+// of every stage: a wave owns 64 columns x BM rows (4 x BM/16
+// v_mfma_f32_16x16x32 tiles) for 32 of the stage's 128 K values, so every
+// weight value is dequantised exactly once per workgroup and each weight
+// fragment feeds BM/16 MFMAs; the four K quarters are summed in LDS at the
+// end, in quarter order, 64 rows at a time.  The weight stream is what costs
+// at these shapes; the activations (at most 128 rows) stay L2-resident and
+// are re-read once per 128-column block.
+//   * codes move stage by stage through LDS rings of 4 slots (3 for 128 rows,
+//     whose activation stages are twice as large), three (two) stages ahead
 //     of the one in use, so each stage waits only for its own loads and the
 //     MFMAs follow the stream: per stage the weight codes (one load per wave:
 //     16 rows x 64 bytes into [row][64 B], the 16-byte piece p of row r at
@@ -265,45 +267,58 @@ __global__ void __launch_bounds__(kNT, 1)
 //     load of 8 bytes per row and stage measured 1.7 us slower at
 //     64 x 4096 x 7168: each such load touches 32 rows; unswizzled chunks
 //     0.4 us slower again, from 8-way bank conflicts).  Measured for W4A16
-//     at 64 x 4096 x 7168 cold (both
-//     kernels, events): weights of the whole range issued before the first
+//     at 64 x 4096 x 7168 cold (both kernels, events): weights of the
+//     whole range issued before the first
 //     stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us (the first
 //     of these is 16.6 us of this kernel in a rocprofv3 trace, against 17.7 us
 //     when the range was copied in long row segments ahead of everything);
-//   * bf16 activations: 64 rows x 256 bytes a stage, the 16-byte chunk x of
-//     row r at position x ^ (r & 15) (conflict-free fragment reads), two loads
-//     per wave;
-//   * NVFP4 activations: the stage's 64 rows x 64 code bytes (waves 0-3; the
-//     scale chunks by all waves) are dequantised once per workgroup, one
-//     stage ahead of the MFMAs, into a 2-slot fp16 buffer laid out like the
-//     bf16 stages (each thread one 16-value block: two code words, one scale
-//     byte), so stage s waits for its weights and for the activations of
-//     stage s + 1;
+//   * bf16 activations: BM rows x 256 bytes a stage, the 16-byte chunk x of
+//     row r at position x ^ (r & 15) (conflict-free fragment reads), BM/32
+//     loads per wave;
+//   * NVFP4 activations: the stage's BM rows x 64 code bytes (one load per
+//     wave below BM/16; the scale chunks by all waves) are dequantised once
+//     per workgroup, one stage ahead of the MFMAs, into a 2-slot fp16 buffer
+//     laid out like the bf16 stages (each thread BM/64 16-value blocks: two
+//     code words and one scale byte each), so stage s waits for its weights
+//     and for the activations of stage s + 1;
 //   * K ranges of one column block are summed by splitk_reduce in range order;
 //     a range may hold any number of stages (the K split is planned by rounds
 //     of workgroups, rows64_splits).
-constexpr int kRBM = 64, kRBN = 128, kRNT = 512;
+constexpr int kRBN = 128, kRNT = 512;
 constexpr int kRSK = 128;                     // K values per stage
-constexpr int kRA = kRBM * kRSK * 2;           // 16 KB of bf16 / fp16 activations per stage
-constexpr int kRRing = 4;                     // stages in LDS: 3 in flight ahead of the one in use
 constexpr int kRW = kRBN * 64;                 // weight codes of a stage [128 rows][64 B]
-constexpr int kRAq = kRBM * 64;                // NVFP4 activation codes of a stage [64 rows][64 B]
 constexpr int kRChunk = 8;                     // stages per scale chunk
-constexpr int kRScW = kRBN * 8 * kRChunk, kRScA = kRBM * 8 * kRChunk;  // [rows][64 B] per chunk
-constexpr int kRActBytes = kRRing * kRA;       // bf16 ring; NVFP4: 2 fp16 stages + the code ring
-static_assert(2 * kRA + kRRing * kRAq <= kRActBytes, "NVFP4 activation buffers fit");
-constexpr int kRScBase = kRActBytes + kRRing * kRW;  // two scale chunks: [buf][W 8 KB | A 4 KB]
-constexpr int kRLoadBytes = kRScBase + 2 * (kRScW + kRScA);
-constexpr int kRedBytes = 4 * kRBM * (kRBN + 4) * 4;  // the four K quarters' FP32 tiles at the end
-constexpr int kRSmem = kRLoadBytes > kRedBytes ? kRLoadBytes : kRedBytes;
+constexpr int kRScW = kRBN * 8 * kRChunk;      // weight scales of a chunk [128 rows][64 B]
+constexpr int kRHalf = 64;                     // rows of one quarter-sum pass
+constexpr int kRedBytes = 4 * kRHalf * (kRBN + 4) * 4;  // the four K quarters' FP32 tiles of 64 rows
 
-template <int AKIND>
+// LDS plan of the BM-row kernel (BM = 64 or 128): RING stages (4, or 3 for
+// 128 rows) of activations (bf16: BM x 256 B; NVFP4: 2 fp16 stages and a ring
+// of BM x 64 code bytes) and of weight codes, and two scale chunks.
+template <int BM>
+struct RowsGeo {
+  static constexpr int kRing = BM == 64 ? 4 : 3;
+  static constexpr int kA = BM * kRSK * 2;     // bf16 / fp16 activations of a stage
+  static constexpr int kAq = BM * 64;          // NVFP4 activation codes of a stage
+  static constexpr int kScA = BM * 8 * kRChunk;  // NVFP4 activation scales of a chunk [BM rows][64 B]
+  static constexpr int kActBytes = kRing * kA;
+  static_assert(2 * kA + kRing * kAq <= kActBytes, "NVFP4 activation buffers fit");
+  static constexpr int kScBase = kActBytes + kRing * kRW;
+  static constexpr int kLoadBytes = kScBase + 2 * (kRScW + kScA);
+  static constexpr int kSmem = kLoadBytes > kRedBytes ? kLoadBytes : kRedBytes;
+  static_assert(kSmem <= 160 * 1024, "LDS");
+};
+
+template <int AKIND, int BM>
 __global__ void __launch_bounds__(kRNT)
     rows64_gemm(const void* __restrict__ Aptr, const uint8_t* __restrict__ SFA, const uint8_t* __restrict__ B,
                 const uint8_t* __restrict__ SFB, const float* __restrict__ alpha_ptr, uint16_t* __restrict__ D,
                 int M, int N, int K, int splits, float* __restrict__ part) {
   constexpr bool kFp4A = AKIND == 0;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRSmem];
+  using G = RowsGeo<BM>;
+  constexpr int kRing = G::kRing, kRA = G::kA, kRAq = G::kAq, kRScA = G::kScA;
+  constexpr int kTM = BM / 16;  // 16-row MFMA tiles of a wave
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::kSmem];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x % splits;
@@ -312,9 +327,9 @@ __global__ void __launch_bounds__(kRNT)
   const int sb = (int)((int64_t)total * split / splits);
   const int nst = (int)((int64_t)total * (split + 1) / splits) - sb;
   const int k_lo = sb * kRSK;
-  uint8_t* const sw = smem + kRActBytes;  // [slot][codes 128 x 64 B]
-  uint8_t* const saq = smem + 2 * kRA;    // NVFP4: [slot][codes 64 x 64 B]
-  uint8_t* const ssc = smem + kRScBase;   // [chunk % 2][W scales 128 x 64 B | A scales 64 x 64 B]
+  uint8_t* const sw = smem + G::kActBytes;  // [slot][codes 128 x 64 B]
+  uint8_t* const saq = smem + 2 * kRA;      // NVFP4: [slot][codes BM x 64 B]
+  uint8_t* const ssc = smem + G::kScBase;   // [chunk % 2][W scales 128 x 64 B | A scales BM x 64 B]
   const v4u32 ra = make_rsrc4(Aptr, kFp4A ? (int64_t)M * (K / 2) : (int64_t)M * K * 2);
   const v4u32 rq = make_rsrc4(B, (int64_t)N * (K / 2));
   const v4u32 rs = make_rsrc4(SFB, (int64_t)N * (K / 16));
@@ -329,43 +344,47 @@ __global__ void __launch_bounds__(kRNT)
                           ? (uint32_t)((n0 + wrow) * (K / 2) + k_lo / 2 + 16 * ((lane & 3) ^ ((wrow >> 2) & 3)))
                           : kBufOOB;
   // scale chunks: load j (0..3) of wave w covers weight rows 4 (4 w + j) +
-  // lane / 16, NVFP4 activation load j (0..1) rows 4 (2 w + j) + lane / 16;
-  // dword d of the chunk's 64 bytes of row r lands at position d ^ (r & 15) of
-  // the row, so the 16 rows that one scale read spans hit distinct banks
-  uint32_t vws[4], vas[2];
+  // lane / 16, NVFP4 activation load j (0..BM/32-1) rows 4 (BM/32 w + j) +
+  // lane / 16; dword d of the chunk's 64 bytes of row r lands at position
+  // d ^ (r & 15) of the row, so the 16 rows that one scale read spans hit
+  // distinct banks
+  constexpr int kAsc = BM / 32;  // activation-scale loads per wave and chunk (NVFP4)
+  uint32_t vws[4], vas[kAsc];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int wr = 4 * (4 * wave + j) + (lane >> 4);
     vws[j] = n0 + wr < N ? (uint32_t)((n0 + wr) * (K / 16) + k_lo / 16 + 4 * ((lane & 15) ^ (wr & 15))) : kBufOOB;
   }
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int ar = 4 * (2 * wave + j) + (lane >> 4);
+  for (int j = 0; j < kAsc; j++) {
+    const int ar = 4 * (kAsc * wave + j) + (lane >> 4);
     vas[j] = ar < M ? (uint32_t)(ar * (K / 16) + k_lo / 16 + 4 * ((lane & 15) ^ (ar & 15))) : kBufOOB;
   }
   // byte `byte` of row r's 64 chunk bytes (dword swizzle above)
   auto sc_at = [](int r, int byte) { return r * 64 + (((byte >> 2) ^ (r & 15)) << 2) + (byte & 3); };
-  uint32_t va[2];
+  // activations: NVFP4 codes, waves w < BM/16: rows 16 w + lane / 4, 16-byte
+  // piece lane & 3 of the stage's 64 bytes; bf16, BM/32 loads per wave: rows
+  // 4 (BM/32 w + j) + lane / 16, the 16-byte chunk landing at position lane & 15
+  constexpr int kAb = BM / 32;  // bf16 activation loads per wave and stage
+  uint32_t va[kFp4A ? 1 : kAb];
   if constexpr (kFp4A) {
-    // waves 0-3: rows 16 wave + lane / 4, 16-byte piece lane & 3 of the stage's 64 code bytes
     const int r = 16 * wave + (lane >> 2);
-    va[0] = r < M ? (uint32_t)(r * (K / 2) + k_lo / 2 + 16 * (lane & 3)) : kBufOOB;
-    va[1] = kBufOOB;
+    va[0] = (wave < BM / 16 && r < M) ? (uint32_t)(r * (K / 2) + k_lo / 2 + 16 * (lane & 3)) : kBufOOB;
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int r = 4 * (2 * wave + j) + (lane >> 4);
+    for (int j = 0; j < kAb; j++) {
+      const int r = 4 * (kAb * wave + j) + (lane >> 4);
       const int x = (lane & 15) ^ (r & 15);  // global chunk landing at position lane & 15
       va[j] = r < M ? (uint32_t)(r * (K * 2) + x * 16) : kBufOOB;
     }
   }
   // This wave's loads of one stage, in issue order: NVFP4 the activation
-  // codes (waves 0-3) then the weight codes; bf16 weight codes then two
-  // activation loads.  A scale chunk is cl loads: 4 of weight scales, and for
-  // NVFP4 2 more of activation scales.
-  const int n_act = kFp4A ? (wave < 4 ? 1 : 0) : 2;
+  // codes (waves below BM/16) then the weight codes; bf16 weight codes then
+  // BM/32 activation loads.  A scale chunk is cl loads: 4 of weight scales and
+  // for NVFP4 BM/32 of activation scales.
+  const int n_act = kFp4A ? (wave < BM / 16 ? 1 : 0) : kAb;
   const int per_stage = n_act + 1;
-  constexpr int cl = kFp4A ? 6 : 4;
+  constexpr int cl = 4 + (kFp4A ? kAsc : 0);
   const int nchunks = (nst + kRChunk - 1) / kRChunk;
   auto issue_chunk = [&](int k) {
     uint8_t* buf = ssc + (k & 1) * (kRScW + kRScA);
@@ -374,40 +393,44 @@ __global__ void __launch_bounds__(kRNT)
     if constexpr (kFp4A) {
       const v4u32 ras = make_rsrc4(SFA, (int64_t)M * (K / 16));
 #pragma unroll
-      for (int j = 0; j < 2; j++) buf_lds4(ras, vas[j], soff(64 * k), lds_u(buf + kRScW + (2 * wave + j) * 256));
+      for (int j = 0; j < kAsc; j++)
+        buf_lds4(ras, vas[j], soff(64 * k), lds_u(buf + kRScW + (kAsc * wave + j) * 256));
     }
   };
   auto issue_w = [&](int st) {
-    buf_lds16(rq, vw, soff(st * 64), lds_u(sw + (st % kRRing) * kRW + wave * 1024));
+    buf_lds16(rq, vw, soff(st * 64), lds_u(sw + (st % kRing) * kRW + wave * 1024));
   };
   auto issue = [&](int st) {
     if constexpr (kFp4A) {
-      if (wave < 4) buf_lds16(ra, va[0], soff(st * 64), lds_u(saq + (st % kRRing) * kRAq + wave * 1024));
+      if (wave < BM / 16) buf_lds16(ra, va[0], soff(st * 64), lds_u(saq + (st % kRing) * kRAq + wave * 1024));
       issue_w(st);
     } else {
       issue_w(st);
-      uint8_t* base = smem + (st % kRRing) * kRA;
+      uint8_t* base = smem + (st % kRing) * kRA;
       const uint32_t k0 = soff((k_lo + st * kRSK) * 2);
-      buf_lds16(ra, va[0], k0, lds_u(base + (2 * wave) * 1024));
-      buf_lds16(ra, va[1], k0, lds_u(base + (2 * wave + 1) * 1024));
+#pragma unroll
+      for (int j = 0; j < kAb; j++) buf_lds16(ra, va[j], k0, lds_u(base + (kAb * wave + j) * 1024));
     }
   };
-  // NVFP4: dequantise stage st's activation codes into fp16 slot st % 2; thread
-  // = (row tid / 8, 16-value block tid % 8), chunks 2b and 2b + 1 of the row
+  // NVFP4: dequantise stage st's activation codes into fp16 slot st % 2; a
+  // thread takes BM/64 (row, 16-value block) items, chunks 2b and 2b + 1 of the row
   auto dequant_a = [&](int st) {
-    const int r = tid >> 3, b = tid & 7;
-    const uint2 w = *reinterpret_cast<const uint2*>(saq + (st % kRRing) * kRAq + r * 64 + 8 * b);
     const uint8_t* asc = ssc + ((st / kRChunk) & 1) * (kRScW + kRScA) + kRScW;
-    const _Float16 s = e4m3_to_f16(asc[sc_at(r, (st % kRChunk) * 8 + b)]);
-    uint8_t* row = smem + (st & 1) * kRA + r * 256;
-    *reinterpret_cast<v8h*>(row + (((2 * b) ^ (r & 15)) * 16)) = dq8_f16(w.x, s);
-    *reinterpret_cast<v8h*>(row + (((2 * b + 1) ^ (r & 15)) * 16)) = dq8_f16(w.y, s);
+#pragma unroll
+    for (int i = 0; i < BM / 64; i++) {
+      const int it = tid + kRNT * i, r = it >> 3, b = it & 7;
+      const uint2 w = *reinterpret_cast<const uint2*>(saq + (st % kRing) * kRAq + r * 64 + 8 * b);
+      const _Float16 s = e4m3_to_f16(asc[sc_at(r, (st % kRChunk) * 8 + b)]);
+      uint8_t* row = smem + (st & 1) * kRA + r * 256;
+      *reinterpret_cast<v8h*>(row + (((2 * b) ^ (r & 15)) * 16)) = dq8_f16(w.x, s);
+      *reinterpret_cast<v8h*>(row + (((2 * b + 1) ^ (r & 15)) * 16)) = dq8_f16(w.y, s);
+    }
   };
-  // This wave's issue order: chunk 0, stages 0, 1, 2, then at stage s the
-  // loads of stage s + 3, followed by chunk k when s + 3 == 8k - 1.  Loads
-  // complete in order; waiting for "issued - 1 - index" outstanding means the
-  // load at that index has landed.
-  constexpr int kAhead = kRRing - 1;
+  // This wave's issue order: chunk 0, stages 0 .. kAhead - 1, then at stage s
+  // the loads of stage s + kAhead, followed by chunk k when s + kAhead ==
+  // 8k - 1.  Loads complete in order; waiting for "issued - 1 - index"
+  // outstanding means the load at that index has landed.
+  constexpr int kAhead = kRing - 1;
   auto chunks_before = [&](int st) { return min(st / kRChunk, nchunks - 1); };  // chunks k >= 1 before stage st
   auto last_of_stage = [&](int st) { return cl - 1 + per_stage * (st + 1) + cl * chunks_before(st); };
   auto last_of_chunk = [&](int k) { return k == 0 ? cl - 1 : last_of_stage(kRChunk * k - 1) + cl; };
@@ -418,7 +441,7 @@ __global__ void __launch_bounds__(kRNT)
   issue_chunk(0);
   for (int st = 0; st < min(nst, kAhead); st++) issue(st);
   if constexpr (kFp4A) {
-    // the activation codes (waves 0-3) and scales (waves 4-7) of stage 0
+    // the activation codes and scales of stage 0
     wait_vmcnt_upto(issued_before(0) - 1 - (n_act > 0 ? last_of_stage(0) - per_stage + n_act : last_of_chunk(0)));
     __builtin_amdgcn_s_barrier();
     dequant_a(0);
@@ -428,15 +451,15 @@ __global__ void __launch_bounds__(kRNT)
   // lane (c, g) of the 16x16x32 MFMAs: weight row / activation row c, K 8g..8g+7
   const int c = lane & 15, g = lane >> 4;
   const int h = wave & 1, q = wave >> 1;
-  v4f acc[4][4];
+  v4f acc[4][kTM];
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
-    for (int t = 0; t < 4; t++) acc[j][t] = v4f{};
+    for (int t = 0; t < kTM; t++) acc[j][t] = v4f{};
   for (int s = 0; s < nst; s++) {
     // this wave's loads of stage s (and so its scale chunk); NVFP4 also the
-    // activation codes of stage s + 1 (waves 0-3) or the scale chunk of stage
-    // s + 1 (waves 4-7)
+    // activation codes of stage s + 1 (waves that load them) or else the
+    // scale chunk of stage s + 1
     int last = last_of_stage(s);
     if (kFp4A && s + 1 < nst)
       last = n_act > 0 ? last_of_stage(s + 1) - per_stage + n_act : max(last, last_of_chunk((s + 1) / kRChunk));
@@ -449,11 +472,11 @@ __global__ void __launch_bounds__(kRNT)
     if constexpr (kFp4A) {
       if (s + 1 < nst) dequant_a(s + 1);  // read after the barrier at stage s + 1
     }
-    const uint8_t* sa = smem + (kFp4A ? (s & 1) : (s % kRRing)) * kRA;
-    v8h fh[4];
-    v8bf fa[4];
+    const uint8_t* sa = smem + (kFp4A ? (s & 1) : (s % kRing)) * kRA;
+    v8h fh[kTM];
+    v8bf fa[kTM];
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
+    for (int t = 0; t < kTM; t++) {
       const int r = 16 * t + c;
       const uint4 v = *reinterpret_cast<const uint4*>(sa + r * 256 + (((4 * q + g) ^ (r & 15)) * 16));
       if constexpr (kFp4A)
@@ -465,60 +488,66 @@ __global__ void __launch_bounds__(kRNT)
     for (int j = 0; j < 4; j++) {
       const int col = 64 * h + 16 * j + c;
       // K values 32q + 8g .. +7 of the stage: code word 4q + g, scale byte 2q + g/2
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(sw + (s % kRRing) * kRW + col * 64 +
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(sw + (s % kRing) * kRW + col * 64 +
                                                                ((q ^ ((col >> 2) & 3)) * 16) + 4 * g);
       const uint32_t sbw = ssc[((s / kRChunk) & 1) * (kRScW + kRScA) + sc_at(col, (s % kRChunk) * 8 + 2 * q + (g >> 1))];
       if constexpr (kFp4A) {
         const v8h fb = dq8_f16(word, e4m3_to_f16(sbw));
 #pragma unroll
-        for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb, fh[t], acc[j][t], 0, 0, 0);
+        for (int t = 0; t < kTM; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb, fh[t], acc[j][t], 0, 0, 0);
       } else {
         const v8bf fb = dq8_bf16(word, e4m3_to_f32(sbw));
 #pragma unroll
-        for (int t = 0; t < 4; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[t], acc[j][t], 0, 0, 0);
+        for (int t = 0; t < kTM; t++) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[t], acc[j][t], 0, 0, 0);
       }
     }
   }
-  // ---- sum the four K quarters in LDS (in quarter order), then store
-  __syncthreads();  // LDS is free
+  // ---- sum the four K quarters in LDS (in quarter order), 64 rows at a time, then store
   constexpr int kRedPitch = kRBN + 4;  // floats per row of one quarter's 64 x 128 tile
-  static_assert(4 * kRBM * kRedPitch * 4 <= kRSmem && kRedBytes == 4 * kRBM * kRedPitch * 4, "quarter tiles fit");
+  static_assert(kRedBytes == 4 * kRHalf * kRedPitch * 4 && kRedBytes <= G::kSmem, "quarter tiles fit");
   float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int j = 0; j < 4; j++)
-#pragma unroll
-    for (int t = 0; t < 4; t++)
-      *reinterpret_cast<float4*>(red + (q * kRBM + 16 * t + c) * kRedPitch + 64 * h + 16 * j + 4 * g) =
-          make_float4(acc[j][t][0], acc[j][t][1], acc[j][t][2], acc[j][t][3]);
-  __syncthreads();
   const float alpha = alpha_ptr ? alpha_ptr[0] : 1.0f;
-  for (int idx = tid; idx < kRBM * kRBN / 4; idx += kRNT) {  // 4 consecutive outputs per item
-    const int m = idx / (kRBN / 4), nl = (idx % (kRBN / 4)) * 4;
-    const int n = n0 + nl;
-    if (m >= M || n >= N) continue;
-    float4 v = *reinterpret_cast<const float4*>(red + m * kRedPitch + nl);
 #pragma unroll
-    for (int qq = 1; qq < 4; qq++) {
-      const float4 u = *reinterpret_cast<const float4*>(red + (qq * kRBM + m) * kRedPitch + nl);
-      v.x += u.x;
-      v.y += u.y;
-      v.z += u.z;
-      v.w += u.w;
+  for (int hh = 0; hh < BM / kRHalf; hh++) {
+    __syncthreads();  // LDS is free (the ring, or the previous half's tiles)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+        *reinterpret_cast<float4*>(red + (q * kRHalf + 16 * t + c) * kRedPitch + 64 * h + 16 * j + 4 * g) =
+            make_float4(acc[j][4 * hh + t][0], acc[j][4 * hh + t][1], acc[j][4 * hh + t][2], acc[j][4 * hh + t][3]);
+    __syncthreads();
+    for (int idx = tid; idx < kRHalf * kRBN / 4; idx += kRNT) {  // 4 consecutive outputs per item
+      const int ml = idx / (kRBN / 4), nl = (idx % (kRBN / 4)) * 4;
+      const int m = kRHalf * hh + ml, n = n0 + nl;
+      if (m >= M || n >= N) continue;
+      float4 v = *reinterpret_cast<const float4*>(red + ml * kRedPitch + nl);
+#pragma unroll
+      for (int qq = 1; qq < 4; qq++) {
+        const float4 u = *reinterpret_cast<const float4*>(red + (qq * kRHalf + ml) * kRedPitch + nl);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
+      }
+      if (splits == 1)
+        *reinterpret_cast<uint2*>(D + (int64_t)m * N + n) =
+            make_uint2(pack_bf16x2(alpha * v.x, alpha * v.y), pack_bf16x2(alpha * v.z, alpha * v.w));
+      else
+        *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + n) = v;
     }
-    if (splits == 1)
-      *reinterpret_cast<uint2*>(D + (int64_t)m * N + n) =
-          make_uint2(pack_bf16x2(alpha * v.x, alpha * v.y), pack_bf16x2(alpha * v.z, alpha * v.w));
-    else
-      *reinterpret_cast<float4*>(part + ((int64_t)split * M + m) * N + n) = v;
   }
 }
 
-// K split of the 64-row kernel: the number of K ranges that minimises an
+// K split of the row kernel: the number of K ranges that minimises an
 // estimate of the time in units of one stage (~0.6 us, measured cold): rounds
 // of workgroups (one per CU) x (stages per range + ~3 for the set-up and the
 // quarter sum), plus for a split the FP32 partials written and read back (M x N
 // x 8 bytes per range at ~5 TB/s) and the reduce launch (~6).  Measurement
 // override BSFP4_ROWS64_SPLITS=n.
+constexpr int64_t kRMaxRows = 128;     // rows the kernel takes (64-row form up to 64, 128-row form above)
+constexpr int64_t kRW4A16Rows = 128;   // default upper limits of the row kernel per activation kind
+constexpr int64_t kRNvfp4Rows = 128;
 int rows64_splits(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = (N + kRBN - 1) / kRBN, total = K / kRSK;
   if (total < 1) return 0;
@@ -578,18 +607,22 @@ hipError_t launch_w4a16_tiled(const uint16_t* A, const uint8_t* B, const uint8_t
 
 namespace bsfp4 {
 
-// Used for 17..64 rows.  Measured cold at N = 4096, K = 7168 (both kernels,
+// Used for 17..128 rows.  Measured cold at N = 4096, K = 7168 (both kernels,
 // events) against the split-K small-M kernels: M = 16 17.6 / 16.9 us (so 16
 // and fewer rows keep those), M = 17 17.8 / 18.7, M = 32 19.2 / 20.4; at the
 // projection shapes (M = 32; N x K = 6656 x 19968 / 19968 x 6656) 46.8 /
-// 49.4 us, where K ranges of up to 8 stages took 67.8 / 65.6 us.
-// Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for any 5..64 rows.
+// 49.4 us, where K ranges of up to 8 stages took 67.8 / 65.6 us.  The
+// 128-row form against the 256 x 256 tiled kernel: M = 65 / 96 / 128 at
+// 4096 x 7168 24.5 / 25.4 / 26.5 against 36.1 / 36.5 / 37.5 us, M = 128 at
+// the projection shapes 68.4 / 76.3 against 84.6 / 80.6 us.
+// Measurement overrides: BSFP4_W4A16_ROWS64=0 never, =1 for any 5..128 rows.
 bool w4a16_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_W4A16_ROWS64");
   if (e && e[0] == '0') return false;
-  const int64_t min_rows = (e && e[0] == '1') ? 5 : 17;
+  const bool force = e && e[0] == '1';
+  const int64_t min_rows = force ? 5 : 17, max_rows = force ? kRMaxRows : kRW4A16Rows;
   const int64_t lim = (int64_t)1 << 31;
-  return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
+  return M >= min_rows && M <= max_rows && K % kRSK == 0 && M * K * 2 < lim && N * (K / 2) < lim &&
          rows64_splits(M, N, K, device_cu_count()) > 0;
 }
 
@@ -598,16 +631,19 @@ size_t w4a16_rows64_workspace(int64_t M, int64_t N, int64_t K) {
   return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
-// NVFP4 activations: used for 24..64 rows.  Measured cold at N = 4096,
+// NVFP4 activations: used for 24..128 rows.  Measured cold at N = 4096,
 // K = 7168 (both kernels, events) against the split / per-wave small-M
-// kernels: M = 17 18.8 / 18.4 us, M = 32 19.8 / 20.2, M = 64 22.2 / 23.6.
-// Measurement overrides: BSFP4_NVFP4_ROWS64=0 never, =1 for any 5..64 rows.
+// kernels: M = 17 18.8 / 18.4 us, M = 32 19.8 / 20.2, M = 64 22.2 / 23.6;
+// against the tiled kernel: M = 65 / 96 / 128 26.4 / 27.9 / 29.1 against
+// 27.0 / 29.4 / 30.9 us.
+// Measurement overrides: BSFP4_NVFP4_ROWS64=0 never, =1 for any 5..128 rows.
 bool nvfp4_rows64_ok(int64_t M, int64_t N, int64_t K) {
   const char* e = getenv("BSFP4_NVFP4_ROWS64");
   if (e && e[0] == '0') return false;
-  const int64_t min_rows = (e && e[0] == '1') ? 5 : 24;
+  const bool force = e && e[0] == '1';
+  const int64_t min_rows = force ? 5 : 24, max_rows = force ? kRMaxRows : kRNvfp4Rows;
   const int64_t lim = (int64_t)1 << 31;
-  return M >= min_rows && M <= kRBM && K % kRSK == 0 && M * (K / 2) < lim && N * (K / 2) < lim &&
+  return M >= min_rows && M <= max_rows && K % kRSK == 0 && M * (K / 2) < lim && N * (K / 2) < lim &&
          rows64_splits(M, N, K, device_cu_count()) > 0;
 }
 
@@ -620,7 +656,10 @@ hipError_t launch_rows64(const void* A, const uint8_t* SFA, const uint8_t* B, co
   if (splits < 1 || (splits > 1 && (part == nullptr || part_bytes < (size_t)splits * M * N * sizeof(float))))
     return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(((N + kRBN - 1) / kRBN) * splits);
-  rows64_gemm<AKIND><<<grid, kRNT, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
+  if (M <= 64)
+    rows64_gemm<AKIND, 64><<<grid, kRNT, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
+  else
+    rows64_gemm<AKIND, 128><<<grid, kRNT, 0, stream>>>(A, SFA, B, SFB, alpha, D, (int)M, (int)N, (int)K, splits, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, alpha, D, M * N, stream);

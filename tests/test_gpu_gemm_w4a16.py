@@ -76,12 +76,14 @@ def test_w4a16_rows_17_to_64_small_m_kernels(monkeypatch, mt4, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(5, 128, 128), (16, 96, 1024), (33, 4096, 7168), (63, 288, 2048),
                                    (64, 160, 4224), (12, 1056, 8192), (64, 32, 128), (40, 96, 4160),
-                                   (50, 4000, 5120), (36, 4096, 6144), (64, 4096, 8192)])
+                                   (50, 4000, 5120), (36, 4096, 6144), (64, 4096, 8192),
+                                   (65, 160, 2048), (100, 4096, 7168), (128, 288, 4224), (96, 96, 1024),
+                                   (120, 1056, 19968)])
 def test_w4a16_rows64_kernel(monkeypatch, M, N, K):
-    """The 64 x 128 tiled kernel forced for any 5..64 rows with K % 128 == 0
-    (partial row and column tiles, one or several K ranges, 1 to 8 stages per
-    range: 1, 2-4, 7, and 5 / 6 / 8 in the last three shapes); K % 128 != 0
-    takes the chunked small-M kernels."""
+    """The row kernel forced for any 5..128 rows with K % 128 == 0:
+    its 64-row and 128-row forms, partial row and column tiles, K ranges of
+    one to several stages (the planner's choice); K % 128 != 0 takes the
+    other small-M kernels."""
     monkeypatch.setenv("BSFP4_W4A16_ROWS64", "1")
     _run_check(*_problem(M, N, K, 720 + M))
 
