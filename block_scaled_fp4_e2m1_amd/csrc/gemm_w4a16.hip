@@ -241,8 +241,8 @@ __global__ void __launch_bounds__(kNT, 1)
 
 
 // ---------------------------------------------------------------------------
-// Row GEMM for 17 <= M <= 128 (fewer rows use the kernels of
-// gemm_skinny.hip), W4A16 (AKIND 1: bf16 activations, bf16 MFMA) or NVFP4 W4A4
+// Row GEMM for up to 128 rows (W4A16 from 17, NVFP4 from 24 rows; fewer rows
+// use the kernels of gemm_skinny.hip), W4A16 (AKIND 1: bf16 activations, bf16 MFMA) or NVFP4 W4A4
 // (AKIND 0: NVFP4 activations dequantised to fp16, fp16 MFMA; E2M1 x E4M3
 // values are exact in either type): one workgroup = all BM = 64 or 128 rows x
 // 128 output columns x one K range, 8 waves = 2 column halves x 4 K quarters
@@ -259,19 +259,19 @@ __global__ void __launch_bounds__(kNT, 1)
 //     MFMAs follow the stream: per stage the weight codes (one load per wave:
 //     16 rows x 64 bytes into [row][64 B], the 16-byte piece p of row r at
 //     position p ^ ((r >> 2) & 3), so the MFMA's 4-byte reads are
-//     conflict-free) and the activations; the scales (8 bytes per row and
-//     stage) come in chunks of eight stages, 64 bytes per row (16 lanes of 4
-//     bytes per row, 4 rows per load, dwords swizzled within the row so that
-//     the scale reads are conflict-free), double-buffered: chunk 0
-//     before the first stage, chunk k with the codes of stage 8k - 1 (one
-//     load of 8 bytes per row and stage measured 1.7 us slower at
-//     64 x 4096 x 7168: each such load touches 32 rows; unswizzled chunks
-//     0.4 us slower again, from 8-way bank conflicts).  Measured for W4A16
-//     at 64 x 4096 x 7168 cold (both kernels, events): weights of the
-//     whole range issued before the first
-//     stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us (the first
-//     of these is 16.6 us of this kernel in a rocprofv3 trace, against 17.7 us
-//     when the range was copied in long row segments ahead of everything);
+//     conflict-free) and the activations.  Measured for W4A16 at 64 x 4096 x
+//     7168 cold (both kernels, events): the range's weights issued before the
+//     first stage 22.7 us, 5 / 4 / 3 stages ahead 22.4 / 21.7 / 21.4 us (the
+//     first of these is 16.6 us of this kernel in a rocprofv3 trace, against
+//     17.7 us when the range was copied in long row segments ahead of
+//     everything);
+//   * the scales (8 bytes per row and stage) come in double-buffered chunks of
+//     eight stages, 64 bytes per row (16 lanes of 4 bytes per row, 4 rows per
+//     load, dwords swizzled within the row so that the scale reads are
+//     conflict-free): chunk 0 before the first stage, chunk k with the codes
+//     of stage 8k - 1.  One load of 8 bytes per row and stage measured 1.7 us
+//     slower at 64 x 4096 x 7168 (each such load touches 32 rows), unswizzled
+//     chunks 0.4 us slower (8-way bank conflicts);
 //   * bf16 activations: BM rows x 256 bytes a stage, the 16-byte chunk x of
 //     row r at position x ^ (r & 15) (conflict-free fragment reads), BM/32
 //     loads per wave;
