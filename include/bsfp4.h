@@ -163,7 +163,7 @@ BSFP4_API bsfp4_status fp4_gemm(int fmt, const uint8_t* A, const uint8_t* SFA, c
  *   plan and K split, so the output equals fp4_gemm's bit for bit)
  *   returns BSFP4_ERR_WORKSPACE, before any launch, when the shape needs
  *   more than fp4_gemm_noalloc_max_workspace() bytes of partials, i.e. when
- *   fp4_gemm_workspace_size(fmt, M, N, K) exceeds it (NVFP4 with M > 512 at
+ *   fp4_gemm_workspace_size(fmt, M, N, K) exceeds it (NVFP4 with M = 1024 at
  *   N = 4096, K = 7168, for example; MXFP4 never needs any)
  * Every call on one GPU shares that GPU's array, and the partials of a call
  * are written in full before they are read, so nothing needs clearing; calls
