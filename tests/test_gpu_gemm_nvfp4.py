@@ -245,10 +245,11 @@ def test_nvfp4_gemm_rows64_kernel(monkeypatch, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(64, 256, 8192, "1"), (40, 640, 4096, "3"), (17, 6656, 19968, ""),
-                                          (33, 1024, 2048, "16")])
+                                          (33, 1024, 2048, "16"), (128, 256, 8192, "1"),
+                                          (96, 640, 4096, "3"), (80, 1024, 2048, "16")])
 def test_nvfp4_gemm_rows64_long_ranges(monkeypatch, M, N, K, splits):
-    """The 64-row kernel (NVFP4 activations) with K ranges of many stages and
-    with one stage per range."""
+    """The row kernel (NVFP4 activations), 64- and 128-row forms, with K
+    ranges of many stages and with one stage per range."""
     if splits:
         monkeypatch.setenv("BSFP4_ROWS64_SPLITS", splits)
     aq, sfa, bq, sfb, alpha = nvfp4_problem(M, N, K, seed=680 + M)

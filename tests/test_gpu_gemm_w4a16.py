@@ -89,10 +89,12 @@ def test_w4a16_rows64_kernel(monkeypatch, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(64, 256, 8192, "1"), (40, 640, 4096, "3"), (17, 6656, 19968, ""),
-                                          (33, 1024, 2048, "16")])
+                                          (33, 1024, 2048, "16"), (128, 256, 8192, "1"),
+                                          (96, 640, 4096, "3"), (80, 1024, 2048, "16")])
 def test_w4a16_rows64_long_ranges(monkeypatch, M, N, K, splits):
-    """The 64-row kernel with K ranges of many stages (64 in one range, the
-    planner's 4 x 39 at the down-projection shape) and with one stage per range."""
+    """The row kernel, 64- and 128-row forms, with K ranges of many stages (64
+    in one range, the planner's 4 x 39 at the down-projection shape) and with
+    one stage per range."""
     if splits:
         monkeypatch.setenv("BSFP4_ROWS64_SPLITS", splits)
     _run_check(*_problem(M, N, K, 740 + M))

@@ -163,11 +163,14 @@ def test_nvfp4_moe_single_expert():
     _check(d, _run(d))
 
 
-def test_nvfp4_experts_quantize_edges():
+@pytest.mark.parametrize("K", [64, 1024, 1040, 2064])
+def test_nvfp4_experts_quantize_edges(K):
     """Rows whose row_map entry is out of range, and rows outside the expert
-    offsets, are written as zeros; the other rows match the oracle."""
-    T, K, E = 12, 64, 3
-    x = synth.bf16_normal(91, (T, K))
+    offsets, are written as zeros; the other rows match the oracle.  K of at
+    least 1024 (64 blocks) takes the one-wave-per-row form, with a partial
+    last pass over the row's blocks for K = 1040 and 2064."""
+    T, E = 12, 3
+    x = synth.bf16_normal(91 + K, (T, K))
     offs = np.array([2, 5, 5, 9], np.int32)            # rows 0-1 and 9-10 belong to no expert
     row_map = np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 9, -1, 30], np.int32)
     gs = np.array([50.0, 20.0, 400.0], np.float32)
