@@ -14,17 +14,27 @@
 // pair of values: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) and a packed fp16
 // multiply by the block scale.
 //
-// Structure (one workgroup = 256 threads = 4 waves in a 2x2 grid):
-//   * BM x BN output tile, K walked in stages of 128 elements (64 code bytes and
-//     8 scale bytes per row);
-//   * each stage's packed codes and scale bytes are loaded from HBM with 128-bit
-//     loads into registers one stage ahead, then stored to LDS (double buffered)
-//     in a chunk-swizzled layout that keeps the MFMA fragment reads free of bank
-//     conflicts;
-//   * every wave reads its fragments from LDS as packed FP4 (4x less LDS traffic
-//     than fp16 tiles), dequantises them in registers and issues
-//     v_mfma_f32_32x32x16_f16 on a (BM/2) x (BN/2) wave tile;
-//   * epilogue: alpha * acc, RNE to bf16, bounds-checked stores.
+// Kernels, by M:
+//   * 24..128 rows with K % 128 == 0: the row kernel of gemm_w4a16.hip with
+//     its NVFP4 activation form;
+//   * other shapes of up to 64 rows: the weight-streaming kernels of
+//     gemm_skinny.hip;
+//   * the rest: nvfp4_gemm_f16lds, the dequantise-once kernel on the shared
+//     core of nvfp4_f16core.h (256x256 tiles of 16 waves, or 256x128 / 128x128
+//     tiles of 4 waves; every E2M1 value dequantised once per workgroup into
+//     fp16 LDS stages), with the tile shape and a K split planned from
+//     measured per-workgroup rates (plan_tiled) and split partials summed by
+//     splitk_reduce;
+//   * operands of 2^31 bytes or more: nvfp4_gemm_tiled, the register-dequant
+//     kernel below (64-bit addressing).  Its structure: a BM x BN tile, K in
+//     stages of 128 elements (64 code bytes and 8 scale bytes per row); each
+//     stage's packed codes and scale bytes are loaded with 128-bit loads into
+//     registers one stage ahead, then stored to LDS (double buffered) in a
+//     chunk-swizzled layout that keeps the fragment reads free of bank
+//     conflicts; every wave reads its fragments from LDS as packed FP4 (4x less
+//     LDS traffic than fp16 tiles), dequantises them in registers and issues
+//     v_mfma_f32_32x32x16_f16 on its wave tile.
+// Epilogues: alpha * acc, RNE to bf16, bounds-checked stores.
 //
 // MFMA lane layouts (measured on gfx950): for 32x32x16, lane l supplies row
 // l%32 and eight consecutive K values of group l/32 of each operand; output
@@ -548,10 +558,7 @@ hipError_t launch_nvfp4_gemm(const uint8_t* A, const uint8_t* SFA, const uint8_t
 #undef BSFP4_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
-  const int64_t q = M * N / 4;
-  const unsigned rgrid = (unsigned)((q + 255) / 256 > 16384 ? 16384 : (q + 255) / 256);
-  splitk_reduce<<<rgrid, 256, 0, stream>>>(part, pl.splits, alpha, D, M * N);
-  return hipGetLastError();
+  return launch_splitk_reduce(part, pl.splits, alpha, D, M * N, stream);
 }
 
 hipError_t launch_splitk_reduce(const float* part, int splits, const float* alpha, uint16_t* D, int64_t MN,

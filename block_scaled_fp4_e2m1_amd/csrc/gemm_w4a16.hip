@@ -1,27 +1,33 @@
-// W4A16 GEMM for larger M on gfx950: D = bf16(alpha * A @ dec(B)^T) with A bf16
-// [M, K], B NVFP4 (E2M1 codes [N, K/2], one E4M3 scale per 16 K-elements
-// [N, K/16]) and alpha the tensor-wide weight scale applied to the FP32
-// accumulator: the dense W4A16 GEMM of the FlashInfer `mm_bf16_fp4` pages
-// ("feat: sm100 cute_dsl w4a16 gemm" and its follow-ups).  Rows up to 64 use
-// the weight-streaming kernels of gemm_skinny.hip.
+// GEMMs of more than 16 rows with NVFP4 weights on gfx950.
+//
+// W4A16: D = bf16(alpha * A @ dec(B)^T) with A bf16 [M, K], B NVFP4 (E2M1
+// codes [N, K/2], one E4M3 scale per 16 K-elements [N, K/16]) and alpha the
+// tensor-wide weight scale applied to the FP32 accumulator: the dense W4A16
+// GEMM of the FlashInfer `mm_bf16_fp4` pages ("feat: sm100 cute_dsl w4a16
+// gemm" and its follow-ups).  The row kernel further down also takes NVFP4
+// activations (the W4A4 GEMM of "perf(gemm): optimize SM103 CuTe DSL mm_fp4
+// kernel" at 24..128 rows).  Two kernels: the tiled kernel below for more than
+// 128 rows (and 65..128 rows when K % 128 != 0), the row kernel for 17..128
+// rows; 16 rows and fewer (and 17..64 rows when K % 128 != 0) use the
+// weight-streaming kernels of gemm_skinny.hip.
 //
 // An E2M1 value times an E4M3 scale has at most 6 significant bits, so the
 // dequantised weights are exact in bf16 and v_mfma_f32_32x32x16_bf16 forms the
 // exact products with FP32 accumulation.
 //
-// One workgroup = 8 waves (1 x 8) on a 256 x 256 output tile, 256 x 32 per
-// wave, so every B fragment is read and dequantised by exactly one wave (the
-// A fragments, plain bf16, are read by all eight; measured 3-12 % faster at
-// the projection shapes than 2 x 4 waves of 128 x 64); K in stages of 64 values.  A 3-slot LDS ring is filled by
-// direct-to-LDS buffer loads issued by 4 loader waves: per stage the A rows
-// (128 bytes of bf16, their 16-byte chunks XOR-swizzled by row so that the
-// fragment reads are conflict-free), the B code rows (32 bytes, chunk order
-// swapped on alternate 8-row blocks) and the B scale bytes (4 per row).  Each
-// wave reads its A fragments as bf16 and dequantises its B fragments in
-// registers.  B is the MFMA's first operand, so a lane ends with runs of 4
-// consecutive output columns of one row; the tile leaves through LDS in row
-// bands (bf16 output, or FP32 partials of a K split that splitk_reduce sums in
-// split order).
+// Tiled kernel: one workgroup = 8 waves (1 x 8) on a 256 x 256 output tile,
+// 256 x 32 per wave, so every B fragment is read and dequantised by exactly
+// one wave (the A fragments, plain bf16, are read by all eight; measured
+// 3-12 % faster at the projection shapes than 2 x 4 waves of 128 x 64); K in
+// stages of 64 values.  A 3-slot LDS ring is filled by direct-to-LDS buffer
+// loads issued by 4 loader waves: per stage the A rows (128 bytes of bf16,
+// their 16-byte chunks XOR-swizzled by row so that the fragment reads are
+// conflict-free), the B code rows (32 bytes, chunk order swapped on alternate
+// 8-row blocks) and the B scale bytes (4 per row).  Each wave reads its A
+// fragments as bf16 and dequantises its B fragments in registers.  B is the
+// MFMA's first operand, so a lane ends with runs of 4 consecutive output
+// columns of one row; the tile leaves through LDS in row bands (bf16 output,
+// or FP32 partials of a K split that splitk_reduce sums in split order).
 #include <algorithm>
 #include <cstdlib>
 #include <type_traits>
