@@ -9,7 +9,22 @@
 // page notes that narrow output tiles are what make the small-M case fast;
 // here the narrowest tile is 16 output columns.
 //
-// Decomposition (one workgroup per 16 consecutive output columns n):
+// Kernels (launch_kind picks the first that applies; the row kernel of
+// gemm_w4a16.hip has already taken 17..64 W4A16 rows and 24..64 NVFP4 rows when
+// K % 128 == 0):
+//   * skinny_lds_few: at most four rows, K <= 8192 (also the fused quantise +
+//     GEMM of nvfp4_quantize_gemm);
+//   * skinny_lds: NVFP4 activations, up to 16 rows, K <= 8192;
+//   * skinny_onepass: NVFP4 activations, up to 16 rows, K up to what its 8
+//     waves cover;
+//   * skinny_split: split-K form with one or two 16-row tiles (up to 32 rows),
+//     and four tiles (33..64 rows) for bf16 activations, when the weights fit
+//     32-bit buffer offsets;
+//   * skinny_gemm: the original form described below, for 33..64 rows of
+//     NVFP4 activations and for weights of 2^31 bytes or more (64-bit
+//     addressing).
+//
+// skinny_gemm decomposition (one workgroup per 16 consecutive output columns n):
 //   * the workgroup's waves split K into slices of 1024 elements; in a slice
 //     lane l (row n0 + l%16, quarter g = l/16) owns 256 consecutive K values:
 //     128 code bytes (eight 128-bit loads) and 16 scale bytes (one load), all
