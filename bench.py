@@ -764,9 +764,12 @@ def run_rows(torch, bs, synth, timer, only):
         nbytes = wbytes + 2 * T * H * 2 + 2 * (xq.numel() + xsf.numel()) + 2 * (aq.numel() + asf.numel())
         flops = 2.0 * R * (2 * I) * H + 2.0 * R * H * I
         layer()
+        ref = out.clone()
         rows["moe_mxfp4_4096x2048_e128_top8"] = {
             "layer_cold": _rate(timer.run(layer, iters=10, cold=True), flops, nbytes),
             "layer_warm": _rate(timer.run(layer, iters=10), flops, nbytes),
+            "layer_graph": _rate(timer.graph(layer, calls=3), flops, nbytes),
+            "graph_matches_eager": bool(torch.equal(out, ref)),
             "stages_cold_us": {"prep": timer.run(prep, cold=True)["median_us"],
                                "experts_quant": timer.run(equant, cold=True)["median_us"],
                                "gate_up_silu_quant": timer.run(gemm1, cold=True)["median_us"],
@@ -844,9 +847,12 @@ def run_rows(torch, bs, synth, timer, only):
         nbytes = wbytes + 2 * T * H * 2 + 2 * (xq.numel() + xsf.numel()) + 2 * (aq.numel() + asf.numel())
         flops = 2.0 * R * (2 * I) * H + 2.0 * R * H * I
         layer()
+        ref = out.clone()
         rows["moe_nvfp4_4096x2048_e128_top8"] = {
             "layer_cold": _rate(timer.run(layer, iters=10, cold=True), flops, nbytes),
             "layer_warm": _rate(timer.run(layer, iters=10), flops, nbytes),
+            "layer_graph": _rate(timer.graph(layer, calls=3), flops, nbytes),
+            "graph_matches_eager": bool(torch.equal(out, ref)),
             "stages_cold_us": {"prep": timer.run(prep, cold=True)["median_us"],
                                "experts_quant": timer.run(equant, cold=True)["median_us"],
                                "gate_up_silu_quant": timer.run(gemm1, cold=True)["median_us"],
