@@ -54,8 +54,11 @@ def _nvfp4_experts(seed, E, N, K):
     return dev_u8(q), dev_u8(sf)
 
 
-def test_moe_layers_in_a_graph():
-    T, H, I, E, topk = 96, 256, 128, 8, 2
+@pytest.mark.parametrize("H", [256, 1024])
+def test_moe_layers_in_a_graph(H):
+    """Both MoE layers captured in one graph; H = 1024 gives the NVFP4 experts
+    quantiser rows of 64 blocks (its one-wave-per-row form)."""
+    T, I, E, topk = 96, 128, 8, 2
     x = dev_bf16(synth.bf16_normal(1, (T, H)))
     ids_np, w_np = synth.routing(2, T, E, topk)
     ids, tw = dev_i32(ids_np), dev_f32(w_np)
